@@ -1,0 +1,225 @@
+"""Seeded synthetic workloads for the quantized gated delta-rule decode step.
+
+This module only draws random numbers and arranges them into arrays: it holds
+none of the decode step's arithmetic (no update, no readout, no quantization).
+Both the CPU oracle and the GPU path consume what it produces.
+
+The pages measure on real hybrid models (Qwen3.8-27B GDN heads and Kimi-Linear
+KDA heads, 128 x 128 states, served at batch sizes up to 512; STEPQuant paper,
+Sec. 5.1 and App. F.5) and public suites; none of those are available here.
+These generators stand in for them with the same state shape and the row and
+column outlier structure the paper reports for recurrent states (Sec. 4.2,
+App. B.6: max-to-median RMS contrasts of about 10x along key rows and 19x
+along value columns).
+
+Laws (per sequence b, head h, step t):
+  q, k ~ N(0, 1)^d, then L2-normalised in fp32     (key head)
+  v    ~ N(0, 1)^d                                  (value head)
+  alpha ~ U(lo, 1),  beta = sigmoid(N(0, 1))        (value head)
+  bf16 inputs are the fp32 draws rounded to nearest-even bf16.
+Random packed states (for per-step parity from an arbitrary state) draw codes
+uniformly from the symmetric range of their row width, log-uniform row factors,
+log-normal column factors and a random physical row order per head.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# ----------------------------------------------------------------- configs --
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    hk: int
+    hv: int
+    d: int
+    n8: int
+    T: int
+    dtype: str  # "f32" or "bf16" for q, k, v
+    seed: int
+    calib_seed: int | None
+    s0: str  # "zero", "normal", "outlier"
+    s0_scale: float = 1.0  # std of the normal part
+    outlier_sigma: float = 0.0  # log-normal sigma of row/column factors
+    alpha_lo: float = 0.9
+    layers: int = 1
+    calib_steps: int = 32
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def units(self) -> int:
+        return self.B * self.hv
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", B=1, hk=1, hv=1, d=16, n8=16, T=64, dtype="f32", seed=0,
+                     calib_seed=None, s0="zero"),
+    "small_mixed": Workload("small_mixed", B=8, hk=4, hv=4, d=64, n8=32, T=256, dtype="f32",
+                            seed=1, calib_seed=1001, s0="normal", s0_scale=0.1),
+    "serving_6bit": Workload("serving_6bit", B=256, hk=16, hv=32, d=128, n8=64, T=100,
+                             dtype="bf16", seed=2, calib_seed=1002, s0="outlier",
+                             outlier_sigma=1.0),
+    "highconc_4p5bit": Workload("highconc_4p5bit", B=1024, hk=16, hv=32, d=128, n8=16, T=100,
+                                dtype="bf16", seed=3, calib_seed=1003, s0="outlier",
+                                outlier_sigma=1.5),
+    "highconc_6bit": Workload("highconc_6bit", B=1024, hk=16, hv=32, d=128, n8=64, T=100,
+                              dtype="bf16", seed=3, calib_seed=1003, s0="outlier",
+                              outlier_sigma=1.5),
+    "stacked_6bit": Workload("stacked_6bit", B=512, hk=16, hv=32, d=128, n8=64, T=2048,
+                             dtype="bf16", seed=4, calib_seed=1004, s0="outlier",
+                             outlier_sigma=1.0, alpha_lo=0.95, layers=48),
+}
+
+# stream tags keep the random streams of different purposes independent
+_TAG_INPUTS = 11
+_TAG_S0 = 12
+_TAG_PACKED = 13
+_TAG_RECORDS = 14
+
+
+def rng_for(*key: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([int(x) for x in key]))
+
+
+# -------------------------------------------------------------- bf16 utils --
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to the nearest bf16 (ties to even); returns uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    lsb = (u >> 16) & 1
+    return ((u + np.uint32(0x7FFF) + lsb) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to fp32 exactly."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ------------------------------------------------------------------ inputs --
+
+
+@dataclass
+class StepInputs:
+    """One decode step's inputs.  q, k, v are fp32 arrays holding exactly the
+    values the kernel sees (bf16-representable when dtype == 'bf16');
+    q_bits, k_bits, v_bits hold the bf16 patterns in that case."""
+    q: np.ndarray  # [B][Hk][d]
+    k: np.ndarray  # [B][Hk][d]
+    v: np.ndarray  # [B][Hv][d]
+    alpha: np.ndarray  # [B][Hv]
+    beta: np.ndarray  # [B][Hv]
+    dtype: str
+    q_bits: np.ndarray | None = None
+    k_bits: np.ndarray | None = None
+    v_bits: np.ndarray | None = None
+
+
+def _l2n(x: np.ndarray) -> np.ndarray:
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True, dtype=np.float32), dtype=np.float32)
+    return (x / n).astype(np.float32)
+
+
+def draw_inputs(B: int, hk: int, hv: int, d: int, *, dtype: str, seed: int, step: int,
+                alpha_lo: float = 0.9, stream: int = _TAG_INPUTS, layer: int = 0) -> StepInputs:
+    g = rng_for(seed, stream, layer, step)
+    q = _l2n(g.standard_normal((B, hk, d), dtype=np.float32))
+    k = _l2n(g.standard_normal((B, hk, d), dtype=np.float32))
+    v = g.standard_normal((B, hv, d), dtype=np.float32)
+    alpha = g.uniform(alpha_lo, 1.0, size=(B, hv)).astype(np.float32)
+    beta = (1.0 / (1.0 + np.exp(-g.standard_normal((B, hv))))).astype(np.float32)
+    if dtype == "bf16":
+        qb, kb, vb = f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+        return StepInputs(bf16_bits_to_f32(qb), bf16_bits_to_f32(kb), bf16_bits_to_f32(vb),
+                          alpha, beta, dtype, qb, kb, vb)
+    assert dtype == "f32"
+    return StepInputs(q, k, v, alpha, beta, dtype)
+
+
+def workload_inputs(w: Workload, step: int, *, calibration: bool = False, layer: int = 0,
+                    B: int | None = None) -> StepInputs:
+    seed = w.calib_seed if calibration else w.seed
+    assert seed is not None
+    return draw_inputs(B or w.B, w.hk, w.hv, w.d, dtype=w.dtype, seed=seed, step=step,
+                       alpha_lo=w.alpha_lo, layer=layer)
+
+
+def initial_state(w: Workload, *, layer: int = 0, B: int | None = None) -> np.ndarray:
+    """S0 [B][Hv][d][d] fp32 following the workload's law."""
+    B = B or w.B
+    shape = (B, w.hv, w.d, w.d)
+    if w.s0 == "zero":
+        return np.zeros(shape, np.float32)
+    g = rng_for(w.seed, _TAG_S0, layer)
+    S = g.standard_normal(shape, dtype=np.float32)
+    if w.s0 == "normal":
+        S *= np.float32(w.s0_scale)
+        return S
+    assert w.s0 == "outlier"
+    # per-head row and column factors, shared across sequences (Sec. 4.2 outliers)
+    a = g.lognormal(0.0, w.outlier_sigma, size=(w.hv, w.d, 1)).astype(np.float32)
+    e = g.lognormal(0.0, w.outlier_sigma, size=(w.hv, 1, w.d)).astype(np.float32)
+    S *= a[None]
+    S *= e[None]
+    return S
+
+
+def random_states(n: int, hv: int, d: int, *, seed: int, scale: float = 1.0,
+                  outlier_sigma: float = 1.0) -> np.ndarray:
+    """Arbitrary fp32 states [n][Hv][d][d] with row/column outliers (for pack
+    and calibration parity)."""
+    g = rng_for(seed, _TAG_RECORDS)
+    S = g.standard_normal((n, hv, d, d), dtype=np.float32) * np.float32(scale)
+    a = g.lognormal(0.0, outlier_sigma, size=(1, hv, d, 1)).astype(np.float32)
+    e = g.lognormal(0.0, outlier_sigma, size=(1, hv, 1, d)).astype(np.float32)
+    return (S * a * e).astype(np.float32)
+
+
+@dataclass
+class PackedState:
+    pool8: np.ndarray  # int8  [B][Hv][n8][d]
+    pool4: np.ndarray  # uint8 [B][Hv][d-n8][d/2]
+    r: np.ndarray  # f32   [B][Hv][d]   physical row order
+    c: np.ndarray  # f32   [Hv][d]
+    perm: np.ndarray  # i32   [Hv][d]   logical row of each physical row
+    n8: int
+
+
+def random_packed_state(B: int, hv: int, d: int, n8: int, *, seed: int,
+                        c_one: bool = False, identity_perm: bool = False,
+                        r_log10_range: tuple[float, float] = (-2.0, 0.5)) -> PackedState:
+    """A valid packed state drawn directly: codes uniform on the symmetric range
+    of each row width, log-uniform row factors, log-normal column factors."""
+    g = rng_for(seed, _TAG_PACKED)
+    pool8 = g.integers(-127, 128, size=(B, hv, n8, d), dtype=np.int16).astype(np.int8)
+    nib = g.integers(-7, 8, size=(B, hv, d - n8, d), dtype=np.int16).astype(np.int8)
+    lo = nib[..., 0::2].astype(np.uint8) & 0x0F
+    hi = nib[..., 1::2].astype(np.uint8) & 0x0F
+    pool4 = (lo | (hi << 4)).astype(np.uint8)
+    r = (10.0 ** g.uniform(*r_log10_range, size=(B, hv, d))).astype(np.float32)
+    if c_one:
+        c = np.ones((hv, d), np.float32)
+    else:
+        c = g.lognormal(0.0, 1.0, size=(hv, d)).astype(np.float32)
+    if identity_perm:
+        perm = np.tile(np.arange(d, dtype=np.int32), (hv, 1))
+    else:
+        perm = np.stack([g.permutation(d).astype(np.int32) for _ in range(hv)])
+    return PackedState(pool8, pool4, r, c, perm, n8)
+
+
+def unpack_codes(ps_pool8: np.ndarray, ps_pool4: np.ndarray) -> np.ndarray:
+    """Codes of every physical row as int8 [B][Hv][d][d] (layout read-out for
+    test statistics; not part of any arithmetic)."""
+    lo = (ps_pool4 & 0x0F).astype(np.int8)
+    hi = (ps_pool4 >> 4).astype(np.int8)
+    lo = np.where(lo >= 8, lo - 16, lo).astype(np.int8)
+    hi = np.where(hi >= 8, hi - 16, hi).astype(np.int8)
+    z4 = np.empty(ps_pool4.shape[:-1] + (ps_pool4.shape[-1] * 2,), np.int8)
+    z4[..., 0::2] = lo
+    z4[..., 1::2] = hi
+    return np.concatenate([ps_pool8, z4], axis=-2)

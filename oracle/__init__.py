@@ -1,0 +1,243 @@
+"""CPU oracle for the quantized gated delta-rule decode step.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the CPU-baseline leg of
+the benchmark may import this package; the product library never does.
+
+The arithmetic lives in ``stq_oracle.c`` (plain loops, IEEE double, built with
+``-ffp-contract=off``); this module only builds it and marshals numpy arrays.
+Every function below states the passage of the STEPQuant paper it follows
+("STEPQuant: When and Where Errors Matter in Delta-Rule Recurrent State
+Quantization", arXiv 2609.38169).
+
+Parity status of each function (what pins it is in ``tests/test_oracle_pins.py``):
+  rhe            pinned: numpy's rint on a half-integer grid (library routine)
+  dequant        pinned: hand-made golden layout fixture, quantizer round trip
+  pack           pinned: round trip, half-step error bound, S=0 closed form
+  step           pinned: fixed point, delta-write closed form (o = v),
+                 Proposition 1 identity, half-step bound, S0 = 0 closed form
+  fp_step        pinned: App. B.1 norm identity, App. B.3 isolated-row read error
+  calib_*        pinned: numpy max / stable argsort (library routines)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+_SRC = _HERE / "stq_oracle.c"
+_LIB = _HERE / "libstq_oracle.so"
+
+
+def compile_oracle(src: Path, out: Path) -> Path:
+    """Compile an oracle source file with gcc (plain C, no GPU code)."""
+    tmp = out.with_suffix(".so.tmp")
+    subprocess.run(
+        ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+         "-Wall", "-o", str(tmp), str(src), "-lm", "-lpthread"],
+        check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> Path:
+    """Build ``libstq_oracle.so`` next to its source."""
+    if force or not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+        compile_oracle(_SRC, _LIB)
+    return _LIB
+
+
+def _bind(path: Path):
+    lib = ctypes.CDLL(str(path))
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    L = ctypes.c_long
+    lib.oracle_rhe.argtypes = [ctypes.c_double]
+    lib.oracle_rhe.restype = ctypes.c_double
+    lib.oracle_dequant.argtypes = [I, I, I, I, I, P, P, P, P, P, P, I]
+    lib.oracle_pack.argtypes = [I, I, I, I, I, P, P, P, P, P, P, I]
+    lib.oracle_step.argtypes = [I, I, I, I, I, I] + [P] * 15 + [I]
+    lib.oracle_fp_step.argtypes = [I, I, I, I, I] + [P] * 7 + [I]
+    lib.oracle_calib_cols.argtypes = [L, I, I, I, P, P]
+    lib.oracle_calib_rows.argtypes = [L, I, I, I, P, P]
+    lib.oracle_calib_finalize.argtypes = [I, I, I, I, P, P, P, P]
+    for name in ("oracle_dequant", "oracle_pack", "oracle_step", "oracle_fp_step",
+                 "oracle_calib_cols", "oracle_calib_rows", "oracle_calib_finalize"):
+        getattr(lib, name).restype = I
+    return lib
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+class Oracle:
+    """The oracle's entry points bound to one compiled library (the default one,
+    or a deliberately broken copy in the mutation tests)."""
+
+    def __init__(self, path: Path | None = None):
+        self._path = path
+        self._lib = None
+
+    def lib(self):
+        if self._lib is None:
+            if self._path is None:
+                if not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+                    build(force=True)
+                self._path = _LIB
+            self._lib = _bind(self._path)
+        return self._lib
+
+    def rhe(self, y: float) -> float:
+        """Round half to even (Sec. 2.2 'round', reading R1)."""
+        return self.lib().oracle_rhe(float(y))
+
+    def dequant(self, pool8, pool4, r, c, perm, *, n8: int, nthreads: int = 1) -> np.ndarray:
+        """Reconstruct S_ij = r_i c_j z_ij in logical row order (Sec. 4.3).
+
+        pool8 [B][Hv][n8][dv] int8, pool4 [B][Hv][dk-n8][dv/2] uint8,
+        r [B][Hv][dk] f32, c [Hv][dv] f32, perm [Hv][dk] i32 -> S [B][Hv][dk][dv] f64.
+        """
+        r = _c(r, np.float32)
+        B, hv, dk = r.shape
+        c = _c(c, np.float32)
+        dv = c.shape[1]
+        pool8 = _c(pool8, np.int8).reshape(B, hv, n8, dv)
+        pool4 = _c(pool4, np.uint8).reshape(B, hv, dk - n8, dv // 2)
+        perm = _c(perm, np.int32)
+        S = np.empty((B, hv, dk, dv), np.float64)
+        rc = self.lib().oracle_dequant(B, hv, dk, dv, n8, _ptr(pool8), _ptr(pool4), _ptr(r),
+                                    _ptr(c), _ptr(perm), _ptr(S), nthreads)
+        assert rc == 0
+        return S
+
+    def pack(self, S, c, perm, *, n8: int, nthreads: int = 1):
+        """Requantize fp32 states S [B][Hv][dk][dv] (logical order) into the packed
+        layout (Table C2 steps 4 and 6 applied to a given state).
+
+        Returns (pool8, pool4, r)."""
+        S = _c(S, np.float32)
+        B, hv, dk, dv = S.shape
+        c = _c(c, np.float32)
+        perm = _c(perm, np.int32)
+        pool8 = np.zeros((B, hv, n8, dv), np.int8)
+        pool4 = np.zeros((B, hv, dk - n8, dv // 2), np.uint8)
+        r = np.empty((B, hv, dk), np.float32)
+        rc = self.lib().oracle_pack(B, hv, dk, dv, n8, _ptr(S), _ptr(c), _ptr(perm), _ptr(pool8),
+                                 _ptr(pool4), _ptr(r), nthreads)
+        assert rc == 0
+        return pool8, pool4, r
+
+    def step(self, pool8, pool4, r, c, perm, q, k, v, alpha, beta, *, n8: int,
+             want_X: bool = False, nthreads: int = 1):
+        """One quantized decode step (Table C2; Sec. 2.1 Eq. (1) with D = alpha I).
+
+        q, k [B][Hk][dk], v [B][Hv][dv], alpha, beta [B][Hv] (fp32 values; bf16
+        inputs are passed widened).  Returns dict with pool8, pool4, r, o and,
+        if want_X, the pre-requantization state X [B][Hv][dk][dv] (f64)."""
+        r = _c(r, np.float32)
+        B, hv, dk = r.shape
+        c = _c(c, np.float32)
+        dv = c.shape[1]
+        q = _c(q, np.float32)
+        hk = q.shape[1]
+        k = _c(k, np.float32)
+        v = _c(v, np.float32)
+        alpha = _c(alpha, np.float32)
+        beta = _c(beta, np.float32)
+        assert q.shape == (B, hk, dk) and k.shape == (B, hk, dk)
+        assert v.shape == (B, hv, dv) and alpha.shape == (B, hv) and beta.shape == (B, hv)
+        pool8 = _c(pool8, np.int8).reshape(B, hv, n8, dv)
+        pool4 = _c(pool4, np.uint8).reshape(B, hv, dk - n8, dv // 2)
+        perm = _c(perm, np.int32)
+        out = {
+            "pool8": np.zeros_like(pool8),
+            "pool4": np.zeros_like(pool4),
+            "r": np.empty_like(r),
+            "o": np.empty((B, hv, dv), np.float32),
+        }
+        X = np.empty((B, hv, dk, dv), np.float64) if want_X else None
+        rc = self.lib().oracle_step(B, hv, hk, dk, dv, n8, _ptr(pool8), _ptr(pool4), _ptr(r),
+                                 _ptr(c), _ptr(perm), _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(alpha), _ptr(beta), _ptr(out["pool8"]),
+                                 _ptr(out["pool4"]), _ptr(out["r"]), _ptr(out["o"]),
+                                 _ptr(X), nthreads)
+        assert rc == 0
+        if want_X:
+            out["X"] = X
+        return out
+
+    def fp_step(self, S, q, k, v, alpha, beta, *, nthreads: int = 1):
+        """Unquantized gated delta-rule step (Sec. 2.1 Eq. (1), D = alpha I).
+
+        S [B][Hv][dk][dv] f64 is updated IN PLACE; returns o [B][Hv][dv] f64."""
+        assert S.dtype == np.float64 and S.flags["C_CONTIGUOUS"]
+        B, hv, dk, dv = S.shape
+        q = _c(q, np.float32)
+        hk = q.shape[1]
+        k = _c(k, np.float32)
+        v = _c(v, np.float32)
+        alpha = _c(alpha, np.float32)
+        beta = _c(beta, np.float32)
+        o = np.empty((B, hv, dv), np.float64)
+        rc = self.lib().oracle_fp_step(B, hv, hk, dk, dv, _ptr(S), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(alpha), _ptr(beta), _ptr(o), nthreads)
+        assert rc == 0
+        return o
+
+    def calib_cols(self, S, colmax):
+        """colmax[h][j] <- max(colmax, max over records, rows of |S|).
+        S [n_rec][Hv][dk][dv]; colmax [Hv][dv] f64, updated in place."""
+        S = _c(S, np.float64)
+        n, hv, dk, dv = S.shape
+        assert colmax.dtype == np.float64 and colmax.shape == (hv, dv)
+        assert self.lib().oracle_calib_cols(n, hv, dk, dv, _ptr(S), _ptr(colmax)) == 0
+
+    def calib_rows(self, S, rowscore):
+        """rowscore[h][i] += sum over records and columns of S^2."""
+        S = _c(S, np.float64)
+        n, hv, dk, dv = S.shape
+        assert rowscore.dtype == np.float64 and rowscore.shape == (hv, dk)
+        assert self.lib().oracle_calib_rows(n, hv, dk, dv, _ptr(S), _ptr(rowscore)) == 0
+
+    def calib_finalize(self, colmax, rowscore, n8: int):
+        """Return (c [Hv][dv] f32, perm [Hv][dk] i32) from the accumulated
+        statistics: c = column absmax (0 -> 1); the n8 top-score rows (ties to the
+        lower index) first in ascending order, then the rest ascending."""
+        colmax = _c(colmax, np.float64)
+        rowscore = _c(rowscore, np.float64)
+        hv, dv = colmax.shape
+        dk = rowscore.shape[1]
+        c = np.empty((hv, dv), np.float32)
+        perm = np.empty((hv, dk), np.int32)
+        assert self.lib().oracle_calib_finalize(hv, dk, dv, n8, _ptr(colmax), _ptr(rowscore),
+                                             _ptr(c), _ptr(perm)) == 0
+        return c, perm
+
+
+_default = Oracle()
+rhe = _default.rhe
+dequant = _default.dequant
+pack = _default.pack
+step = _default.step
+fp_step = _default.fp_step
+calib_cols = _default.calib_cols
+calib_rows = _default.calib_rows
+calib_finalize = _default.calib_finalize

@@ -1,0 +1,91 @@
+"""Mutation check of the oracle's pins (CPU only).
+
+Each case plants one plausible mistake in a private copy of the oracle's C
+source, builds it, and runs the pins against that copy: at least one pin must
+fail.  This shows the pins constrain the oracle beyond agreeing with itself.
+"""
+from __future__ import annotations
+
+from pathlib import Path
+
+import pytest
+
+import oracle as oracle_pkg
+from tests import test_oracle_pins as pins
+
+SRC = Path(oracle_pkg.__file__).resolve().parent / "stq_oracle.c"
+
+# (name, text in the oracle source, replacement)
+MUTANTS = [
+    ("u transposed (S k instead of S^T k)",
+     "acc += S[(size_t)i * dv + j] * k[i];", "acc += S[(size_t)j * dv + i] * k[i];"),
+    ("sign of the delta correction", "(v[j] - alpha * u[j])", "(v[j] + alpha * u[j])"),
+    ("gate dropped on S^T k", "(v[j] - alpha * u[j])", "(v[j] - u[j])"),
+    ("gate dropped on S", "*x = alpha * (*x) + ", "*x = (*x) + "),
+    ("beta dropped", "beta * k[i] * (v[j]", "k[i] * (v[j]"),
+    ("readout with k instead of q",
+     "acc += S[(size_t)i * dv + j] * q[i];", "acc += S[(size_t)i * dv + j] * k[i];"),
+    ("round half away from zero", "return (fmod(f, 2.0) == 0.0) ? f : f + 1.0;",
+     "return f + 1.0;"),
+    ("nibble order swapped", "(j % 2 == 0) ? (byte & 0x0F) : (byte >> 4)",
+     "(j % 2 == 0) ? (byte >> 4) : (byte & 0x0F)"),
+    ("nibble not sign-extended", "return nib >= 8 ? nib - 16 : nib;", "return nib;"),
+    ("row factor from the mean instead of the max", "if (fabs(x) > m) m = fabs(x);",
+     "m += fabs(x) / s->dv;"),
+    ("physical order ignored in dequant",
+     "int i = perm[p];\n        for (int j = 0; j < s->dv; ++j) {\n            double rc",
+     "int i = p;\n        for (int j = 0; j < s->dv; ++j) {\n            double rc"),
+    ("column factor ignored in requant", "double x = row[j] / (double)c[j];",
+     "double x = row[j];"),
+    ("q_b off by one", "(1 << (bits - 1)) - 1", "(1 << (bits - 1))"),
+    ("no floor on the row factor", "if (rr < floor_r) rr = floor_r;", ""),
+    ("wrong GQA map", "int hk = h / (s->hv / s->hk); /* reading R5 */", "int hk = h % s->hk;"),
+    ("row factor not rounded to fp32", "double rr = (double)(float)(m / (double)qb);",
+     "double rr = m / (double)qb;"),
+    ("row score of |S| instead of S^2", "acc += x * x;", "acc += fabs(x);"),
+    ("ties to the higher row", "(sc[a] == sc[i] && a < i)", "(sc[a] == sc[i] && a > i)"),
+    ("zero column kept at 0", "(m > 0.0) ? (float)m : 1.0f", "(float)m"),
+    ("bit width from the logical row", "int qb = qmax_of_bits(row_bits(p, s->n8));",
+     "int qb = qmax_of_bits(row_bits(i, s->n8));"),
+]
+
+
+def _pin_cases():
+    return [
+        (pins.test_rhe_matches_numpy_rint_on_half_grid, {}),
+        (pins.test_dequant_golden_layout, {}),
+        (pins.test_pack_golden_half_ties, {"fixture": "requant_ties.json"}),
+        (pins.test_pack_golden_half_ties, {"fixture": "requant_fp32_factor.json"}),
+        (pins.test_quantizer_round_trip_brute_force, {"d": 32, "n8": 13}),
+        (pins.test_pack_error_within_half_step, {"n8": 5}),
+        (pins.test_int8row_equals_textbook_rowwise_absmax, {}),
+        (pins.test_step_fixed_point, {"d": 16, "n8": 8}),
+        (pins.test_step_delta_write_closed_form, {"d": 64, "n8": 32}),
+        (pins.test_step_from_zero_state_closed_form, {}),
+        (pins.test_step_requant_within_half_step, {"d": 32, "n8": 8}),
+        (pins.test_proposition1_readout_error, {"d": 16, "n8": 8}),
+        (pins.test_delta_feedback_norm_identity, {"d": 16}),
+        (pins.test_isolated_row_read_error, {"d": 16}),
+        (pins.test_error_recursion_and_drift_bound, {}),
+        (pins.test_calibration_matches_numpy_max_and_stable_argsort, {}),
+    ]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, name, old, new):
+    src = SRC.read_text()
+    assert src.count(old) >= 1, f"mutation site missing: {name}"
+    mutated = src.replace(old, new)
+    msrc = tmp_path / "mutant.c"
+    msrc.write_text(mutated)
+    lib = oracle_pkg.compile_oracle(msrc, tmp_path / "libmutant.so")
+    mut = oracle_pkg.Oracle(lib)
+    caught = []
+    for fn, kw in _pin_cases():
+        try:
+            fn(mut, **kw)
+        except AssertionError:
+            caught.append(fn.__name__)
+        except (ValueError, FloatingPointError, OverflowError):
+            caught.append(fn.__name__)
+    assert caught, f"no pin caught the planted mistake: {name}"
