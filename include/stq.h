@@ -1,0 +1,202 @@
+/*
+ * stq.h -- C ABI of the quantized gated delta-rule decode library for AMD
+ * MI355X (gfx950).
+ *
+ * What it computes (STEPQuant paper, "STEPQuant: When and Where Errors Matter in
+ * Delta-Rule Recurrent State Quantization", arXiv 2609.38169):
+ *   - the gated delta rule with a scalar gate, Sec. 2.1 Eq. (1) with D_t = a I:
+ *       X = a S + b k (v - a S^T k)^T,      o = X^T q
+ *   - over a recurrent state stored in the dual-axis form of Sec. 4.3,
+ *       S_ij = r_i c_j z_ij,
+ *     with per-key-row bit widths (4 or 8 bits, Sec. 3.2 mixed precision),
+ *     a key-row factor r_i recomputed at every step and a value-column factor
+ *     c_j fixed offline (Sec. 3.2 / Sec. 4.4: the precision map is calibrated
+ *     offline and fixed across requests);
+ *   - in the order of App. C.3 Table C2: reconstruct, update, emit the readout
+ *     before requantization, derive row factors, pack and write back.
+ * Quantizer (Sec. 2.2): z = clip(round(x / s), -q_b, q_b), q_b = 2^(b-1) - 1,
+ * with round = round-half-to-even; row factor r_i = max(fl32(max_j |X_ij / c_j|
+ * / q_b), 2^-126); the code of X_ij is taken against the stored r_i.
+ *
+ * Conventions
+ *   - Every function is extern "C", returns stq_status and never throws.
+ *   - All device memory is owned by the caller and passed as plain device
+ *     pointers.  The library allocates nothing and keeps no global state, so it
+ *     is re-entrant; the caller keeps every buffer alive until the work queued
+ *     on the stream has finished.
+ *   - Device work is queued on the caller's HIP stream (stq_stream_t is a
+ *     hipStream_t; NULL means the default stream) with no implicit
+ *     synchronisation.  Arguments are validated on the host before any launch;
+ *     a rejected call queues nothing.
+ *
+ * Packed layout (slot s, value head h; physical row p holds logical key row
+ * perm[h][p]; the first n8 physical rows are 8-bit, the rest 4-bit):
+ *   pool8  int8   [n_slots][Hv][n8][dv]       two's-complement codes
+ *   pool4  uint8  [n_slots][Hv][dk-n8][dv/2]  two's-complement nibbles; byte m
+ *                                             holds column 2m in bits 0..3 and
+ *                                             column 2m+1 in bits 4..7
+ *   r      float  [n_slots][Hv][dk]           row factor, physical row order
+ *   c      float  [Hv][dv]                    column factor (c_j > 0)
+ *   perm   int32  [Hv][dk]                    logical row of physical row p
+ * Vectors: q, k [B][Hk][dk]; v [B][Hv][dv]; alpha, beta [B][Hv] fp32;
+ * o [B][Hv][dv] fp32.  Value head h reads key head h / (Hv / Hk).
+ * States passed as fp32 matrices (pack input, dequant output, calibration
+ * records) are [B or n_rec][Hv][dk][dv] in logical row order.
+ */
+#ifndef STQ_H
+#define STQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *stq_stream_t; /* a hipStream_t; NULL = default stream */
+
+typedef enum {
+    STQ_OK = 0,
+    STQ_E_ARG = 1,         /* null or misaligned pointer, bad flag or enum */
+    STQ_E_SHAPE = 2,       /* inconsistent dimensions or batch size */
+    STQ_E_UNSUPPORTED = 3, /* a d_k / d_v outside the compiled set */
+    STQ_E_SPACE = 4,       /* caller buffer smaller than stq_state_bytes() */
+    STQ_E_STATE = 5,       /* mixed state decoded before calibration */
+    STQ_E_DEVICE = 6       /* a HIP launch or runtime call failed */
+} stq_status;
+
+typedef enum {
+    STQ_FMT_MIXED48 = 0, /* 4/8-bit key rows, fp32 r, calibrated c and perm */
+    STQ_FMT_INT8ROW = 1, /* uniform symmetric rowwise-absmax INT8: n8 = d_k,
+                            c = 1, identity row order (Sec. 5.1 baseline) */
+    STQ_FMT_FP32 = 2     /* unquantized fp32 state (the FP32-state baseline) */
+} stq_format;
+
+typedef enum { STQ_F32 = 0, STQ_BF16 = 1 } stq_dtype;
+
+/* Calibration flags (stq_calibrate), combinable. */
+#define STQ_CAL_RESET 1u    /* zero the accumulated statistics first */
+#define STQ_CAL_COLS 2u     /* fold records into the per-column absmax */
+#define STQ_CAL_ROWS 4u     /* fold records into the per-row sum of squares */
+#define STQ_CAL_FINALIZE 8u /* set c and perm from the statistics */
+
+/* Geometry.  Supported: d_k == d_v in {16, 32, 64, 128}; 0 <= n8 <= d_k
+ * (MIXED48; INT8ROW forces n8 = d_k); n_heads_v % n_heads_k == 0. */
+typedef struct {
+    int32_t n_slots;
+    int32_t n_heads_v;
+    int32_t n_heads_k;
+    int32_t d_k;
+    int32_t d_v;
+    int32_t n8;  /* 8-bit rows per head (same for every head) */
+    int32_t fmt; /* stq_format */
+} stq_desc;
+
+/* A state carved out of one caller buffer by stq_alloc_state.  Plain device
+ * pointers; fields that a format does not use are NULL. */
+typedef struct {
+    stq_desc desc;
+    int8_t *pool8;
+    uint8_t *pool4;
+    float *r;
+    float *c;
+    int32_t *perm;
+    float *colmax;      /* [Hv][dv]  calibration: column absmax */
+    double *rowscore;   /* [Hv][dk]  calibration: row sum of squares */
+    float *cal_colpart; /* [Hv][STQ_CAL_CHUNKS][dv] per-chunk partials */
+    double *cal_rowpart;/* [Hv][STQ_CAL_CHUNKS][dk] per-chunk partials */
+    float *s32;         /* [n_slots][Hv][dk][dv]  FP32 format only */
+    int32_t calibrated; /* host flag: c and perm hold a calibration */
+    int32_t reserved;
+} stq_state;
+
+#define STQ_CAL_CHUNKS 64
+
+/* Bytes of device memory a state with this geometry needs (host arithmetic
+ * only, no device call); 0 if the descriptor is invalid or unsupported. */
+size_t stq_state_bytes(const stq_desc *desc);
+
+/* Carve a state out of the caller's device buffer `dev` (256-byte aligned,
+ * `bytes` >= stq_state_bytes) and queue its initialisation on `stream`:
+ * codes 0, r = 2^-126 (the state S = 0), c = 1, perm = identity, fp32 state 0,
+ * statistics 0.  INT8ROW and FP32 states are ready to decode at once; a MIXED48
+ * state must be calibrated (stq_calibrate with STQ_CAL_FINALIZE, or
+ * stq_set_calibration) before stq_decode_step accepts it.
+ * Errors: STQ_E_ARG (null/misaligned), STQ_E_SHAPE / STQ_E_UNSUPPORTED (desc),
+ * STQ_E_SPACE (short buffer), STQ_E_DEVICE (launch failed). */
+stq_status stq_alloc_state(const stq_desc *desc, void *dev, size_t bytes,
+                           stq_stream_t stream, stq_state *out);
+
+/* Offline calibration of the fixed column factor and the 4/8-bit split of a
+ * MIXED48 state (Sec. 3.2 and Sec. 4.4: calibrated offline, fixed across
+ * requests; App. A.3: each batch element of a recorded step is one sample).
+ * `records` are n_rec fp32 states [n_rec][Hv][dk][dv] in logical row order
+ * (e.g. the states of an unquantized run at successive steps); n_rec may be 0
+ * with only RESET and/or FINALIZE.  Rule:
+ *   c_j    = max over all COLS records and rows of |S_ij| (a zero column -> 1)
+ *   score_i= sum over all ROWS records of sum_j S_ij^2
+ *   FINALIZE makes the n8 rows of highest score 8-bit (ties to the lower row),
+ *   and sets perm to those rows ascending, then the others ascending.
+ * FINALIZE rewrites c and perm, which invalidates packed contents: pack the
+ * state again afterwards.  The statistics are reduced in a fixed order, so the
+ * result does not depend on scheduling.
+ * Errors: STQ_E_ARG (null state/records, unknown flags, format not MIXED48),
+ * STQ_E_SHAPE (n_rec < 0), STQ_E_DEVICE. */
+stq_status stq_calibrate(stq_state *st, const float *records, int64_t n_rec,
+                         uint32_t flags, stq_stream_t stream);
+
+/* Install a calibration computed elsewhere: copies c [Hv][dv] (each > 0) and
+ * perm [Hv][dk] (a permutation of 0..dk-1 per head) from device memory and
+ * marks the state calibrated.  Like FINALIZE it invalidates packed contents.
+ * Errors: STQ_E_ARG (null, format not MIXED48), STQ_E_DEVICE. */
+stq_status stq_set_calibration(stq_state *st, const float *c, const int32_t *perm,
+                               stq_stream_t stream);
+
+/* Pack fp32 states S [B][Hv][dk][dv] (logical order) into slots[b] (slots: a
+ * device int32 array of B distinct slots, or NULL for slots 0..B-1): the
+ * requantization half of a decode step applied to a given state (the
+ * prefill-boundary pack).  FP32 format: copies S.
+ * Errors: STQ_E_ARG, STQ_E_SHAPE (B < 1 or B > n_slots), STQ_E_STATE
+ * (MIXED48 not calibrated), STQ_E_DEVICE. */
+stq_status stq_pack_state(const stq_state *st, const float *S, const int32_t *slots,
+                          int32_t B, stq_stream_t stream);
+
+/* One decode step for B sequences x Hv value heads, in place on slots[b]
+ * (App. C.3 Table C2 steps 1-4 and 6-7, fused into a single read and a single
+ * write of the packed state):
+ *   S_hat = r c z;  u = S_hat^T k;  X = a S_hat + b k (v - a u)^T;  o = X^T q
+ *   r'_i = max(fl32(max_j |X_ij / c_j| / q_b), 2^-126);
+ *   z'_ij = clip(rhe(X_ij / c_j / r'_i), -q_b, q_b)
+ * q, k, v are fp32 or bf16 (`dtype`); alpha, beta and o are fp32.
+ * Preconditions: slots distinct within a call (not checked on the device);
+ * a slot outside [0, n_slots) is skipped and its o is filled with NaN.
+ * Errors: STQ_E_ARG (null/misaligned pointer, bad dtype), STQ_E_SHAPE (B < 1
+ * or B > n_slots), STQ_E_STATE (MIXED48 not calibrated), STQ_E_DEVICE. */
+stq_status stq_decode_step(const stq_state *st, const int32_t *slots, int32_t B,
+                           const void *q, const void *k, const void *v, int32_t dtype,
+                           const float *alpha, const float *beta, float *o,
+                           stq_stream_t stream);
+
+/* Reconstruct S_ij = r_i c_j z_ij (Sec. 4.3) of slots[b] into fp32
+ * S_out [B][Hv][dk][dv] in logical row order (FP32 format: copies the state).
+ * Errors: STQ_E_ARG, STQ_E_SHAPE, STQ_E_DEVICE. */
+stq_status stq_dequant_state(const stq_state *st, const int32_t *slots, int32_t B,
+                             float *S_out, stq_stream_t stream);
+
+/* Streaming copy of `bytes` (a multiple of 16, both pointers 16-byte aligned)
+ * from src to dst: the plain copy kernel used to measure the practical HBM
+ * ceiling and to scale hardware byte counters.
+ * Errors: STQ_E_ARG, STQ_E_DEVICE. */
+stq_status stq_stream_copy(const void *src, void *dst, size_t bytes, stq_stream_t stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *stq_status_str(int32_t status);
+
+/* Library ABI version (bumped on any change to the declarations above). */
+int32_t stq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STQ_H */

@@ -1,0 +1,307 @@
+// C ABI of libstq.so: argument validation, layout arithmetic and dispatch.
+// Every check runs on the host before anything is queued; a rejected call
+// leaves the stream untouched.  See include/stq.h for the contract.
+#include "stq.h"
+
+#include <cstdint>
+#include <cstring>
+
+#include "stq_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr uint32_t kRowFloorBits = 0x00800000u; // 2^-126
+constexpr uint32_t kOneBits = 0x3f800000u;      // 1.0f
+
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_d(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+struct Layout {
+    size_t pool8, pool4, r, c, perm, colmax, rowscore, colpart, rowpart, s32, total;
+};
+
+// Validates a descriptor; fills byte sizes of each region (0 = absent).
+stq_status describe(const stq_desc *d, Layout *L) {
+    if (!d) return STQ_E_ARG;
+    if (d->fmt < STQ_FMT_MIXED48 || d->fmt > STQ_FMT_FP32) return STQ_E_ARG;
+    if (d->n_slots < 1 || d->n_heads_v < 1 || d->n_heads_k < 1) return STQ_E_SHAPE;
+    if (d->n_heads_v % d->n_heads_k != 0) return STQ_E_SHAPE;
+    if (d->d_k < 1 || d->d_v < 1) return STQ_E_SHAPE;
+    if (d->d_k != d->d_v || !supported_d(d->d_k)) return STQ_E_UNSUPPORTED;
+    if (d->fmt == STQ_FMT_MIXED48 && (d->n8 < 0 || d->n8 > d->d_k)) return STQ_E_SHAPE;
+    if (d->fmt == STQ_FMT_INT8ROW && d->n8 != d->d_k) return STQ_E_SHAPE;
+    const size_t S = static_cast<size_t>(d->n_slots), H = static_cast<size_t>(d->n_heads_v);
+    const size_t D = static_cast<size_t>(d->d_k);
+    std::memset(L, 0, sizeof(*L));
+    if (d->fmt != STQ_FMT_FP32) {
+        const size_t n8 = static_cast<size_t>(d->n8);
+        L->pool8 = S * H * n8 * D;
+        L->pool4 = S * H * (D - n8) * (D / 2);
+        L->r = S * H * D * sizeof(float);
+    } else {
+        L->s32 = S * H * D * D * sizeof(float);
+    }
+    L->c = H * D * sizeof(float);
+    L->perm = H * D * sizeof(int32_t);
+    if (d->fmt == STQ_FMT_MIXED48) {
+        L->colmax = H * D * sizeof(float);
+        L->rowscore = H * D * sizeof(double);
+        L->colpart = H * stq::kCalChunks * D * sizeof(float);
+        L->rowpart = H * stq::kCalChunks * D * sizeof(double);
+    }
+    L->total = round_up(L->pool8) + round_up(L->pool4) + round_up(L->r) + round_up(L->c) +
+               round_up(L->perm) + round_up(L->colmax) + round_up(L->rowscore) +
+               round_up(L->colpart) + round_up(L->rowpart) + round_up(L->s32);
+    return STQ_OK;
+}
+
+// Re-validates a state handed back by the caller.
+stq_status check_state(const stq_state *st) {
+    if (!st) return STQ_E_ARG;
+    Layout L;
+    stq_status e = describe(&st->desc, &L);
+    if (e != STQ_OK) return e;
+    if (!st->c || !st->perm) return STQ_E_ARG;
+    if (st->desc.fmt == STQ_FMT_FP32) {
+        if (!st->s32 || !aligned(st->s32, 16)) return STQ_E_ARG;
+    } else {
+        if (!st->r || !aligned(st->pool8, 16) || !aligned(st->pool4, 16)) return STQ_E_ARG;
+        if ((L.pool8 && !st->pool8) || (L.pool4 && !st->pool4)) return STQ_E_ARG;
+    }
+    if (st->desc.fmt == STQ_FMT_MIXED48 &&
+        (!st->colmax || !st->rowscore || !st->cal_colpart || !st->cal_rowpart))
+        return STQ_E_ARG;
+    return STQ_OK;
+}
+
+stq_status dev(hipError_t e) { return e == hipSuccess ? STQ_OK : STQ_E_DEVICE; }
+
+} // namespace
+
+extern "C" {
+
+int32_t stq_abi_version(void) { return 1; }
+
+const char *stq_status_str(int32_t s) {
+    switch (s) {
+    case STQ_OK: return "STQ_OK";
+    case STQ_E_ARG: return "STQ_E_ARG: null, misaligned or invalid argument";
+    case STQ_E_SHAPE: return "STQ_E_SHAPE: inconsistent dimensions";
+    case STQ_E_UNSUPPORTED: return "STQ_E_UNSUPPORTED: head dimension not compiled";
+    case STQ_E_SPACE: return "STQ_E_SPACE: buffer smaller than stq_state_bytes";
+    case STQ_E_STATE: return "STQ_E_STATE: mixed-precision state not calibrated";
+    case STQ_E_DEVICE: return "STQ_E_DEVICE: HIP launch or runtime failure";
+    default: return "unknown stq_status";
+    }
+}
+
+size_t stq_state_bytes(const stq_desc *desc) {
+    Layout L;
+    return describe(desc, &L) == STQ_OK ? L.total : 0;
+}
+
+stq_status stq_alloc_state(const stq_desc *desc, void *devp, size_t bytes, stq_stream_t stream,
+                           stq_state *out) {
+    if (!desc || !out || !devp) return STQ_E_ARG;
+    if (!aligned(devp, kAlign)) return STQ_E_ARG;
+    Layout L;
+    stq_status e = describe(desc, &L);
+    if (e != STQ_OK) return e;
+    if (bytes < L.total) return STQ_E_SPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *p = static_cast<char *>(devp);
+    stq_state st;
+    std::memset(&st, 0, sizeof(st));
+    st.desc = *desc;
+    auto take = [&p](size_t n) -> void * {
+        if (n == 0) return nullptr;
+        void *q = p;
+        p += round_up(n);
+        return q;
+    };
+    st.pool8 = static_cast<int8_t *>(take(L.pool8));
+    st.pool4 = static_cast<uint8_t *>(take(L.pool4));
+    st.r = static_cast<float *>(take(L.r));
+    st.c = static_cast<float *>(take(L.c));
+    st.perm = static_cast<int32_t *>(take(L.perm));
+    st.colmax = static_cast<float *>(take(L.colmax));
+    st.rowscore = static_cast<double *>(take(L.rowscore));
+    st.cal_colpart = static_cast<float *>(take(L.colpart));
+    st.cal_rowpart = static_cast<double *>(take(L.rowpart));
+    st.s32 = static_cast<float *>(take(L.s32));
+    st.calibrated = desc->fmt == STQ_FMT_MIXED48 ? 0 : 1;
+
+    const int D = desc->d_k;
+    hipError_t he = hipSuccess;
+    auto run = [&he](hipError_t x) {
+        if (he == hipSuccess) he = x;
+    };
+    if (L.pool8) run(stq::launch_fill_u32(reinterpret_cast<uint32_t *>(st.pool8), L.pool8 / 4, 0u, s));
+    if (L.pool4) run(stq::launch_fill_u32(reinterpret_cast<uint32_t *>(st.pool4), L.pool4 / 4, 0u, s));
+    if (L.r) run(stq::launch_fill_u32(reinterpret_cast<uint32_t *>(st.r), L.r / 4, kRowFloorBits, s));
+    run(stq::launch_fill_u32(reinterpret_cast<uint32_t *>(st.c), L.c / 4, kOneBits, s));
+    run(stq::launch_iota_rows(st.perm, desc->n_heads_v, D, s));
+    if (L.colmax) run(stq::launch_fill_u32(reinterpret_cast<uint32_t *>(st.colmax), L.colmax / 4, 0u, s));
+    if (L.rowscore) run(stq::launch_fill_u64(reinterpret_cast<uint64_t *>(st.rowscore), L.rowscore / 8, 0u, s));
+    if (L.s32) run(stq::launch_fill_u32(reinterpret_cast<uint32_t *>(st.s32), L.s32 / 4, 0u, s));
+    if (he != hipSuccess) return STQ_E_DEVICE;
+    *out = st;
+    return STQ_OK;
+}
+
+stq_status stq_calibrate(stq_state *st, const float *records, int64_t n_rec, uint32_t flags,
+                         stq_stream_t stream) {
+    stq_status e = check_state(st);
+    if (e != STQ_OK) return e;
+    if (st->desc.fmt != STQ_FMT_MIXED48) return STQ_E_ARG;
+    if (flags & ~(STQ_CAL_RESET | STQ_CAL_COLS | STQ_CAL_ROWS | STQ_CAL_FINALIZE)) return STQ_E_ARG;
+    if (n_rec < 0) return STQ_E_SHAPE;
+    const bool accumulate = (flags & (STQ_CAL_COLS | STQ_CAL_ROWS)) != 0;
+    if (accumulate && n_rec > 0 && (!records || !aligned(records, 16))) return STQ_E_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int D = st->desc.d_k, H = st->desc.n_heads_v;
+    stq::CalibArgs a;
+    a.records = records;
+    a.n_rec = n_rec;
+    a.Hv = H;
+    a.n8 = st->desc.n8;
+    a.do_cols = (flags & STQ_CAL_COLS) ? 1 : 0;
+    a.do_rows = (flags & STQ_CAL_ROWS) ? 1 : 0;
+    a.colmax = st->colmax;
+    a.rowscore = st->rowscore;
+    a.colpart = st->cal_colpart;
+    a.rowpart = st->cal_rowpart;
+    a.c = st->c;
+    a.perm = st->perm;
+    if (flags & STQ_CAL_RESET) {
+        if ((e = dev(stq::launch_fill_u32(reinterpret_cast<uint32_t *>(st->colmax),
+                                          static_cast<size_t>(H) * D, 0u, s))) != STQ_OK)
+            return e;
+        if ((e = dev(stq::launch_fill_u64(reinterpret_cast<uint64_t *>(st->rowscore),
+                                          static_cast<size_t>(H) * D, 0u, s))) != STQ_OK)
+            return e;
+    }
+    if (accumulate && n_rec > 0)
+        if ((e = dev(stq::launch_calib_accumulate(D, a, s))) != STQ_OK) return e;
+    if (flags & STQ_CAL_FINALIZE) {
+        if ((e = dev(stq::launch_calib_finalize(D, a, s))) != STQ_OK) return e;
+        st->calibrated = 1;
+    }
+    return STQ_OK;
+}
+
+stq_status stq_set_calibration(stq_state *st, const float *c, const int32_t *perm,
+                               stq_stream_t stream) {
+    stq_status e = check_state(st);
+    if (e != STQ_OK) return e;
+    if (st->desc.fmt != STQ_FMT_MIXED48) return STQ_E_ARG;
+    if (!c || !perm || !aligned(c, 16) || !aligned(perm, 16)) return STQ_E_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t n = static_cast<size_t>(st->desc.n_heads_v) * st->desc.d_k * 4;
+    if ((e = dev(stq::launch_copy_bytes(c, st->c, n, s))) != STQ_OK) return e;
+    if ((e = dev(stq::launch_copy_bytes(perm, st->perm, n, s))) != STQ_OK) return e;
+    st->calibrated = 1;
+    return STQ_OK;
+}
+
+namespace {
+
+stq_status batch_args(const stq_state *st, const int32_t *slots, int32_t B) {
+    stq_status e = check_state(st);
+    if (e != STQ_OK) return e;
+    if (B < 1 || B > st->desc.n_slots) return STQ_E_SHAPE;
+    if (slots && !aligned(slots, 4)) return STQ_E_ARG;
+    return STQ_OK;
+}
+
+stq::PackArgs pack_args(const stq_state *st, const int32_t *slots, int32_t B) {
+    stq::PackArgs a;
+    a.pool8 = st->pool8;
+    a.pool4 = st->pool4;
+    a.r = st->r;
+    a.c = st->c;
+    a.perm = st->perm;
+    a.slots = slots;
+    a.S_in = nullptr;
+    a.S_out = nullptr;
+    a.B = B;
+    a.Hv = st->desc.n_heads_v;
+    a.n8 = st->desc.n8;
+    a.n_slots = st->desc.n_slots;
+    return a;
+}
+
+} // namespace
+
+stq_status stq_pack_state(const stq_state *st, const float *S, const int32_t *slots, int32_t B,
+                          stq_stream_t stream) {
+    stq_status e = batch_args(st, slots, B);
+    if (e != STQ_OK) return e;
+    if (!S || !aligned(S, 16)) return STQ_E_ARG;
+    if (st->desc.fmt == STQ_FMT_MIXED48 && !st->calibrated) return STQ_E_STATE;
+    stq::PackArgs a = pack_args(st, slots, B);
+    a.S_in = S;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (st->desc.fmt == STQ_FMT_FP32) return dev(stq::launch_copy_slots_fp32(st->desc.d_k, a, true, st->s32, s));
+    return dev(stq::launch_pack(st->desc.d_k, a, s));
+}
+
+stq_status stq_dequant_state(const stq_state *st, const int32_t *slots, int32_t B, float *S_out,
+                             stq_stream_t stream) {
+    stq_status e = batch_args(st, slots, B);
+    if (e != STQ_OK) return e;
+    if (!S_out || !aligned(S_out, 16)) return STQ_E_ARG;
+    stq::PackArgs a = pack_args(st, slots, B);
+    a.S_out = S_out;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (st->desc.fmt == STQ_FMT_FP32) return dev(stq::launch_copy_slots_fp32(st->desc.d_k, a, false, st->s32, s));
+    return dev(stq::launch_dequant(st->desc.d_k, a, s));
+}
+
+stq_status stq_decode_step(const stq_state *st, const int32_t *slots, int32_t B, const void *q,
+                           const void *k, const void *v, int32_t dtype, const float *alpha,
+                           const float *beta, float *o, stq_stream_t stream) {
+    stq_status e = batch_args(st, slots, B);
+    if (e != STQ_OK) return e;
+    if (dtype != STQ_F32 && dtype != STQ_BF16) return STQ_E_ARG;
+    const size_t el = dtype == STQ_F32 ? 4 : 2;
+    if (!q || !k || !v || !alpha || !beta || !o) return STQ_E_ARG;
+    if (!aligned(q, el) || !aligned(k, el) || !aligned(v, el) || !aligned(alpha, 4) ||
+        !aligned(beta, 4) || !aligned(o, 4))
+        return STQ_E_ARG;
+    if (st->desc.fmt == STQ_FMT_MIXED48 && !st->calibrated) return STQ_E_STATE;
+    stq::DecodeArgs a;
+    a.pool8 = st->pool8;
+    a.pool4 = st->pool4;
+    a.r = st->r;
+    a.s32 = st->s32;
+    a.c = st->c;
+    a.perm = st->perm;
+    a.slots = slots;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.o = o;
+    a.B = B;
+    a.Hv = st->desc.n_heads_v;
+    a.Hk = st->desc.n_heads_k;
+    a.n8 = st->desc.n8;
+    a.n_slots = st->desc.n_slots;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool bf16 = dtype == STQ_BF16;
+    if (st->desc.fmt == STQ_FMT_FP32) return dev(stq::launch_decode_fp32(st->desc.d_k, bf16, a, s));
+    return dev(stq::launch_decode_mixed(st->desc.d_k, bf16, a, s));
+}
+
+stq_status stq_stream_copy(const void *src, void *dst, size_t bytes, stq_stream_t stream) {
+    if (!src || !dst || !aligned(src, 16) || !aligned(dst, 16) || bytes % 16 != 0) return STQ_E_ARG;
+    return dev(stq::launch_copy_bytes(src, dst, bytes, static_cast<hipStream_t>(stream)));
+}
+
+} // extern "C"

@@ -1,0 +1,71 @@
+// Internal declarations shared by the C-ABI layer and the HIP kernels of
+// libstq.so.  Not installed; the public interface is include/stq.h.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace stq {
+
+// One decode launch: B sequences x Hv value heads, in place on slots[b].
+struct DecodeArgs {
+    int8_t *pool8;        // [n_slots][Hv][n8][D]
+    uint8_t *pool4;       // [n_slots][Hv][D-n8][D/2]
+    float *r;             // [n_slots][Hv][D]
+    float *s32;           // [n_slots][Hv][D][D]   (FP32 format)
+    const float *c;       // [Hv][D]
+    const int32_t *perm;  // [Hv][D]
+    const int32_t *slots; // [B] or nullptr (identity)
+    const void *q;        // [B][Hk][D]
+    const void *k;        // [B][Hk][D]
+    const void *v;        // [B][Hv][D]
+    const float *alpha;   // [B][Hv]
+    const float *beta;    // [B][Hv]
+    float *o;             // [B][Hv][D]
+    int32_t B, Hv, Hk, n8, n_slots;
+};
+
+// Pack / dequant of B slots.
+struct PackArgs {
+    int8_t *pool8;
+    uint8_t *pool4;
+    float *r;
+    const float *c;
+    const int32_t *perm;
+    const int32_t *slots;
+    const float *S_in; // pack: [B][Hv][D][D] logical order
+    float *S_out;      // dequant: [B][Hv][D][D] logical order
+    int32_t B, Hv, n8, n_slots;
+};
+
+struct CalibArgs {
+    const float *records; // [n_rec][Hv][D][D]
+    int64_t n_rec;
+    int32_t Hv, n8;
+    int32_t do_cols, do_rows;
+    float *colmax;       // [Hv][D]
+    double *rowscore;    // [Hv][D]
+    float *colpart;      // [Hv][chunks][D]
+    double *rowpart;     // [Hv][chunks][D]
+    float *c;            // [Hv][D]
+    int32_t *perm;       // [Hv][D]
+};
+
+constexpr int kCalChunks = 64;
+
+// Launchers (return hipSuccess or the launch error).  D in {16, 32, 64, 128}.
+hipError_t launch_decode_mixed(int D, bool bf16, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_fp32(int D, bool bf16, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_pack(int D, const PackArgs &a, hipStream_t s);
+hipError_t launch_dequant(int D, const PackArgs &a, hipStream_t s);
+hipError_t launch_copy_slots_fp32(int D, const PackArgs &a, bool to_state, float *s32,
+                                  hipStream_t s);
+hipError_t launch_calib_accumulate(int D, const CalibArgs &a, hipStream_t s);
+hipError_t launch_calib_finalize(int D, const CalibArgs &a, hipStream_t s);
+hipError_t launch_fill_u32(uint32_t *dst, size_t n, uint32_t value, hipStream_t s);
+hipError_t launch_fill_u64(uint64_t *dst, size_t n, uint64_t value, hipStream_t s);
+hipError_t launch_iota_rows(int32_t *perm, int rows, int D, hipStream_t s);
+hipError_t launch_copy_bytes(const void *src, void *dst, size_t bytes, hipStream_t s);
+
+} // namespace stq

@@ -191,12 +191,21 @@ class PackedState:
 
 def random_packed_state(B: int, hv: int, d: int, n8: int, *, seed: int,
                         c_one: bool = False, identity_perm: bool = False,
+                        full_rows: bool = False,
                         r_log10_range: tuple[float, float] = (-2.0, 0.5)) -> PackedState:
     """A valid packed state drawn directly: codes uniform on the symmetric range
-    of each row width, log-uniform row factors, log-normal column factors."""
+    of each row width, log-uniform row factors, log-normal column factors.
+    With full_rows, one random entry of every row is set to +-(top code) so
+    that every row spans its whole range."""
     g = rng_for(seed, _TAG_PACKED)
     pool8 = g.integers(-127, 128, size=(B, hv, n8, d), dtype=np.int16).astype(np.int8)
     nib = g.integers(-7, 8, size=(B, hv, d - n8, d), dtype=np.int16).astype(np.int8)
+    if full_rows:
+        for arr, top in ((pool8, 127), (nib, 7)):
+            if arr.size:
+                col = g.integers(0, d, size=arr.shape[:-1])
+                sign = np.where(g.random(arr.shape[:-1]) < 0.5, -1, 1).astype(np.int8)
+                np.put_along_axis(arr, col[..., None], (sign * top)[..., None], axis=-1)
     lo = nib[..., 0::2].astype(np.uint8) & 0x0F
     hi = nib[..., 1::2].astype(np.uint8) & 0x0F
     pool4 = (lo | (hi << 4)).astype(np.uint8)

@@ -1,0 +1,164 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and exports
+every function include/stq.h declares, the layout arithmetic is right, and
+every rejection path returns its documented status before anything is queued
+(the pointers used here are never dereferenced because validation fails
+first)."""
+from __future__ import annotations
+
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "stq.h"
+
+stq = pytest.importorskip("linear_attention_recurrent_rule_amd.stq")
+
+E_ARG, E_SHAPE, E_UNSUPPORTED, E_SPACE, E_STATE = 1, 2, 3, 4, 5
+FAKE = 0x10000000  # an aligned address that validation must reject before use
+
+
+def _declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(stq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = stq.lib()
+    names = _declared_functions()
+    assert "stq_decode_step" in names and len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), f"libstq.so does not export {n}"
+    assert lib.stq_abi_version() == 1
+
+
+def _desc(n_slots=4, hv=4, hk=2, d=64, n8=32, fmt=stq.FMT_MIXED48, dv=None):
+    return stq.Desc(n_slots, hv, hk, d, d if dv is None else dv, n8, fmt)
+
+
+def _bytes(**kw):
+    return stq.lib().stq_state_bytes(ctypes.byref(_desc(**kw)))
+
+
+def _r(n):
+    return (n + 255) // 256 * 256
+
+
+def test_state_bytes_layout_arithmetic():
+    # mixed 6-bit, d = 128, 1024 slots x 32 heads (the serving pool sizes)
+    S, H, D, n8 = 1024, 32, 128, 64
+    expect = (_r(S * H * n8 * D) + _r(S * H * (D - n8) * D // 2) + _r(S * H * D * 4)
+              + _r(H * D * 4) * 2 + _r(H * D * 4) + _r(H * D * 8)
+              + _r(H * 64 * D * 4) + _r(H * 64 * D * 8))
+    assert _bytes(n_slots=S, hv=H, hk=16, d=D, n8=n8) == expect
+    # the state itself: 12,800 B per (slot, head) at the 6-bit mix = 6.25 bits/value
+    per_unit = n8 * D + (D - n8) * D // 2 + D * 4
+    assert per_unit == 12800 and per_unit * 8 / (D * D) == 6.25
+    # INT8ROW: codes + r, no calibration buffers
+    assert _bytes(n_slots=S, hv=H, hk=16, d=D, n8=D, fmt=stq.FMT_INT8ROW) == (
+        _r(S * H * D * D) + _r(S * H * D * 4) + _r(H * D * 4) * 2)
+    # FP32 state
+    assert _bytes(n_slots=8, hv=4, hk=4, d=64, n8=0, fmt=stq.FMT_FP32) == (
+        _r(8 * 4 * 64 * 64 * 4) + _r(4 * 64 * 4) * 2)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(d=48),                       # not compiled
+    dict(d=256),                      # not compiled
+    dict(d=64, dv=32),                # d_k != d_v
+    dict(hv=3, hk=2),                 # Hv % Hk
+    dict(n8=65),                      # n8 > d_k
+    dict(n8=-1),
+    dict(n_slots=0),
+    dict(fmt=7),
+    dict(fmt=stq.FMT_INT8ROW, n8=32),  # INT8ROW needs n8 = d_k
+])
+def test_state_bytes_rejects_bad_geometry(kw):
+    assert _bytes(**kw) == 0
+
+
+def test_alloc_state_rejections():
+    lib = stq.lib()
+    out = stq.CState()
+    d = _desc()
+    need = lib.stq_state_bytes(ctypes.byref(d))
+    assert lib.stq_alloc_state(None, FAKE, need, None, ctypes.byref(out)) == E_ARG
+    assert lib.stq_alloc_state(ctypes.byref(d), None, need, None, ctypes.byref(out)) == E_ARG
+    assert lib.stq_alloc_state(ctypes.byref(d), FAKE + 16, need, None, ctypes.byref(out)) == E_ARG
+    assert lib.stq_alloc_state(ctypes.byref(d), FAKE, need - 1, None, ctypes.byref(out)) == E_SPACE
+    assert lib.stq_alloc_state(ctypes.byref(_desc(d=48)), FAKE, need, None,
+                               ctypes.byref(out)) == E_UNSUPPORTED
+    assert lib.stq_alloc_state(ctypes.byref(_desc(hv=3)), FAKE, need, None,
+                               ctypes.byref(out)) == E_SHAPE
+
+
+def _fake_state(fmt=stq.FMT_MIXED48, calibrated=0, n8=32, d=64, n_slots=4):
+    st = stq.CState()
+    st.desc = _desc(fmt=fmt, n8=n8, d=d, n_slots=n_slots)
+    for i, f in enumerate(("pool8", "pool4", "r", "c", "perm", "colmax", "rowscore",
+                           "cal_colpart", "cal_rowpart", "s32")):
+        setattr(st, f, FAKE + 0x1000000 * (i + 1))
+    st.calibrated = calibrated
+    return st
+
+
+def _decode(st, B=2, dtype=0, slots=None, ptrs=None):
+    p = ptrs or [FAKE] * 6
+    return stq.lib().stq_decode_step(ctypes.byref(st), slots, B, p[0], p[1], p[2], dtype,
+                                     p[3], p[4], p[5], None)
+
+
+def test_decode_rejections():
+    st = _fake_state(calibrated=0)
+    assert _decode(st) == E_STATE  # mixed state before calibration
+    st = _fake_state(calibrated=1)
+    assert _decode(st, B=0) == E_SHAPE
+    assert _decode(st, B=5) == E_SHAPE  # more sequences than slots
+    assert _decode(st, dtype=2) == E_ARG
+    assert _decode(st, ptrs=[FAKE, FAKE, None, FAKE, FAKE, FAKE]) == E_ARG
+    assert _decode(st, ptrs=[FAKE + 1, FAKE, FAKE, FAKE, FAKE, FAKE], dtype=1) == E_ARG
+    assert _decode(st, slots=FAKE + 2) == E_ARG
+    bad = _fake_state(calibrated=1)
+    bad.pool8 = None
+    assert _decode(bad) == E_ARG
+    bad = _fake_state(calibrated=1)
+    bad.desc.n_heads_k = 3
+    assert _decode(bad) == E_SHAPE
+    assert stq.lib().stq_decode_step(None, None, 1, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE,
+                                     None) == E_ARG
+
+
+def test_pack_dequant_calibrate_rejections():
+    lib = stq.lib()
+    st = _fake_state(calibrated=0)
+    assert lib.stq_pack_state(ctypes.byref(st), FAKE, None, 2, None) == E_STATE
+    st = _fake_state(calibrated=1)
+    assert lib.stq_pack_state(ctypes.byref(st), None, None, 2, None) == E_ARG
+    assert lib.stq_pack_state(ctypes.byref(st), FAKE + 4, None, 2, None) == E_ARG
+    assert lib.stq_pack_state(ctypes.byref(st), FAKE, None, 9, None) == E_SHAPE
+    assert lib.stq_dequant_state(ctypes.byref(st), None, 0, FAKE, None) == E_SHAPE
+    assert lib.stq_dequant_state(ctypes.byref(st), None, 2, None, None) == E_ARG
+    assert lib.stq_calibrate(ctypes.byref(st), FAKE, 1, 64, None) == E_ARG  # unknown flag
+    assert lib.stq_calibrate(ctypes.byref(st), FAKE, -1, stq.CAL_COLS, None) == E_SHAPE
+    assert lib.stq_calibrate(ctypes.byref(st), None, 3, stq.CAL_COLS, None) == E_ARG
+    i8 = _fake_state(fmt=stq.FMT_INT8ROW, calibrated=1, n8=64)
+    assert lib.stq_calibrate(ctypes.byref(i8), FAKE, 1, stq.CAL_COLS, None) == E_ARG
+    assert lib.stq_set_calibration(ctypes.byref(i8), FAKE, FAKE, None) == E_ARG
+    assert lib.stq_set_calibration(ctypes.byref(st), None, FAKE, None) == E_ARG
+
+
+def test_stream_copy_rejections():
+    lib = stq.lib()
+    assert lib.stq_stream_copy(None, FAKE, 16, None) == E_ARG
+    assert lib.stq_stream_copy(FAKE, FAKE + 8, 16, None) == E_ARG
+    assert lib.stq_stream_copy(FAKE, FAKE, 15, None) == E_ARG
+
+
+def test_status_strings():
+    lib = stq.lib()
+    for s in range(7):
+        assert lib.stq_status_str(s).decode().startswith("STQ_")
+    assert lib.stq_status_str(99) == b"unknown stq_status"
