@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Throughput of the quantized gated delta-rule decode step on one MI355X.
+
+One "step" is one decode step of the whole batch: every (sequence, value head)
+state is dequantized, updated, read out, requantized and written back once.
+Metric: quantized state-updates/s (sequence x head x step) and the algorithmic
+HBM bytes/s of the decode kernel as a fraction of MI355X peak (8 TB/s).
+
+Default workload: B = 1024 sequences, 32 value heads sharing 16 key heads,
+128 x 128 states at the 6-bit mix (64 rows 8-bit, 64 rows 4-bit per head,
+fp32 row factors, calibrated column factors), bf16 q/k/v, synthetic seeded
+inputs.  The timed loop rotates over --pools independent state pools so the
+working set (pools x 419 MB) exceeds the 256 MB Infinity Cache.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
+COUNTERS_FILE = ROOT / "profiles" / "decode_counters.json"
+DECODE_SRC = ROOT / "linear_attention_recurrent_rule_amd" / "csrc" / "decode.hip"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="highconc_6bit")
+    p.add_argument("--pools", type=int, default=4, help="state pools rotated in the timed loop")
+    p.add_argument("--window", type=int, default=16, help="distinct input steps cycled")
+    p.add_argument("--no-variants", action="store_true", help="skip the comparison formats")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only-decode", action="store_true",
+                   help="time the main workload only (for profiler runs)")
+    return p.parse_args()
+
+
+def unit_state_bytes(fmt: str, d: int, n8: int) -> int:
+    if fmt == "fp32":
+        return 4 * d * d
+    if fmt == "int8row":
+        return d * d + 4 * d
+    return n8 * d + (d - n8) * d // 2 + 4 * d
+
+
+def algorithmic_bytes(fmt: str, B: int, hv: int, hk: int, d: int, n8: int, in_el: int) -> int:
+    """Bytes one decode launch must move: read + write of every state, q and k
+    once per key head, v, alpha, beta once per value head, o written once."""
+    state = 2 * unit_state_bytes(fmt, d, n8) * B * hv
+    vecs = B * hk * 2 * d * in_el + B * hv * (d * in_el + 8 + 4 * d)
+    return state + vecs
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        log("bench.py measures one GPU: this build has no multi-GPU path (every decode unit is "
+            "independent; see the sharding notes in DESIGN.md). Run with --gpus 1.")
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from linear_attention_recurrent_rule_amd import stq
+    from linear_attention_recurrent_rule_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    stq.lib()  # fails loudly if libstq.so is missing
+    w = wl.WORKLOADS[args.workload]
+    B, hv, hk, d = w.B, w.hv, w.hk, w.d
+    in_el = 2 if w.dtype == "bf16" else 4
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+
+    def to_dev_inputs(x):
+        if x.dtype == "bf16":
+            cv = lambda bits: dev(bits.view(np.int16)).view(torch.bfloat16)  # noqa: E731
+            return cv(x.q_bits), cv(x.k_bits), cv(x.v_bits), dev(x.alpha), dev(x.beta)
+        return dev(x.q), dev(x.k), dev(x.v), dev(x.alpha), dev(x.beta)
+
+    # ---------------------------------------------------------------- setup --
+    t0 = time.time()
+    log(f"[bench] workload {w.name}: B={B} Hv={hv} Hk={hk} d={d} n8={w.n8} {w.dtype}")
+    S0 = dev(wl.initial_state(w))
+    log(f"[bench] S0 generated ({S0.numel() * 4 / 2**30:.2f} GiB) in {time.time() - t0:.1f}s")
+
+    # offline calibration: 32 unquantized steps on the calibration stream
+    fp_cal = stq.State(stq.Geometry(B, hv, hk, d, 0, stq.FMT_FP32))
+    fp_cal.pack(S0)
+    cal = stq.State(stq.Geometry(1, hv, hk, d, w.n8, stq.FMT_MIXED48))
+    cal.calibrate(None, stq.CAL_RESET)
+    for t in range(w.calib_steps):
+        q, k, v, a, b = to_dev_inputs(wl.workload_inputs(w, t, calibration=True))
+        fp_cal.decode_step(q, k, v, a, b)
+        last = t == w.calib_steps - 1
+        cal.calibrate(fp_cal.s32, stq.CAL_COLS | (stq.CAL_ROWS if last else 0))
+    cal.calibrate(None, stq.CAL_FINALIZE)
+    c, perm = cal.c.clone(), cal.perm.clone()
+    del fp_cal
+    torch.cuda.synchronize()
+    log(f"[bench] calibrated in {time.time() - t0:.1f}s")
+
+    window = [to_dev_inputs(wl.workload_inputs(w, t)) for t in range(args.window)]
+    o = torch.empty((B, hv, d), dtype=torch.float32, device="cuda")
+
+    def make_pools(fmt: int, n8: int, n: int):
+        pools = []
+        for _ in range(n):
+            st = stq.State(stq.Geometry(B, hv, hk, d, n8, fmt))
+            if fmt == stq.FMT_MIXED48:
+                st.set_calibration(c, perm)
+            st.pack(S0)
+            pools.append(st)
+        torch.cuda.synchronize()
+        return pools
+
+    def time_decode(pools, steps, warmup):
+        """Per-launch HIP events on the launch stream + one pair around the loop."""
+        stream = torch.cuda.current_stream()
+        for t in range(warmup):
+            q, k, v, a, b = window[t % len(window)]
+            pools[t % len(pools)].decode_step(q, k, v, a, b, o=o)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for t in range(steps):
+            q, k, v, a, b = window[t % len(window)]
+            ev[t][0].record(stream)
+            pools[t % len(pools)].decode_step(q, k, v, a, b, o=o)
+            ev[t][1].record(stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        total_ms = start.elapsed_time(end)
+        per = [s.elapsed_time(e) for s, e in ev]
+        return total_ms, float(np.mean(per)), float(np.median(per))
+
+    def measure(fmt_name: str, fmt: int, n8: int, npools: int, steps: int, warmup: int):
+        pools = make_pools(fmt, n8, npools)
+        total_ms, mean_ms, med_ms = time_decode(pools, steps, warmup)
+        nbytes = algorithmic_bytes(fmt_name, B, hv, hk, d, n8, in_el)
+        res = dict(updates_per_s=B * hv * steps / (total_ms / 1e3), ms_per_step=total_ms / steps,
+                   kernel_ms_mean=mean_ms, kernel_ms_median=med_ms,
+                   algorithmic_bytes_per_launch=nbytes,
+                   hbm_gbps=nbytes / (mean_ms / 1e3) / 1e9,
+                   frac_of_peak=nbytes / (mean_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
+                   pools=npools, pool_bytes=int(pools[0].buffer.numel()))
+        del pools
+        torch.cuda.empty_cache()
+        return res
+
+    # ------------------------------------------------------------ main run --
+    main_res = measure("mixed", stq.FMT_MIXED48, w.n8, args.pools, args.steps, args.warmup)
+    log(f"[bench] main: {main_res['updates_per_s'] / 1e6:.1f} M updates/s, "
+        f"{main_res['hbm_gbps']:.0f} GB/s ({100 * main_res['frac_of_peak']:.1f}% of peak)")
+
+    variants = {}
+    copy_gbps = None
+    if not args.only_decode and not args.no_variants:
+        variants["single_pool_as_stated"] = measure("mixed", stq.FMT_MIXED48, w.n8, 1,
+                                                    args.steps, args.warmup)
+        if w.n8 != 16:
+            variants["mix_4p5bit_n8_16"] = measure("mixed", stq.FMT_MIXED48, 16, args.pools,
+                                                   args.steps, args.warmup)
+        variants["int8row"] = measure("int8row", stq.FMT_INT8ROW, d, args.pools, args.steps,
+                                      args.warmup)
+        variants["fp32_state"] = measure("fp32", stq.FMT_FP32, 0, 2, args.steps, args.warmup)
+        for k_, v_ in variants.items():
+            log(f"[bench] {k_}: {v_['updates_per_s'] / 1e6:.1f} M updates/s, "
+                f"{v_['hbm_gbps']:.0f} GB/s")
+        # practical ceiling: a plain streaming copy of 2 GiB
+        src = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            stq.stream_copy(src, dst)
+        torch.cuda.synchronize()
+        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_ev.record()
+        for _ in range(10):
+            stq.stream_copy(src, dst)
+        e_ev.record()
+        torch.cuda.synchronize()
+        copy_gbps = 2 * src.numel() * 10 / (s_ev.elapsed_time(e_ev) / 1e3) / 1e9
+        del src, dst
+        log(f"[bench] streaming copy ceiling: {copy_gbps:.0f} GB/s")
+
+    # ------------------------------------------------------- CPU baseline --
+    cpu = None
+    if not args.no_cpu_baseline and not args.only_decode:
+        import oracle
+
+        threads = oracle.default_threads()
+        ps = wl.random_packed_state(B, hv, d, w.n8, seed=w.seed + 700)
+        x = wl.workload_inputs(w, 0)
+        t1 = time.perf_counter()
+        oracle.step(ps.pool8, ps.pool4, ps.r, ps.c, ps.perm, x.q, x.k, x.v, x.alpha, x.beta,
+                    n8=w.n8, nthreads=threads)
+        dt = time.perf_counter() - t1
+        cpu = dict(value=B * hv / dt, unit="state-updates/s", cores=threads, kind="oracle",
+                   sample=f"one full decode step of the workload ({B * hv} units, d={d}, "
+                          f"n8={w.n8}) from a seeded random packed state, {dt:.1f}s wall")
+        log(f"[bench] oracle: {cpu['value']:.0f} updates/s on {threads} threads")
+
+    # -------------------------------------------------------- roofline etc --
+    traffic = None
+    if COUNTERS_FILE.exists():
+        try:
+            cnt = json.loads(COUNTERS_FILE.read_text())
+            sha = hashlib.sha256(DECODE_SRC.read_bytes()).hexdigest()
+            if cnt.get("decode_source_sha256") == sha and cnt.get("workload") == w.name:
+                traffic = cnt.get("hbm_bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+    achieved = main_res["hbm_gbps"]
+    line = {
+        "metric": "quantized state-updates/s (seq*head*step) + % of MI355X peak HBM GB/s",
+        "value": main_res["updates_per_s"],
+        "unit": "state-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: B={B}, Hv={hv} value heads over Hk={hk} key heads, "
+                        f"d_k=d_v={d}, n8={w.n8} 8-bit rows + {d - w.n8} 4-bit rows per head "
+                        f"({8 * unit_state_bytes('mixed', d, w.n8) / (d * d):.2f} bits/value), "
+                        f"{w.dtype} q/k/v, {args.pools} rotated pools (MALL-cold)",
+            "global_batch": B, "heads_v": hv, "heads_k": hk, "d": d, "n8": w.n8,
+            "parallelism": "single GPU",
+        },
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
+        "cpu_baseline": cpu,
+        "hbm_gbps": achieved,
+        "kernel_ms_mean": main_res["kernel_ms_mean"],
+        "algorithmic_bytes_per_launch": main_res["algorithmic_bytes_per_launch"],
+        "copy_ceiling_gbps": copy_gbps,
+        "variants": variants,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

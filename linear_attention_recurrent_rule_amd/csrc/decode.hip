@@ -397,6 +397,7 @@ hipError_t launch_fp32_d(bool bf16, const DecodeArgs &a, hipStream_t s) {
 } // namespace
 
 hipError_t launch_decode_mixed(int D, bool bf16, const DecodeArgs &a, hipStream_t s) {
+    if (D == 128 && decode128_supported(a.n8)) return launch_decode128(a.n8, bf16, a, s);
     switch (D) {
     case 16: return launch_mixed_d<16>(bf16, a, s);
     case 32: return launch_mixed_d<32>(bf16, a, s);

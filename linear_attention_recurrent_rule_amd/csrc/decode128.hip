@@ -1,0 +1,362 @@
+// Decode step specialised for 128 x 128 heads and a compile-time 4/8-bit row
+// split (n8 a multiple of 16): the serving shapes.  Same arithmetic contract as
+// decode.hip (STEPQuant paper, Sec. 2.1 Eq. (1) with D_t = a I; Sec. 2.2
+// quantizer; Sec. 4.3 representation; App. C.3 Table C2 step order), arranged
+// to keep the vector ALU count per state entry low:
+//
+//  * one workgroup of 256 lanes per (slot, head); lane (g, c), g = lane / 16,
+//    c = lane % 16, owns columns 8c..8c+7 of physical rows g + 16 m, m = 0..7;
+//    with n8 a multiple of 16, row m of every lane is 8-bit iff m < n8 / 16,
+//    so the row width is a compile-time property of m and no lane diverges;
+//  * per-row factors are formed once per row by the staging lanes and read
+//    from LDS: r k and r q (with 1/16 folded in for 4-bit rows, whose codes are
+//    widened as 16 z), and the update in the form
+//        x_ij = X_ij / c_j = s_i (P_i z_ij + E_ij)
+//    with s_i = b k_i, P_i = a r_i / (b k_i), E_ij = e_j for a row whose b k_i
+//    is not negligible next to a r_i, and s_i = 1, P_i = a r_i, E_ij = 0 for a
+//    row where |b k_i| <= 2^-64 |a r_i| (then b k_i e_j is below fp32
+//    resolution against any non-zero code).  Either way one FMA per entry;
+//    the lane picks e or a zero vector per row by its LDS address;
+//  * the row absmax over the 16 lanes of a row is a DPP reduce-scatter that
+//    leaves row c / 2 in lane c, so each lane derives one row factor and its
+//    reciprocal, and the 8 multipliers are exchanged through LDS;
+//  * codes: one FMA adds 1.5 * 2^23 (round-half-even to an integer in the low
+//    mantissa bits), then bytes are gathered with v_perm and nibbles with one
+//    shift and one bit-field insert per 8 codes.
+#include <hip/hip_runtime.h>
+
+#include "stq_internal.h"
+
+namespace stq {
+namespace {
+
+constexpr int D = 128;
+constexpr float kRoundMagic = 12582912.0f;               // 1.5 * 2^23
+constexpr float kRowFloor = 1.17549435082228750797e-38f; // 2^-126
+constexpr float kMulMax = 1.70141183460469231732e38f;    // 2^127
+constexpr float kFormTiny = 5.42101086242752217004e-20f; // 2^-64
+
+template <typename T> struct In;
+template <> struct In<float> {
+    static __device__ __forceinline__ float get(const void *p, unsigned i) {
+        return static_cast<const float *>(p)[i];
+    }
+};
+template <> struct In<uint16_t> {
+    static __device__ __forceinline__ float get(const void *p, unsigned i) {
+        return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(p)[i]) << 16);
+    }
+};
+
+__device__ __forceinline__ float sbyte(uint32_t w, int k) {
+    return static_cast<float>(static_cast<int8_t>(w >> (8 * k)));
+}
+
+// DPP lane exchange inside 16-lane rows (controls from the GFX9 DPP encoding).
+template <int CTRL> __device__ __forceinline__ uint32_t dpp(uint32_t v) {
+    return static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kRowRor8 = 0x128;       // lane l <- lane l^8 within the row
+constexpr int kRowHalfMirror = 0x141; // lane l <- lane 7-l within each half row
+constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+
+struct Smem {
+    float2 rkq[D];          // {r k, r q} per physical row (1/16 folded for 4-bit)
+    float4 row[D];          // {P, s, -, offset of E in ez} per physical row
+    float v[D], c[D];
+    float ez[2 * D];        // e (first half) and a zero vector (second half)
+    float red[2][16][D];    // column partials of u~ and w~ per row group
+    float kq[2];
+    float mul[16][8];       // per row group: code multipliers of its 8 rows
+};
+
+struct Lane {
+    int t, c, g;
+    unsigned unit;
+    float alpha, beta;
+    int8_t *p8;
+    uint8_t *p4;
+    float *rr;
+};
+
+// Fetch this lane's packed rows (Table C2 step 1).
+template <int N8>
+__device__ __forceinline__ void load_codes(const Lane &L, uint32_t (&w0)[8], uint32_t (&w1)[8]) {
+    constexpr int M8 = N8 / 16;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const unsigned p = static_cast<unsigned>(L.g + 16 * m);
+        if (m < M8) {
+            const uint2 v2 = *reinterpret_cast<const uint2 *>(L.p8 + (p * D + 8 * L.c));
+            w0[m] = v2.x;
+            w1[m] = v2.y;
+        } else {
+            w0[m] = *reinterpret_cast<const uint32_t *>(L.p4 + ((p - N8) * (D / 2) + 4 * L.c));
+            w1[m] = 0u;
+        }
+    }
+}
+
+// Everything after the staging barrier.
+template <int N8>
+__device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const Lane &L,
+                                            const uint32_t (&w0)[8], const uint32_t (&w1)[8]) {
+    constexpr int M8 = N8 / 16;
+    const int t = L.t, c = L.c, g = L.g;
+
+    // ---- widen the codes and accumulate this lane's share of u~ and w~
+    float z[8][8];
+    float pu[8], pw[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        pu[e] = 0.0f;
+        pw[e] = 0.0f;
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const float2 f = sh.rkq[g + 16 * m];
+        if (m < M8) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                z[m][e] = sbyte(w0[m], e);
+                z[m][4 + e] = sbyte(w1[m], e);
+            }
+        } else {
+            const uint32_t hi = w0[m] & 0xF0F0F0F0u;         // odd columns, x16
+            const uint32_t lo = (w0[m] << 4) & 0xF0F0F0F0u;  // even columns, x16
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                z[m][2 * e] = sbyte(lo, e);
+                z[m][2 * e + 1] = sbyte(hi, e);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            pu[e] = __builtin_fmaf(f.x, z[m][e], pu[e]);
+            pw[e] = __builtin_fmaf(f.y, z[m][e], pw[e]);
+        }
+    }
+    *reinterpret_cast<float4 *>(&sh.red[0][g][8 * c]) = make_float4(pu[0], pu[1], pu[2], pu[3]);
+    *reinterpret_cast<float4 *>(&sh.red[0][g][8 * c + 4]) = make_float4(pu[4], pu[5], pu[6], pu[7]);
+    *reinterpret_cast<float4 *>(&sh.red[1][g][8 * c]) = make_float4(pw[0], pw[1], pw[2], pw[3]);
+    *reinterpret_cast<float4 *>(&sh.red[1][g][8 * c + 4]) = make_float4(pw[4], pw[5], pw[6], pw[7]);
+    __syncthreads();
+
+    // ---- column sums: u~ (lanes 0..127) -> e;  w~ (lanes 128..255) kept for o
+    float wsum = 0.0f;
+    {
+        const int half = t >> 7;
+        const int j = t & (D - 1);
+        float s = 0.0f;
+#pragma unroll
+        for (int gg = 0; gg < 16; ++gg) s += sh.red[half][gg][j];
+        if (half == 0)
+            sh.ez[j] = __builtin_fmaf(-L.alpha, s, sh.v[j] / sh.c[j]);
+        else
+            wsum = s;
+    }
+    __syncthreads();
+
+    // ---- Table C2 step 3: readout of the updated state, before requantizing
+    if (t >= D) {
+        const int j = t - D;
+        const float kq = sh.kq[0] + sh.kq[1];
+        a.o[static_cast<size_t>(L.unit) * D + j] =
+            sh.c[j] * __builtin_fmaf(L.alpha, wsum, (L.beta * kq) * sh.ez[j]);
+    }
+
+    // ---- Table C2 steps 2 and 4: updated entries and row absmax
+    uint32_t amax[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const float4 rp = sh.row[g + 16 * m];
+        const float *E = &sh.ez[__float_as_int(rp.w) + 8 * c];
+        const float4 e0 = *reinterpret_cast<const float4 *>(E);
+        const float4 e1 = *reinterpret_cast<const float4 *>(E + 4);
+        const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+        float mx = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            z[m][e] = __builtin_fmaf(rp.x, z[m][e], ev[e]); // x / s
+            mx = fmaxf(mx, fabsf(z[m][e]));
+        }
+        amax[m] = __float_as_uint(mx);
+    }
+    // reduce-scatter over the 16 lanes of the row group: lane c ends with row
+    // c / 2 (non-negative floats order like their bit patterns: integer max)
+    const bool hiHalf = (c & 8) != 0;
+    const bool upper = (c & 4) != 0;
+    const bool q2 = (c & 2) != 0;
+    uint32_t r1[4], r2[2];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t keep = hiHalf ? amax[k + 4] : amax[k];
+        const uint32_t send = hiHalf ? amax[k] : amax[k + 4];
+        r1[k] = max(keep, dpp<kRowRor8>(send));
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const uint32_t keep = upper ? r1[k + 2] : r1[k];
+        const uint32_t send = upper ? r1[k] : r1[k + 2];
+        r2[k] = max(keep, dpp<kRowHalfMirror>(send));
+    }
+    float rmax;
+    {
+        const uint32_t keep = q2 ? r2[1] : r2[0];
+        const uint32_t send = q2 ? r2[0] : r2[1];
+        uint32_t v = max(keep, dpp<kQuadXor2>(send));
+        v = max(v, dpp<kQuadXor1>(v));
+        rmax = __uint_as_float(v);
+    }
+    {
+        const int mm = c >> 1;
+        const int p = g + 16 * mm;
+        const float sc = sh.row[p].y;
+        const float mrow = fabsf(sc) * rmax;
+        const float qinv = (mm < M8) ? (1.0f / 127.0f) : (1.0f / 7.0f);
+        const float rn = fmaxf(mrow * qinv, kRowFloor);
+        const float inv = __builtin_amdgcn_rcpf(rn);
+        float mul = sc * inv;
+        mul = fminf(fmaxf(mul, -kMulMax), kMulMax);
+        if ((c & 1) == 0) {
+            L.rr[p] = rn;
+            sh.mul[g][mm] = mul;
+        }
+    }
+    __syncthreads();
+
+    // ---- Table C2 step 6: codes against the stored factors, pack, write back
+    float mulv[8];
+    {
+        const float4 m0 = *reinterpret_cast<const float4 *>(&sh.mul[g][0]);
+        const float4 m1 = *reinterpret_cast<const float4 *>(&sh.mul[g][4]);
+        mulv[0] = m0.x; mulv[1] = m0.y; mulv[2] = m0.z; mulv[3] = m0.w;
+        mulv[4] = m1.x; mulv[5] = m1.y; mulv[6] = m1.z; mulv[7] = m1.w;
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const unsigned p = static_cast<unsigned>(g + 16 * m);
+        uint32_t bt[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bt[e] = __float_as_uint(__builtin_fmaf(z[m][e], mulv[m], kRoundMagic));
+        if (m < M8) {
+            const uint32_t a01 = __builtin_amdgcn_perm(bt[1], bt[0], 0x0C0C0400u);
+            const uint32_t a23 = __builtin_amdgcn_perm(bt[3], bt[2], 0x04000C0Cu);
+            const uint32_t a45 = __builtin_amdgcn_perm(bt[5], bt[4], 0x0C0C0400u);
+            const uint32_t a67 = __builtin_amdgcn_perm(bt[7], bt[6], 0x04000C0Cu);
+            *reinterpret_cast<uint2 *>(L.p8 + (p * D + 8 * c)) = make_uint2(a01 | a23, a45 | a67);
+        } else {
+            // even columns -> low nibbles, odd columns -> high nibbles
+            const uint32_t ev02 = __builtin_amdgcn_perm(bt[2], bt[0], 0x0C0C0400u);
+            const uint32_t ev46 = __builtin_amdgcn_perm(bt[6], bt[4], 0x04000C0Cu);
+            const uint32_t od13 = __builtin_amdgcn_perm(bt[3], bt[1], 0x0C0C0400u);
+            const uint32_t od57 = __builtin_amdgcn_perm(bt[7], bt[5], 0x04000C0Cu);
+            const uint32_t evn = ev02 | ev46;
+            const uint32_t odd = (od13 | od57) << 4;
+            const uint32_t word = (evn & 0x0F0F0F0Fu) | (odd & 0xF0F0F0F0u);
+            *reinterpret_cast<uint32_t *>(L.p4 + ((p - N8) * (D / 2) + 4 * c)) = word;
+        }
+    }
+}
+
+template <int N8, typename TIn>
+__global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_remap) {
+    static_assert(N8 % 16 == 0 && N8 >= 0 && N8 <= D, "n8 must be a multiple of 16");
+    __shared__ Smem sh;
+
+    Lane L;
+    L.t = threadIdx.x;
+    L.c = L.t & 15;
+    L.g = L.t >> 4;
+    const int t = L.t;
+    unsigned unit = blockIdx.x;
+    if (xcd_remap) {
+        // workgroups are dealt round-robin to the 8 XCDs; give each XCD a
+        // contiguous range of units so value heads sharing a key head (and
+        // their q, k) meet in the same L2
+        const unsigned per = gridDim.x >> 3;
+        unit = (blockIdx.x & 7u) * per + (blockIdx.x >> 3);
+    }
+    L.unit = unit;
+    const int Hv = a.Hv;
+    const int b = static_cast<int>(unit / static_cast<unsigned>(Hv));
+    const int h = static_cast<int>(unit % static_cast<unsigned>(Hv));
+    const int hk = h / (Hv / a.Hk);
+    const int slot = a.slots ? a.slots[b] : b;
+    if (slot < 0 || slot >= a.n_slots) { // whole workgroup leaves together
+        if (t < D) a.o[static_cast<size_t>(unit) * D + t] = __int_as_float(0x7fc00000);
+        return;
+    }
+    L.alpha = a.alpha[unit];
+    L.beta = a.beta[unit];
+    const size_t ub = static_cast<size_t>(slot) * Hv + h;
+    L.p8 = a.pool8 + ub * (N8 * D);
+    L.p4 = a.pool4 + ub * ((D - N8) * (D / 2));
+    L.rr = a.r + ub * D;
+
+    // ---- Table C2 step 1: issue the loads of this lane's packed rows
+    uint32_t w0[8], w1[8];
+    load_codes<N8>(L, w0, w1);
+    // ---- per-row and per-column factors, once per unit
+    if (t < D) {
+        const int p = t;
+        const int i = a.perm[h * D + p] & (D - 1);
+        const unsigned kb = static_cast<unsigned>((b * a.Hk + hk) * D);
+        const float kp = In<TIn>::get(a.k, kb + i);
+        const float qp = In<TIn>::get(a.q, kb + i);
+        const float rp = L.rr[p];
+        const float scale = p < N8 ? rp : rp * 0.0625f; // 4-bit codes are widened as 16 z
+        sh.rkq[p] = make_float2(scale * kp, scale * qp);
+        const float ar = L.alpha * scale;
+        const float bk = L.beta * kp;
+        // |b k| > 2^-64 |a r| (false when both vanish: then x = 0 * z = 0)
+        const bool scaled = fabsf(bk) > fabsf(ar) * kFormTiny;
+        sh.row[p] = make_float4(scaled ? ar / bk : ar, scaled ? bk : 1.0f, 0.0f,
+                                __int_as_float(scaled ? 0 : D));
+        float kq = kp * qp;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) kq += __shfl_xor(kq, off, 64);
+        if ((t & 63) == 0) sh.kq[t >> 6] = kq;
+    } else {
+        const int j = t - D;
+        sh.v[j] = In<TIn>::get(a.v, static_cast<unsigned>((b * Hv + h) * D + j));
+        sh.c[j] = a.c[h * D + j];
+        sh.ez[D + j] = 0.0f;
+    }
+    __syncthreads();
+    finish_unit<N8>(a, sh, L, w0, w1);
+}
+
+template <int N8>
+hipError_t launch_n8(bool bf16, const DecodeArgs &a, hipStream_t s) {
+    const unsigned units = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.Hv);
+    const int remap = (units % 8u) == 0u ? 1 : 0;
+    if (bf16)
+        hipLaunchKernelGGL((decode128_kernel<N8, uint16_t>), dim3(units), dim3(256), 0, s, a, remap);
+    else
+        hipLaunchKernelGGL((decode128_kernel<N8, float>), dim3(units), dim3(256), 0, s, a, remap);
+    return hipGetLastError();
+}
+
+} // namespace
+
+bool decode128_supported(int n8) { return n8 >= 0 && n8 <= D && n8 % 16 == 0; }
+
+hipError_t launch_decode128(int n8, bool bf16, const DecodeArgs &a, hipStream_t s) {
+    switch (n8) {
+    case 0: return launch_n8<0>(bf16, a, s);
+    case 16: return launch_n8<16>(bf16, a, s);
+    case 32: return launch_n8<32>(bf16, a, s);
+    case 48: return launch_n8<48>(bf16, a, s);
+    case 64: return launch_n8<64>(bf16, a, s);
+    case 80: return launch_n8<80>(bf16, a, s);
+    case 96: return launch_n8<96>(bf16, a, s);
+    case 112: return launch_n8<112>(bf16, a, s);
+    case 128: return launch_n8<128>(bf16, a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+} // namespace stq

@@ -56,6 +56,9 @@ constexpr int kCalChunks = 64;
 
 // Launchers (return hipSuccess or the launch error).  D in {16, 32, 64, 128}.
 hipError_t launch_decode_mixed(int D, bool bf16, const DecodeArgs &a, hipStream_t s);
+// 128 x 128 heads with n8 a multiple of 16 (compile-time row split).
+bool decode128_supported(int n8);
+hipError_t launch_decode128(int n8, bool bf16, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_fp32(int D, bool bf16, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_pack(int D, const PackArgs &a, hipStream_t s);
 hipError_t launch_dequant(int D, const PackArgs &a, hipStream_t s);
