@@ -29,7 +29,7 @@ sys.path.insert(0, str(ROOT))
 
 HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 COUNTERS_FILE = ROOT / "profiles" / "decode_counters.json"
-DECODE_SRC = ROOT / "linear_attention_recurrent_rule_amd" / "csrc" / "decode.hip"
+DECODE_SRC = ROOT / "linear_attention_recurrent_rule_amd" / "csrc" / "decode128.hip"
 
 
 def log(*a):
@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only-decode", action="store_true",
                    help="time the main workload only (for profiler runs)")
+    p.add_argument("--with-copy", action="store_true",
+                   help="also run the 1 GiB reference copy (with --only-decode)")
     return p.parse_args()
 
 
@@ -65,6 +67,23 @@ def algorithmic_bytes(fmt: str, B: int, hv: int, hk: int, d: int, n8: int, in_el
     state = 2 * unit_state_bytes(fmt, d, n8) * B * hv
     vecs = B * hk * 2 * d * in_el + B * hv * (d * in_el + 8 + 4 * d)
     return state + vecs
+
+
+def measure_copy(torch, stq, nbytes: int = 1 << 30, iters: int = 10) -> float:
+    """Practical HBM ceiling: read + write bytes/s of the library's plain
+    streaming copy over buffers far larger than the Infinity Cache."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        stq.stream_copy(src, dst)
+    torch.cuda.synchronize()
+    s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s_ev.record()
+    for _ in range(iters):
+        stq.stream_copy(src, dst)
+    e_ev.record()
+    torch.cuda.synchronize()
+    return 2 * nbytes * iters / (s_ev.elapsed_time(e_ev) / 1e3) / 1e9
 
 
 def main():
@@ -187,21 +206,9 @@ def main():
         for k_, v_ in variants.items():
             log(f"[bench] {k_}: {v_['updates_per_s'] / 1e6:.1f} M updates/s, "
                 f"{v_['hbm_gbps']:.0f} GB/s")
-        # practical ceiling: a plain streaming copy of 2 GiB
-        src = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            stq.stream_copy(src, dst)
-        torch.cuda.synchronize()
-        s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s_ev.record()
-        for _ in range(10):
-            stq.stream_copy(src, dst)
-        e_ev.record()
-        torch.cuda.synchronize()
-        copy_gbps = 2 * src.numel() * 10 / (s_ev.elapsed_time(e_ev) / 1e3) / 1e9
-        del src, dst
-        log(f"[bench] streaming copy ceiling: {copy_gbps:.0f} GB/s")
+    if args.with_copy or (not args.only_decode and not args.no_variants):
+        copy_gbps = measure_copy(torch, stq)
+        log(f"[bench] streaming copy ceiling (1 GiB -> 1 GiB): {copy_gbps:.0f} GB/s")
 
     # ------------------------------------------------------- CPU baseline --
     cpu = None

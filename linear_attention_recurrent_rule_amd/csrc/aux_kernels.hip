@@ -314,11 +314,12 @@ __global__ void iota_rows_kernel(int32_t *perm, int rows, int D) {
         perm[i] = static_cast<int32_t>(i % D);
 }
 
+// Streaming copy: one 16-byte word per lane, one 4 KiB tile per workgroup
+// (the fastest of the plain copy shapes measured on gfx950).
 __global__ __launch_bounds__(256) void copy_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
                                                    size_t n) {
-    for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-         i += static_cast<size_t>(gridDim.x) * blockDim.x)
-        dst[i] = src[i];
+    const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i < n) dst[i] = src[i];
 }
 
 unsigned grid_for(size_t n, unsigned cap = 4096) {
@@ -398,7 +399,9 @@ hipError_t launch_iota_rows(int32_t *perm, int rows, int D, hipStream_t s) {
 hipError_t launch_copy_bytes(const void *src, void *dst, size_t bytes, hipStream_t s) {
     const size_t n = bytes / 16;
     if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(copy_kernel, dim3(grid_for(n, 256u * 32u)), dim3(256), 0, s,
+    const size_t blocks = (n + 255) / 256;
+    if (blocks > 0x7fffffffu) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
                        static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), n);
     return hipGetLastError();
 }

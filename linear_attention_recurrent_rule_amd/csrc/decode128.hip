@@ -61,16 +61,59 @@ constexpr int kRowRor8 = 0x128;       // lane l <- lane l^8 within the row
 constexpr int kRowHalfMirror = 0x141; // lane l <- lane 7-l within each half row
 constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kRowMirror = 0x140;     // lane l <- lane 15-l within the row
 
+template <int CTRL> __device__ __forceinline__ float dppf(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the 64 lanes of a wave (valid in every lane): DPP within 16-lane
+// rows, then the four row sums through v_readlane.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dppf<kQuadXor1>(v);
+    v += dppf<kQuadXor2>(v);
+    v += dppf<kRowHalfMirror>(v);
+    v += dppf<kRowMirror>(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// MFMA operand A for the column sums: per wave w and lane group gl, seven
+// 8-entry bf16 rows: r k (hi, mid, lo), r q (hi, mid, lo) of the lane group's
+// 8 state rows, then a zero row for the unused outputs.
 struct Smem {
-    float2 rkq[D];          // {r k, r q} per physical row (1/16 folded for 4-bit)
+    uint16_t coef[4][4][7][8];
     float4 row[D];          // {P, s, -, offset of E in ez} per physical row
     float v[D], c[D];
-    float ez[2 * D];        // e (first half) and a zero vector (second half)
-    float red[2][16][D];    // column partials of u~ and w~ per row group
+    float ez[2 * D];        // e, then a zero vector; each as [e/4][c][e%4]
+    float4 red[4][8][2][16]; // per wave, column offset e, lane group, chunk c
     float kq[2];
     float mul[16][8];       // per row group: code multipliers of its 8 rows
 };
+
+// Round-to-nearest-even fp32 -> bf16 bit pattern (finite inputs).
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_val(uint32_t h) { return __uint_as_float(h << 16); }
+
+// x = hi + mid + lo exactly (each step removes the leading 8 significant bits
+// and the remainders are exact fp32 differences).
+__device__ __forceinline__ void split3(float x, uint32_t &h0, uint32_t &h1, uint32_t &h2) {
+    h0 = bf16_bits(x);
+    const float r1 = x - bf16_val(h0);
+    h1 = bf16_bits(r1);
+    const float r2 = r1 - bf16_val(h1);
+    h2 = bf16_bits(r2);
+}
 
 struct Lane {
     int t, c, g;
@@ -106,17 +149,16 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
     constexpr int M8 = N8 / 16;
     const int t = L.t, c = L.c, g = L.g;
 
-    // ---- widen the codes and accumulate this lane's share of u~ and w~
+    // ---- widen the codes; column sums u~ = S~^T (r k), w~ = S~^T (r q) on the
+    // matrix cores: per column offset e, one 16x16x32 bf16 MFMA multiplies the
+    // 6 x 32 coefficient splits of the wave's 32 rows with the 32 x 16 codes of
+    // column 8c + e (codes are small integers, exact in bf16; the splits are
+    // exact, so only the fp32 accumulation rounds)
+    const int w = t >> 6;
+    const int gl = (t >> 4) & 3;
     float z[8][8];
-    float pu[8], pw[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        pu[e] = 0.0f;
-        pw[e] = 0.0f;
-    }
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-        const float2 f = sh.rkq[g + 16 * m];
         if (m < M8) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -132,39 +174,70 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
                 z[m][2 * e + 1] = sbyte(hi, e);
             }
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            pu[e] = __builtin_fmaf(f.x, z[m][e], pu[e]);
-            pw[e] = __builtin_fmaf(f.y, z[m][e], pw[e]);
-        }
     }
-    *reinterpret_cast<float4 *>(&sh.red[0][g][8 * c]) = make_float4(pu[0], pu[1], pu[2], pu[3]);
-    *reinterpret_cast<float4 *>(&sh.red[0][g][8 * c + 4]) = make_float4(pu[4], pu[5], pu[6], pu[7]);
-    *reinterpret_cast<float4 *>(&sh.red[1][g][8 * c]) = make_float4(pw[0], pw[1], pw[2], pw[3]);
-    *reinterpret_cast<float4 *>(&sh.red[1][g][8 * c + 4]) = make_float4(pw[4], pw[5], pw[6], pw[7]);
+    {
+        const u32x4 araw = *reinterpret_cast<const u32x4 *>(&sh.coef[w][gl][c < 6 ? c : 6][0]);
+        const bf16x8 A = __builtin_bit_cast(bf16x8, araw);
+        // lanes of group 0 receive (u hi, u mid, u lo, w hi), group 1 (w mid, w lo);
+        // two accumulators alternate so a result is stored while the next
+        // product is in flight
+        auto product = [&](int e) {
+            u32x4 braw;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                braw[v] = __builtin_amdgcn_perm(__float_as_uint(z[2 * v + 1][e]),
+                                                __float_as_uint(z[2 * v][e]), 0x07060302u);
+            const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
+            return __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, braw), zero,
+                                                           0, 0, 0);
+        };
+        auto store = [&](int e, const f32x4 &acc) {
+            if (gl < 2) sh.red[w][e][gl][c] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        };
+        f32x4 acc0 = product(0);
+        f32x4 acc1 = product(1);
+#pragma unroll
+        for (int e = 2; e < 8; e += 2) {
+            store(e - 2, acc0);
+            acc0 = product(e);
+            store(e - 1, acc1);
+            acc1 = product(e + 1);
+        }
+        store(6, acc0);
+        store(7, acc1);
+    }
     __syncthreads();
 
-    // ---- column sums: u~ (lanes 0..127) -> e;  w~ (lanes 128..255) kept for o
+    // ---- column sums over the 4 waves: u~ (lanes 0..127) -> e; w~ (128..255)
+    // kept for o.  Lane t handles column 8 (t % 16) + (t / 16) % 8.
     float wsum = 0.0f;
-    {
-        const int half = t >> 7;
-        const int j = t & (D - 1);
-        float s = 0.0f;
+    const int cc = t & 15;
+    const int ce = (t >> 4) & 7;
+    const int jcol = 8 * cc + ce;
+    const int ezi = (ce >> 2) * 64 + cc * 4 + (ce & 3);
+    if (t < D) {
+        float u = 0.0f;
 #pragma unroll
-        for (int gg = 0; gg < 16; ++gg) s += sh.red[half][gg][j];
-        if (half == 0)
-            sh.ez[j] = __builtin_fmaf(-L.alpha, s, sh.v[j] / sh.c[j]);
-        else
-            wsum = s;
+        for (int ww = 0; ww < 4; ++ww) {
+            const float4 f = sh.red[ww][ce][0][cc];
+            u += (f.x + f.y) + f.z;
+        }
+        sh.ez[ezi] = __builtin_fmaf(-L.alpha, u, sh.v[jcol] / sh.c[jcol]);
+    } else {
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) {
+            const float4 f0 = sh.red[ww][ce][0][cc];
+            const float4 f1 = sh.red[ww][ce][1][cc];
+            wsum += (f0.w + f1.x) + f1.y;
+        }
     }
     __syncthreads();
 
     // ---- Table C2 step 3: readout of the updated state, before requantizing
     if (t >= D) {
-        const int j = t - D;
         const float kq = sh.kq[0] + sh.kq[1];
-        a.o[static_cast<size_t>(L.unit) * D + j] =
-            sh.c[j] * __builtin_fmaf(L.alpha, wsum, (L.beta * kq) * sh.ez[j]);
+        a.o[static_cast<size_t>(L.unit) * D + jcol] =
+            sh.c[jcol] * __builtin_fmaf(L.alpha, wsum, (L.beta * kq) * sh.ez[ezi]);
     }
 
     // ---- Table C2 steps 2 and 4: updated entries and row absmax
@@ -172,9 +245,9 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
         const float4 rp = sh.row[g + 16 * m];
-        const float *E = &sh.ez[__float_as_int(rp.w) + 8 * c];
+        const float *E = &sh.ez[__float_as_int(rp.w) + 4 * c];
         const float4 e0 = *reinterpret_cast<const float4 *>(E);
-        const float4 e1 = *reinterpret_cast<const float4 *>(E + 4);
+        const float4 e1 = *reinterpret_cast<const float4 *>(E + 64);
         const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
         float mx = 0.0f;
 #pragma unroll
@@ -308,22 +381,34 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
         const float qp = In<TIn>::get(a.q, kb + i);
         const float rp = L.rr[p];
         const float scale = p < N8 ? rp : rp * 0.0625f; // 4-bit codes are widened as 16 z
-        sh.rkq[p] = make_float2(scale * kp, scale * qp);
+        {
+            // row p = 4 w + gl + 16 m of wave w, lane group gl, slot m
+            uint16_t(&cf)[7][8] = sh.coef[(p & 15) >> 2][p & 3];
+            const int mm = p >> 4;
+            uint32_t h0, h1, h2;
+            split3(scale * kp, h0, h1, h2);
+            cf[0][mm] = static_cast<uint16_t>(h0);
+            cf[1][mm] = static_cast<uint16_t>(h1);
+            cf[2][mm] = static_cast<uint16_t>(h2);
+            split3(scale * qp, h0, h1, h2);
+            cf[3][mm] = static_cast<uint16_t>(h0);
+            cf[4][mm] = static_cast<uint16_t>(h1);
+            cf[5][mm] = static_cast<uint16_t>(h2);
+        }
         const float ar = L.alpha * scale;
         const float bk = L.beta * kp;
         // |b k| > 2^-64 |a r| (false when both vanish: then x = 0 * z = 0)
         const bool scaled = fabsf(bk) > fabsf(ar) * kFormTiny;
         sh.row[p] = make_float4(scaled ? ar / bk : ar, scaled ? bk : 1.0f, 0.0f,
                                 __int_as_float(scaled ? 0 : D));
-        float kq = kp * qp;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) kq += __shfl_xor(kq, off, 64);
+        const float kq = wave_sum(kp * qp);
         if ((t & 63) == 0) sh.kq[t >> 6] = kq;
     } else {
         const int j = t - D;
         sh.v[j] = In<TIn>::get(a.v, static_cast<unsigned>((b * Hv + h) * D + j));
         sh.c[j] = a.c[h * D + j];
         sh.ez[D + j] = 0.0f;
+        if (j < 16) *reinterpret_cast<uint4 *>(&sh.coef[j >> 2][j & 3][6][0]) = make_uint4(0u, 0u, 0u, 0u);
     }
     __syncthreads();
     finish_unit<N8>(a, sh, L, w0, w1);
