@@ -43,6 +43,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="highconc_6bit")
     p.add_argument("--pools", type=int, default=4, help="state pools rotated in the timed loop")
+    p.add_argument("--mode", choices=("in_place", "double_buffered"), default="in_place",
+                   help="in_place: each step rewrites the pool it reads; double_buffered: "
+                        "step t reads pool t and writes pool t+1 (stq_decode_step_into)")
     p.add_argument("--window", type=int, default=16, help="distinct input steps cycled")
     p.add_argument("--no-variants", action="store_true", help="skip the comparison formats")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -149,12 +152,19 @@ def main():
         torch.cuda.synchronize()
         return pools
 
-    def time_decode(pools, steps, warmup):
+    def launch(pools, t, into):
+        q, k, v, a, b = window[t % len(window)]
+        src = pools[t % len(pools)]
+        if into:
+            src.decode_step_into(pools[(t + 1) % len(pools)], q, k, v, a, b, o=o)
+        else:
+            src.decode_step(q, k, v, a, b, o=o)
+
+    def time_decode(pools, steps, warmup, into=False):
         """Per-launch HIP events on the launch stream + one pair around the loop."""
         stream = torch.cuda.current_stream()
         for t in range(warmup):
-            q, k, v, a, b = window[t % len(window)]
-            pools[t % len(pools)].decode_step(q, k, v, a, b, o=o)
+            launch(pools, t, into)
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
@@ -163,9 +173,8 @@ def main():
         torch.cuda.synchronize()
         start.record(stream)
         for t in range(steps):
-            q, k, v, a, b = window[t % len(window)]
             ev[t][0].record(stream)
-            pools[t % len(pools)].decode_step(q, k, v, a, b, o=o)
+            launch(pools, t, into)
             ev[t][1].record(stream)
         end.record(stream)
         torch.cuda.synchronize()
@@ -173,30 +182,37 @@ def main():
         per = [s.elapsed_time(e) for s, e in ev]
         return total_ms, float(np.mean(per)), float(np.median(per))
 
-    def measure(fmt_name: str, fmt: int, n8: int, npools: int, steps: int, warmup: int):
+    def measure(fmt_name: str, fmt: int, n8: int, npools: int, steps: int, warmup: int,
+                into: bool = False):
         pools = make_pools(fmt, n8, npools)
-        total_ms, mean_ms, med_ms = time_decode(pools, steps, warmup)
+        total_ms, mean_ms, med_ms = time_decode(pools, steps, warmup, into)
         nbytes = algorithmic_bytes(fmt_name, B, hv, hk, d, n8, in_el)
         res = dict(updates_per_s=B * hv * steps / (total_ms / 1e3), ms_per_step=total_ms / steps,
                    kernel_ms_mean=mean_ms, kernel_ms_median=med_ms,
                    algorithmic_bytes_per_launch=nbytes,
                    hbm_gbps=nbytes / (mean_ms / 1e3) / 1e9,
                    frac_of_peak=nbytes / (mean_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
-                   pools=npools, pool_bytes=int(pools[0].buffer.numel()))
+                   pools=npools, pool_bytes=int(pools[0].buffer.numel()),
+                   mode="double_buffered" if into else "in_place")
         del pools
         torch.cuda.empty_cache()
         return res
 
     # ------------------------------------------------------------ main run --
-    main_res = measure("mixed", stq.FMT_MIXED48, w.n8, args.pools, args.steps, args.warmup)
+    into = args.mode == "double_buffered"
+    main_res = measure("mixed", stq.FMT_MIXED48, w.n8, args.pools, args.steps, args.warmup, into)
     log(f"[bench] main: {main_res['updates_per_s'] / 1e6:.1f} M updates/s, "
         f"{main_res['hbm_gbps']:.0f} GB/s ({100 * main_res['frac_of_peak']:.1f}% of peak)")
 
     variants = {}
     copy_gbps = None
     if not args.only_decode and not args.no_variants:
-        variants["single_pool_as_stated"] = measure("mixed", stq.FMT_MIXED48, w.n8, 1,
-                                                    args.steps, args.warmup)
+        other = "in_place" if into else "double_buffered"
+        variants[other] = measure("mixed", stq.FMT_MIXED48, w.n8, args.pools, args.steps,
+                                  args.warmup, not into)
+        if not into:
+            variants["single_pool_as_stated"] = measure("mixed", stq.FMT_MIXED48, w.n8, 1,
+                                                        args.steps, args.warmup)
         if w.n8 != 16:
             variants["mix_4p5bit_n8_16"] = measure("mixed", stq.FMT_MIXED48, 16, args.pools,
                                                    args.steps, args.warmup)
@@ -255,8 +271,9 @@ def main():
             "workload": f"{w.name}: B={B}, Hv={hv} value heads over Hk={hk} key heads, "
                         f"d_k=d_v={d}, n8={w.n8} 8-bit rows + {d - w.n8} 4-bit rows per head "
                         f"({8 * unit_state_bytes('mixed', d, w.n8) / (d * d):.2f} bits/value), "
-                        f"{w.dtype} q/k/v, {args.pools} rotated pools (MALL-cold)",
-            "global_batch": B, "heads_v": hv, "heads_k": hk, "d": d, "n8": w.n8,
+                        f"{w.dtype} q/k/v, {args.pools} rotated pools (MALL-cold), "
+                        f"{main_res['mode'].replace('_', '-')} state update",
+            "mode": main_res["mode"], "global_batch": B, "heads_v": hv, "heads_k": hk, "d": d, "n8": w.n8,
             "parallelism": "single GPU",
         },
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

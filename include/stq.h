@@ -177,6 +177,23 @@ stq_status stq_decode_step(const stq_state *st, const int32_t *slots, int32_t B,
                            const float *alpha, const float *beta, float *o,
                            stq_stream_t stream);
 
+/* The same decode step, reading slots[b] of `src` and writing the updated
+ * packed codes and row factors (FP32 format: the updated state) into the same
+ * slots of `dst`; `src` is left unchanged.  This is the double-buffered page
+ * of App. C.3 Table C2 step 6 (the old representation stays valid until its
+ * readers finish) and lets the write stream to other pages than the read.
+ * dst must have the same descriptor as src.  The step reads c and perm from
+ * src only, so the codes written to dst are relative to src's calibration:
+ * give dst the same c and perm before reading it back or decoding from it.
+ * dst == src is the in-place step; pools that overlap partially are rejected.
+ * Errors: as stq_decode_step; STQ_E_SHAPE if the descriptors differ,
+ * STQ_E_ARG for partially overlapping pools. */
+stq_status stq_decode_step_into(const stq_state *src, const stq_state *dst,
+                                const int32_t *slots, int32_t B, const void *q,
+                                const void *k, const void *v, int32_t dtype,
+                                const float *alpha, const float *beta, float *o,
+                                stq_stream_t stream);
+
 /* Reconstruct S_ij = r_i c_j z_ij (Sec. 4.3) of slots[b] into fp32
  * S_out [B][Hv][dk][dv] in logical row order (FP32 format: copies the state).
  * Errors: STQ_E_ARG, STQ_E_SHAPE, STQ_E_DEVICE. */

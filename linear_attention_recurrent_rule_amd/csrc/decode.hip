@@ -94,9 +94,12 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
     const int n8 = a.n8;
 
     const size_t ubase = static_cast<size_t>(live ? slot : 0) * a.Hv + h;
-    int8_t *p8 = a.pool8 + ubase * static_cast<size_t>(n8) * D;
-    uint8_t *p4 = a.pool4 + ubase * static_cast<size_t>(D - n8) * (D / 2);
-    float *rr = a.r + ubase * D;
+    const int8_t *p8 = a.pool8 + ubase * static_cast<size_t>(n8) * D;
+    const uint8_t *p4 = a.pool4 + ubase * static_cast<size_t>(D - n8) * (D / 2);
+    const float *rr = a.r + ubase * D;
+    int8_t *q8 = a.pool8_out + ubase * static_cast<size_t>(n8) * D;
+    uint8_t *q4 = a.pool4_out + ubase * static_cast<size_t>(D - n8) * (D / 2);
+    float *rw = a.r_out + ubase * D;
 
     // Table C2 step 1: fetch the packed rows and row factors of this lane.
     uint32_t w0[8], w1[8];
@@ -229,7 +232,7 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
         const float qinv = (p < n8) ? (1.0f / 127.0f) : (1.0f / 7.0f);
         const float rn = fmaxf(mx * qinv, kRowFloor);
         inv[m] = __builtin_amdgcn_rcpf(rn);
-        if (live && (m % C8) == (c % 8) && c < 8) rr[p] = rn;
+        if (live && (m % C8) == (c % 8) && c < 8) rw[p] = rn;
     }
     // Table C2 step 6: codes against the stored factor, pack, write in place.
 #pragma unroll
@@ -244,12 +247,12 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
             uint2 t;
             t.x = (bits[0] & 0xFFu) | ((bits[1] & 0xFFu) << 8) | ((bits[2] & 0xFFu) << 16) | (bits[3] << 24);
             t.y = (bits[4] & 0xFFu) | ((bits[5] & 0xFFu) << 8) | ((bits[6] & 0xFFu) << 16) | (bits[7] << 24);
-            *reinterpret_cast<uint2 *>(p8 + static_cast<size_t>(p) * D + 8 * c) = t;
+            *reinterpret_cast<uint2 *>(q8 + static_cast<size_t>(p) * D + 8 * c) = t;
         } else {
             uint32_t t = 0u;
 #pragma unroll
             for (int e = 0; e < 8; ++e) t |= (bits[e] & 0xFu) << (4 * e);
-            *reinterpret_cast<uint32_t *>(p4 + static_cast<size_t>(p - n8) * (D / 2) + 4 * c) = t;
+            *reinterpret_cast<uint32_t *>(q4 + static_cast<size_t>(p - n8) * (D / 2) + 4 * c) = t;
         }
     }
 }
@@ -278,7 +281,8 @@ __global__ __launch_bounds__(256) void decode_fp32_kernel(DecodeArgs a) {
     const int hk = h / (a.Hv / a.Hk);
     const int slot = active ? (a.slots ? a.slots[b] : b) : 0;
     const bool live = active && slot >= 0 && slot < a.n_slots;
-    float *S = a.s32 + (static_cast<size_t>(live ? slot : 0) * a.Hv + h) * D * D;
+    const float *S = a.s32 + (static_cast<size_t>(live ? slot : 0) * a.Hv + h) * D * D;
+    float *Sw = a.s32_out + (static_cast<size_t>(live ? slot : 0) * a.Hv + h) * D * D;
 
     float s[8][8];
 #pragma unroll
@@ -366,8 +370,8 @@ __global__ __launch_bounds__(256) void decode_fp32_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(alpha, s[m][e], bk * ev[e]);
         if (live) {
-            *reinterpret_cast<float4 *>(S + static_cast<size_t>(i) * D + 8 * c) = make_float4(x[0], x[1], x[2], x[3]);
-            *reinterpret_cast<float4 *>(S + static_cast<size_t>(i) * D + 8 * c + 4) = make_float4(x[4], x[5], x[6], x[7]);
+            *reinterpret_cast<float4 *>(Sw + static_cast<size_t>(i) * D + 8 * c) = make_float4(x[0], x[1], x[2], x[3]);
+            *reinterpret_cast<float4 *>(Sw + static_cast<size_t>(i) * D + 8 * c + 4) = make_float4(x[4], x[5], x[6], x[7]);
         }
     }
 }

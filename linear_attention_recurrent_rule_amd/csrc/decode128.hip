@@ -119,9 +119,12 @@ struct Lane {
     int t, c, g;
     unsigned unit;
     float alpha, beta;
-    int8_t *p8;
-    uint8_t *p4;
-    float *rr;
+    const int8_t *p8;  // packed rows read ...
+    const uint8_t *p4;
+    int8_t *q8;        // ... and written (the same unless decoding out of place)
+    uint8_t *q4;
+    const float *rr;   // row factors read ...
+    float *rw;         // ... and written
 };
 
 // Fetch this lane's packed rows (Table C2 step 1).
@@ -294,7 +297,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
         float mul = sc * inv;
         mul = fminf(fmaxf(mul, -kMulMax), kMulMax);
         if ((c & 1) == 0) {
-            L.rr[p] = rn;
+            L.rw[p] = rn;
             sh.mul[g][mm] = mul;
         }
     }
@@ -319,7 +322,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
             const uint32_t a23 = __builtin_amdgcn_perm(bt[3], bt[2], 0x04000C0Cu);
             const uint32_t a45 = __builtin_amdgcn_perm(bt[5], bt[4], 0x0C0C0400u);
             const uint32_t a67 = __builtin_amdgcn_perm(bt[7], bt[6], 0x04000C0Cu);
-            *reinterpret_cast<uint2 *>(L.p8 + (p * D + 8 * c)) = make_uint2(a01 | a23, a45 | a67);
+            *reinterpret_cast<uint2 *>(L.q8 + (p * D + 8 * c)) = make_uint2(a01 | a23, a45 | a67);
         } else {
             // even columns -> low nibbles, odd columns -> high nibbles
             const uint32_t ev02 = __builtin_amdgcn_perm(bt[2], bt[0], 0x0C0C0400u);
@@ -329,7 +332,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
             const uint32_t evn = ev02 | ev46;
             const uint32_t odd = (od13 | od57) << 4;
             const uint32_t word = (evn & 0x0F0F0F0Fu) | (odd & 0xF0F0F0F0u);
-            *reinterpret_cast<uint32_t *>(L.p4 + ((p - N8) * (D / 2) + 4 * c)) = word;
+            *reinterpret_cast<uint32_t *>(L.q4 + ((p - N8) * (D / 2) + 4 * c)) = word;
         }
     }
 }
@@ -368,6 +371,9 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
     L.p8 = a.pool8 + ub * (N8 * D);
     L.p4 = a.pool4 + ub * ((D - N8) * (D / 2));
     L.rr = a.r + ub * D;
+    L.q8 = a.pool8_out + ub * (N8 * D);
+    L.q4 = a.pool4_out + ub * ((D - N8) * (D / 2));
+    L.rw = a.r_out + ub * D;
 
     // ---- Table C2 step 1: issue the loads of this lane's packed rows
     uint32_t w0[8], w1[8];

@@ -262,25 +262,50 @@ stq_status stq_dequant_state(const stq_state *st, const int32_t *slots, int32_t 
     return dev(stq::launch_dequant(st->desc.d_k, a, s));
 }
 
-stq_status stq_decode_step(const stq_state *st, const int32_t *slots, int32_t B, const void *q,
-                           const void *k, const void *v, int32_t dtype, const float *alpha,
-                           const float *beta, float *o, stq_stream_t stream) {
-    stq_status e = batch_args(st, slots, B);
+namespace {
+
+bool same_desc(const stq_desc &x, const stq_desc &y) {
+    return x.n_slots == y.n_slots && x.n_heads_v == y.n_heads_v && x.n_heads_k == y.n_heads_k &&
+           x.d_k == y.d_k && x.d_v == y.d_v && x.n8 == y.n8 && x.fmt == y.fmt;
+}
+
+// [p, p + n) and [q, q + n) overlap without being the same range
+bool partial_overlap(const void *p, const void *q, size_t n) {
+    if (!p || !q || n == 0 || p == q) return false;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a < b + n && b < a + n;
+}
+
+stq_status decode(const stq_state *src, const stq_state *dst, const int32_t *slots, int32_t B,
+                  const void *q, const void *k, const void *v, int32_t dtype, const float *alpha,
+                  const float *beta, float *o, stq_stream_t stream) {
+    stq_status e = batch_args(src, slots, B);
     if (e != STQ_OK) return e;
+    if ((e = check_state(dst)) != STQ_OK) return e;
+    if (!same_desc(src->desc, dst->desc)) return STQ_E_SHAPE;
     if (dtype != STQ_F32 && dtype != STQ_BF16) return STQ_E_ARG;
     const size_t el = dtype == STQ_F32 ? 4 : 2;
     if (!q || !k || !v || !alpha || !beta || !o) return STQ_E_ARG;
     if (!aligned(q, el) || !aligned(k, el) || !aligned(v, el) || !aligned(alpha, 4) ||
         !aligned(beta, 4) || !aligned(o, 4))
         return STQ_E_ARG;
-    if (st->desc.fmt == STQ_FMT_MIXED48 && !st->calibrated) return STQ_E_STATE;
+    if (src->desc.fmt == STQ_FMT_MIXED48 && !src->calibrated) return STQ_E_STATE;
+    Layout L;
+    describe(&src->desc, &L);
+    if (partial_overlap(src->pool8, dst->pool8, L.pool8) || partial_overlap(src->pool4, dst->pool4, L.pool4) ||
+        partial_overlap(src->r, dst->r, L.r) || partial_overlap(src->s32, dst->s32, L.s32))
+        return STQ_E_ARG;
     stq::DecodeArgs a;
-    a.pool8 = st->pool8;
-    a.pool4 = st->pool4;
-    a.r = st->r;
-    a.s32 = st->s32;
-    a.c = st->c;
-    a.perm = st->perm;
+    a.pool8 = src->pool8;
+    a.pool4 = src->pool4;
+    a.r = src->r;
+    a.pool8_out = dst->pool8;
+    a.pool4_out = dst->pool4;
+    a.r_out = dst->r;
+    a.s32 = src->s32;
+    a.s32_out = dst->s32;
+    a.c = src->c;
+    a.perm = src->perm;
     a.slots = slots;
     a.q = q;
     a.k = k;
@@ -289,14 +314,30 @@ stq_status stq_decode_step(const stq_state *st, const int32_t *slots, int32_t B,
     a.beta = beta;
     a.o = o;
     a.B = B;
-    a.Hv = st->desc.n_heads_v;
-    a.Hk = st->desc.n_heads_k;
-    a.n8 = st->desc.n8;
-    a.n_slots = st->desc.n_slots;
+    a.Hv = src->desc.n_heads_v;
+    a.Hk = src->desc.n_heads_k;
+    a.n8 = src->desc.n8;
+    a.n_slots = src->desc.n_slots;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool bf16 = dtype == STQ_BF16;
-    if (st->desc.fmt == STQ_FMT_FP32) return dev(stq::launch_decode_fp32(st->desc.d_k, bf16, a, s));
-    return dev(stq::launch_decode_mixed(st->desc.d_k, bf16, a, s));
+    if (src->desc.fmt == STQ_FMT_FP32) return dev(stq::launch_decode_fp32(src->desc.d_k, bf16, a, s));
+    return dev(stq::launch_decode_mixed(src->desc.d_k, bf16, a, s));
+}
+
+} // namespace
+
+stq_status stq_decode_step(const stq_state *st, const int32_t *slots, int32_t B, const void *q,
+                           const void *k, const void *v, int32_t dtype, const float *alpha,
+                           const float *beta, float *o, stq_stream_t stream) {
+    return decode(st, st, slots, B, q, k, v, dtype, alpha, beta, o, stream);
+}
+
+stq_status stq_decode_step_into(const stq_state *src, const stq_state *dst, const int32_t *slots,
+                                int32_t B, const void *q, const void *k, const void *v,
+                                int32_t dtype, const float *alpha, const float *beta, float *o,
+                                stq_stream_t stream) {
+    if (!src || !dst) return STQ_E_ARG;
+    return decode(src, dst, slots, B, q, k, v, dtype, alpha, beta, o, stream);
 }
 
 stq_status stq_stream_copy(const void *src, void *dst, size_t bytes, stq_stream_t stream) {

@@ -10,10 +10,14 @@ namespace stq {
 
 // One decode launch: B sequences x Hv value heads, in place on slots[b].
 struct DecodeArgs {
-    int8_t *pool8;        // [n_slots][Hv][n8][D]
-    uint8_t *pool4;       // [n_slots][Hv][D-n8][D/2]
-    float *r;             // [n_slots][Hv][D]
-    float *s32;           // [n_slots][Hv][D][D]   (FP32 format)
+    const int8_t *pool8;  // [n_slots][Hv][n8][D]       read
+    const uint8_t *pool4; // [n_slots][Hv][D-n8][D/2]   read
+    const float *r;       // [n_slots][Hv][D]           read
+    int8_t *pool8_out;    // written (equal to the read pointers when in place)
+    uint8_t *pool4_out;
+    float *r_out;
+    const float *s32;     // [n_slots][Hv][D][D]   (FP32 format) read
+    float *s32_out;       //                                      written
     const float *c;       // [Hv][D]
     const int32_t *perm;  // [Hv][D]
     const int32_t *slots; // [B] or nullptr (identity)

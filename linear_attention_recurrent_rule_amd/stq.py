@@ -49,8 +49,8 @@ class CState(ctypes.Structure):
 
 _LIB = None
 EXPORTS = ("stq_state_bytes", "stq_alloc_state", "stq_calibrate", "stq_set_calibration",
-           "stq_pack_state", "stq_decode_step", "stq_dequant_state", "stq_stream_copy",
-           "stq_status_str", "stq_abi_version")
+           "stq_pack_state", "stq_decode_step", "stq_decode_step_into", "stq_dequant_state",
+           "stq_stream_copy", "stq_status_str", "stq_abi_version")
 
 
 def _lib():
@@ -70,14 +70,16 @@ def _lib():
         lib.stq_set_calibration.argtypes = [ctypes.POINTER(CState), P, P, P]
         lib.stq_pack_state.argtypes = [ctypes.POINTER(CState), P, P, I32, P]
         lib.stq_decode_step.argtypes = [ctypes.POINTER(CState), P, I32, P, P, P, I32, P, P, P, P]
+        lib.stq_decode_step_into.argtypes = [ctypes.POINTER(CState), ctypes.POINTER(CState), P,
+                                             I32, P, P, P, I32, P, P, P, P]
         lib.stq_dequant_state.argtypes = [ctypes.POINTER(CState), P, I32, P, P]
         lib.stq_stream_copy.argtypes = [P, P, SZ, P]
         lib.stq_status_str.argtypes = [I32]
         lib.stq_status_str.restype = ctypes.c_char_p
         lib.stq_abi_version.restype = I32
         for name in ("stq_alloc_state", "stq_calibrate", "stq_set_calibration",
-                     "stq_pack_state", "stq_decode_step", "stq_dequant_state",
-                     "stq_stream_copy"):
+                     "stq_pack_state", "stq_decode_step", "stq_decode_step_into",
+                     "stq_dequant_state", "stq_stream_copy"):
             getattr(lib, name).restype = I32
         _LIB = lib
     return _LIB
@@ -228,6 +230,29 @@ class State:
                                       _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), dt,
                                       _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
                                       _dev_ptr(o, "o"), _stream(stream)), "stq_decode_step")
+        return o
+
+    def decode_step_into(self, dst: "State", q, k, v, alpha, beta, o=None, slots=None,
+                         stream=None):
+        """Decode reading this state and writing the updated one into `dst`."""
+        if q.dtype == torch.float32:
+            dt = F32
+        elif q.dtype == torch.bfloat16:
+            dt = BF16
+        else:
+            raise ValueError("q, k, v must be float32 or bfloat16")
+        if k.dtype != q.dtype or v.dtype != q.dtype:
+            raise ValueError("q, k, v must share one dtype")
+        B = int(q.shape[0])
+        if o is None:
+            o = torch.empty((B, self.geo.n_heads_v, self.geo.d), dtype=torch.float32,
+                            device=q.device)
+        _check(_lib().stq_decode_step_into(ctypes.byref(self.c_state), ctypes.byref(dst.c_state),
+                                           _dev_ptr(slots, "slots"), B, _dev_ptr(q, "q"),
+                                           _dev_ptr(k, "k"), _dev_ptr(v, "v"), dt,
+                                           _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
+                                           _dev_ptr(o, "o"), _stream(stream)),
+               "stq_decode_step_into")
         return o
 
     def dequant(self, B: int | None = None, slots=None, out=None, stream=None):

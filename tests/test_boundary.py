@@ -162,3 +162,33 @@ def test_status_strings():
     for s in range(7):
         assert lib.stq_status_str(s).decode().startswith("STQ_")
     assert lib.stq_status_str(99) == b"unknown stq_status"
+
+
+def test_decode_into_rejections():
+    lib = stq.lib()
+    src = _fake_state(calibrated=1)
+    p = [FAKE] * 6
+
+    def into(a, b, B=2):
+        return lib.stq_decode_step_into(a, b, None, B, p[0], p[1], p[2], 0, p[3], p[4], p[5],
+                                        None)
+
+    assert into(None, ctypes.byref(src)) == E_ARG
+    assert into(ctypes.byref(src), None) == E_ARG
+    other = _fake_state(calibrated=1, n8=16)  # different descriptor
+    assert into(ctypes.byref(src), ctypes.byref(other)) == E_SHAPE
+    other = _fake_state(calibrated=1, n_slots=8)
+    assert into(ctypes.byref(src), ctypes.byref(other)) == E_SHAPE
+    # a destination pool that overlaps the source pool without being it
+    shifted = _fake_state(calibrated=1)
+    shifted.pool8 = src.pool8 + 64
+    assert into(ctypes.byref(src), ctypes.byref(shifted)) == E_ARG
+    shifted = _fake_state(calibrated=1)
+    shifted.r = src.r + 4
+    assert into(ctypes.byref(src), ctypes.byref(shifted)) == E_ARG
+    bad = _fake_state(calibrated=1)
+    bad.pool4 = None
+    assert into(ctypes.byref(src), ctypes.byref(bad)) == E_ARG
+    uncal = _fake_state(calibrated=0)
+    assert into(ctypes.byref(uncal), ctypes.byref(src)) == E_STATE
+    assert into(ctypes.byref(src), ctypes.byref(src), B=0) == E_SHAPE

@@ -103,10 +103,11 @@ def test_zero_state_first_step(oracle_mod):
     print(gu.compare_step(dict(pool8=p8, pool4=p4, r=r, o=o), ref, n8=n8, d=d))
 
 
-def test_slot_mapping_and_untouched_slots(oracle_mod):
+@pytest.mark.parametrize("d,n8,hv,hk", [(64, 32, 4, 2), (128, 64, 8, 4), (128, 16, 32, 16)])
+def test_slot_mapping_and_untouched_slots(oracle_mod, d, n8, hv, hk):
     """A batch addressing a permuted subset of slots updates exactly those
     slots; the others keep their bytes."""
-    n_slots, B, hv, hk, d, n8 = 10, 4, 4, 2, 64, 32
+    n_slots, B = 10, 4
     ps_all = wl.random_packed_state(n_slots, hv, d, n8, seed=31)
     st = gu.make_state(B, hv, hk, d, n8, n_slots=n_slots)
     gu.load_packed(st, ps_all)
@@ -124,9 +125,10 @@ def test_slot_mapping_and_untouched_slots(oracle_mod):
     np.testing.assert_array_equal(r[rest], ps_all.r[rest])
 
 
-def test_out_of_range_slot_is_skipped():
+@pytest.mark.parametrize("d,n8,hv,hk", [(32, 16, 2, 2), (128, 64, 4, 2)])
+def test_out_of_range_slot_is_skipped(oracle_mod, d, n8, hv, hk):
     """A slot outside [0, n_slots) leaves the pool untouched and fills o with NaN."""
-    n_slots, B, hv, hk, d, n8 = 4, 2, 2, 2, 32, 16
+    n_slots, B = 4, 2
     ps = wl.random_packed_state(n_slots, hv, d, n8, seed=41)
     st = gu.make_state(B, hv, hk, d, n8, n_slots=n_slots)
     gu.load_packed(st, ps)
@@ -136,7 +138,13 @@ def test_out_of_range_slot_is_skipped():
     assert np.all(np.isnan(o[1])) and np.all(np.isfinite(o[0]))
     for s in (0, 2, 3):
         np.testing.assert_array_equal(p8[s], ps.pool8[s])
+        np.testing.assert_array_equal(p4[s], ps.pool4[s])
         np.testing.assert_array_equal(r[s], ps.r[s])
+    # and the live sequence still matches the oracle
+    sub = wl.PackedState(ps.pool8[[1]], ps.pool4[[1]], ps.r[[1]], ps.c, ps.perm, n8)
+    x1 = wl.StepInputs(x.q[[0]], x.k[[0]], x.v[[0]], x.alpha[[0]], x.beta[[0]], x.dtype)
+    ref = gu.oracle_step_on(oracle_mod, sub, x1)
+    gu.compare_step(dict(pool8=p8[[1]], pool4=p4[[1]], r=r[[1]], o=o[[0]]), ref, n8=n8, d=d)
 
 
 @pytest.mark.parametrize("name,steps", [("tiny", 64), ("small_mixed", 48)])
@@ -268,3 +276,66 @@ def test_calibration_deterministic():
         outs.append((st.c.cpu().numpy(), st.perm.cpu().numpy(), st.rowscore.cpu().numpy()))
     for a, b in zip(outs[0], outs[1]):
         np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("d,n8,hv,hk", [(32, 16, 2, 2), (64, 32, 4, 2), (128, 64, 8, 4),
+                                        (128, 16, 32, 16)])
+def test_decode_into_matches_in_place(oracle_mod, d, n8, hv, hk):
+    """Reading one pool and writing another gives the in-place step's bytes in
+    the addressed slots of the destination, leaves the source untouched and
+    the destination's other slots as they were."""
+    n_slots, B = 6, 4
+    print(f"[case] decode_into d={d} n8={n8} hv={hv} hk={hk}", flush=True)
+    ps = wl.random_packed_state(n_slots, hv, d, n8, seed=51)
+    junk = wl.random_packed_state(n_slots, hv, d, n8, seed=52)
+    src = gu.make_state(B, hv, hk, d, n8, n_slots=n_slots)
+    dst = gu.make_state(B, hv, hk, d, n8, n_slots=n_slots)
+    ref_st = gu.make_state(B, hv, hk, d, n8, n_slots=n_slots)
+    gu.load_packed(src, ps)
+    gu.load_packed(ref_st, ps)
+    gu.load_packed(dst, wl.PackedState(junk.pool8, junk.pool4, junk.r, ps.c, ps.perm, n8))
+    slots = np.array([5, 0, 3, 2], np.int32)
+    x = wl.draw_inputs(B, hk, hv, d, dtype="bf16", seed=51, step=0)
+    q, k, v, a, b = gu.inputs_to_device(x)
+    st_t = gu.dev(slots)
+    o_into = src.decode_step_into(dst, q, k, v, a, b, slots=st_t)
+    o_in = ref_st.decode_step(q, k, v, a, b, slots=st_t)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(o_into.cpu().numpy(), o_in.cpu().numpy())
+    s8, s4, sr = gu.read_packed(src)
+    np.testing.assert_array_equal(s8, ps.pool8)
+    np.testing.assert_array_equal(s4, ps.pool4)
+    np.testing.assert_array_equal(sr, ps.r)
+    d8, d4, dr = gu.read_packed(dst)
+    i8, i4, ir = gu.read_packed(ref_st)
+    np.testing.assert_array_equal(d8[slots], i8[slots])
+    np.testing.assert_array_equal(d4[slots], i4[slots])
+    np.testing.assert_array_equal(dr[slots], ir[slots])
+    rest = np.setdiff1d(np.arange(n_slots), slots)
+    np.testing.assert_array_equal(d8[rest], junk.pool8[rest])
+    np.testing.assert_array_equal(d4[rest], junk.pool4[rest])
+    np.testing.assert_array_equal(dr[rest], junk.r[rest])
+    sub = wl.PackedState(ps.pool8[slots], ps.pool4[slots], ps.r[slots], ps.c, ps.perm, n8)
+    ref = gu.oracle_step_on(oracle_mod, sub, x)
+    gu.compare_step(dict(pool8=d8[slots], pool4=d4[slots], r=dr[slots], o=o_into.cpu().numpy()),
+                    ref, n8=n8, d=d)
+
+
+def test_decode_into_fp32_state():
+    """The FP32-state baseline reads one pool and writes the other as well."""
+    B, hv, hk, d = 3, 4, 2, 64
+    print(f"[case] decode_into fp32 B={B} d={d}", flush=True)
+    src = gu.make_state(B, hv, hk, d, 0, fmt=stq.FMT_FP32)
+    dst = gu.make_state(B, hv, hk, d, 0, fmt=stq.FMT_FP32)
+    ref_st = gu.make_state(B, hv, hk, d, 0, fmt=stq.FMT_FP32)
+    S0 = torch.randn(B, hv, d, d, generator=torch.Generator().manual_seed(3)).cuda() * 0.1
+    src.s32.copy_(S0)
+    ref_st.s32.copy_(S0)
+    x = wl.draw_inputs(B, hk, hv, d, dtype="f32", seed=61, step=0)
+    q, k, v, a, b = gu.inputs_to_device(x)
+    o1 = src.decode_step_into(dst, q, k, v, a, b)
+    o2 = ref_st.decode_step(q, k, v, a, b)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(src.s32, S0)
+    assert torch.equal(dst.s32, ref_st.s32)
