@@ -36,6 +36,9 @@ def compile_flags() -> list[str]:
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-ffp-contract=off",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # matrix-core results straight into the vector register file (no
+        # accumulation-register copies: fewer instructions and registers)
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-Wall", "-Wno-unused-function",
         f"-I{INCLUDE}", f"-I{CSRC}",
     ]
