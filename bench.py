@@ -63,6 +63,12 @@ def parse():
                    help="time the main workload only (for profiler runs)")
     p.add_argument("--with-copy", action="store_true",
                    help="also run the 1 GiB reference copy (with --only-decode)")
+    p.add_argument("--drift", action="store_true",
+                   help="instead of timing: run the workload's T steps on the packed state and "
+                        "on an FP32 state from the same S0 and print the drift as one JSON line")
+    p.add_argument("--layers", type=int, default=None, help="layers for --drift (default: all)")
+    p.add_argument("--drift-steps", type=int, default=None, help="T for --drift (default: the "
+                   "workload's)")
     return p.parse_args()
 
 
@@ -102,8 +108,9 @@ def measure_copy(torch, stq, nbytes: int = 1 << 30, iters: int = 10) -> float:
 def main():
     args = parse()
     if args.gpus != 1:
-        log("bench.py measures one GPU: this build has no multi-GPU path (every decode unit is "
-            "independent; see the sharding notes in DESIGN.md). Run with --gpus 1.")
+        log("bench.py measures one GPU only: the decode step has no exchange between units, "
+            "so a multi-GPU run would shard sequence slots and run this same kernel on each "
+            "GPU's share; that path is not built. Run with --gpus 1.")
         sys.exit(2)
 
     import numpy as np
@@ -125,6 +132,10 @@ def main():
             cv = lambda bits: dev(bits.view(np.int16)).view(torch.bfloat16)  # noqa: E731
             return cv(x.q_bits), cv(x.k_bits), cv(x.v_bits), dev(x.alpha), dev(x.beta)
         return dev(x.q), dev(x.k), dev(x.v), dev(x.alpha), dev(x.beta)
+
+    if args.drift:
+        print(json.dumps(run_drift(args, np, torch, stq, wl, w)), flush=True)
+        return
 
     # ---------------------------------------------------------------- setup --
     t0 = time.time()
@@ -300,6 +311,141 @@ def main():
         "variants": variants,
     }
     print(json.dumps(line), flush=True)
+
+
+def device_inputs(torch, w, layer: int, t: int, calibration: bool = False):
+    """One step of inputs drawn on the device (same laws as the host generator:
+    q, k ~ N(0, 1) L2-normalised, v ~ N(0, 1), alpha ~ U(lo, 1),
+    beta = sigmoid(N(0, 1)); bf16 by round-to-nearest-even), for workloads too
+    large to draw on the host every step."""
+    seed = (w.calib_seed if calibration else w.seed) * 1_000_003 + layer * 10_007 + t
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    B, hk, hv, d = w.B, w.hk, w.hv, w.d
+    q = torch.randn(B, hk, d, device="cuda", generator=g)
+    k = torch.randn(B, hk, d, device="cuda", generator=g)
+    q = q / q.norm(dim=-1, keepdim=True)
+    k = k / k.norm(dim=-1, keepdim=True)
+    v = torch.randn(B, hv, d, device="cuda", generator=g)
+    a = torch.rand(B, hv, device="cuda", generator=g) * (1.0 - w.alpha_lo) + w.alpha_lo
+    b = torch.sigmoid(torch.randn(B, hv, device="cuda", generator=g))
+    if w.dtype == "bf16":
+        q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    return q.contiguous(), k.contiguous(), v.contiguous(), a.contiguous(), b.contiguous()
+
+
+def device_initial_state(torch, w, layer: int):
+    """S0 [B][Hv][d][d] on the device with the workload's law (outlier rows and
+    columns from per-head log-normal factors)."""
+    g = torch.Generator(device="cuda").manual_seed(w.seed * 1_000_003 + layer * 10_007 + 999_983)
+    S = torch.randn(w.B, w.hv, w.d, w.d, device="cuda", generator=g)
+    if w.s0 == "zero":
+        return S.zero_()
+    if w.s0 == "normal":
+        return S.mul_(w.s0_scale)
+    ra = torch.exp(torch.randn(1, w.hv, w.d, 1, device="cuda", generator=g) * w.outlier_sigma)
+    ce = torch.exp(torch.randn(1, w.hv, 1, w.d, device="cuda", generator=g) * w.outlier_sigma)
+    return S.mul_(ra).mul_(ce)
+
+
+def run_drift(args, np, torch, stq, wl, w) -> dict:
+    """Drift of the packed (quantized) trajectory against the FP32-state
+    trajectory from the same S0 with the same inputs: relative Frobenius error
+    of the dequantized state and relative L2 error of the readout, per layer
+    at checkpoints, aggregated over layers.  Small workloads draw inputs on
+    the host (the generator the tests use); the stacked one on the device."""
+    layers = args.layers or w.layers
+    T = args.drift_steps or w.T
+    if T >= 512:
+        checkpoints = sorted(set(list(range(256, T + 1, 256)) + [T]))
+    else:
+        checkpoints = sorted(set([1, 2, max(1, T // 4), max(1, T // 2), T]))
+    # one layer small enough to draw on the host every step
+    host = layers == 1 and w.units * w.d <= 1 << 22
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+
+    def inputs(layer, t, calibration=False):
+        if not host:
+            return device_inputs(torch, w, layer, t, calibration)
+        x = wl.workload_inputs(w, t, calibration=calibration, layer=layer)
+        if x.dtype == "bf16":
+            cv = lambda bits: dev(bits.view(np.int16)).view(torch.bfloat16)  # noqa: E731
+            return cv(x.q_bits), cv(x.k_bits), cv(x.v_bits), dev(x.alpha), dev(x.beta)
+        return dev(x.q), dev(x.k), dev(x.v), dev(x.alpha), dev(x.beta)
+
+    t0 = time.time()
+    quant, ref = [], []
+    for layer in range(layers):
+        S0 = dev(wl.initial_state(w, layer=layer)) if host else device_initial_state(torch, w, layer)
+        fp = stq.State(stq.Geometry(w.B, w.hv, w.hk, w.d, 0, stq.FMT_FP32))
+        fp.pack(S0)
+        n8 = w.n8
+        if w.calib_seed is None:  # all rows 8-bit, c = 1 (uniform rowwise INT8)
+            qs = stq.State(stq.Geometry(w.B, w.hv, w.hk, w.d, w.d, stq.FMT_INT8ROW))
+        else:
+            cal = stq.State(stq.Geometry(1, w.hv, w.hk, w.d, n8, stq.FMT_MIXED48))
+            cal.calibrate(None, stq.CAL_RESET)
+            fpc = stq.State(stq.Geometry(w.B, w.hv, w.hk, w.d, 0, stq.FMT_FP32))
+            fpc.pack(S0)
+            for t in range(w.calib_steps):
+                fpc.decode_step(*inputs(layer, t, calibration=True))
+                last = t == w.calib_steps - 1
+                cal.calibrate(fpc.s32, stq.CAL_COLS | (stq.CAL_ROWS if last else 0))
+            cal.calibrate(None, stq.CAL_FINALIZE)
+            qs = stq.State(stq.Geometry(w.B, w.hv, w.hk, w.d, n8, stq.FMT_MIXED48))
+            qs.set_calibration(cal.c.clone(), cal.perm.clone())
+            del fpc, cal
+        qs.pack(S0)
+        del S0
+        quant.append(qs)
+        ref.append(fp)
+        if layer % 8 == 7:
+            torch.cuda.synchronize()
+            log(f"[drift] {layer + 1} of {layers} layers set up ({time.time() - t0:.0f}s)")
+    torch.cuda.synchronize()
+    log(f"[drift] {w.name}: {layers} layer(s) packed and calibrated in {time.time() - t0:.1f}s")
+
+    oq = torch.empty(w.B, w.hv, w.d, device="cuda")
+    of = torch.empty_like(oq)
+    points = []
+    o_err_sum = torch.zeros(layers, device="cuda", dtype=torch.float64)
+    o_ref_sum = torch.zeros_like(o_err_sum)
+    for t in range(1, T + 1):
+        check = t in checkpoints
+        o_rel = []
+        for layer in range(layers):
+            x = inputs(layer, t - 1)
+            quant[layer].decode_step(*x, o=oq)
+            ref[layer].decode_step(*x, o=of)
+            err = (oq - of).double().pow(2).sum()
+            nrm = of.double().pow(2).sum()
+            o_err_sum[layer] += err
+            o_ref_sum[layer] += nrm
+            if check:
+                o_rel.append(float((err / nrm).sqrt()))
+        if t % 64 == 0 and not check:
+            log(f"[drift] step {t} of {T} ({time.time() - t0:.0f}s)")
+        if check:
+            s_rel = []
+            for layer in range(layers):
+                Sq = quant[layer].dequant()
+                Sf = ref[layer].s32
+                s_rel.append(float((Sq - Sf).double().norm() / Sf.double().norm()))
+                del Sq
+            points.append(dict(step=t, state_rel_fro_mean=float(np.mean(s_rel)),
+                               state_rel_fro_max=float(np.max(s_rel)),
+                               readout_rel_l2_mean=float(np.mean(o_rel)),
+                               readout_rel_l2_max=float(np.max(o_rel))))
+            log(f"[drift] step {t}: state rel Frobenius mean {points[-1]['state_rel_fro_mean']:.3e}"
+                f" max {points[-1]['state_rel_fro_max']:.3e}, readout rel L2 mean "
+                f"{points[-1]['readout_rel_l2_mean']:.3e} ({time.time() - t0:.0f}s)")
+    o_all = (o_err_sum / o_ref_sum).sqrt().cpu().numpy()
+    return {"drift": {"workload": w.name, "layers": layers, "steps": T,
+                      "inputs": "host generator" if host else "device generator",
+                      "state": "packed" if w.calib_seed is not None else "int8row",
+                      "n8": w.n8 if w.calib_seed is not None else w.d,
+                      "checkpoints": points,
+                      "readout_rel_l2_over_all_steps_mean": float(np.mean(o_all)),
+                      "readout_rel_l2_over_all_steps_max": float(np.max(o_all))}}
 
 
 if __name__ == "__main__":

@@ -115,6 +115,15 @@ __device__ __forceinline__ void split3(float x, uint32_t &h0, uint32_t &h1, uint
     h2 = bf16_bits(r2);
 }
 
+// n / d for a wave-uniform n < 2^31, with m = ceil(2^32 / d) (d >= 2) or
+// m = 0 (d = 1): hi(n m) is the quotient or one more (scalar unit only).
+__device__ __forceinline__ unsigned udiv(unsigned n, unsigned d, unsigned m) {
+    if (m == 0) return n;
+    unsigned q = __umulhi(n, m);
+    if (q * d > n) --q;
+    return q;
+}
+
 struct Lane {
     int t, c, g;
     unsigned unit;
@@ -194,8 +203,9 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
             return __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, braw), zero,
                                                            0, 0, 0);
         };
+        float4 *red = &sh.red[w][0][gl][c]; // column offset e at red[32 e]
         auto store = [&](int e, const f32x4 &acc) {
-            if (gl < 2) sh.red[w][e][gl][c] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            if (gl < 2) red[32 * e] = make_float4(acc[0], acc[1], acc[2], acc[3]);
         };
         f32x4 acc0 = product(0);
         f32x4 acc1 = product(1);
@@ -225,7 +235,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
             const float4 f = sh.red[ww][ce][0][cc];
             u += (f.x + f.y) + f.z;
         }
-        sh.ez[ezi] = __builtin_fmaf(-L.alpha, u, sh.v[jcol] / sh.c[jcol]);
+        sh.ez[ezi] = __builtin_fmaf(-L.alpha, u, sh.v[jcol] * __builtin_amdgcn_rcpf(sh.c[jcol]));
     } else {
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
@@ -338,7 +348,8 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
 }
 
 template <int N8, typename TIn>
-__global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_remap) {
+__global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_remap, unsigned hv_m,
+                                                        unsigned g_m) {
     static_assert(N8 % 16 == 0 && N8 >= 0 && N8 <= D, "n8 must be a multiple of 16");
     __shared__ Smem sh;
 
@@ -357,9 +368,9 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
     }
     L.unit = unit;
     const int Hv = a.Hv;
-    const int b = static_cast<int>(unit / static_cast<unsigned>(Hv));
-    const int h = static_cast<int>(unit % static_cast<unsigned>(Hv));
-    const int hk = h / (Hv / a.Hk);
+    const int b = static_cast<int>(udiv(unit, static_cast<unsigned>(Hv), hv_m));
+    const int h = static_cast<int>(unit - static_cast<unsigned>(b) * static_cast<unsigned>(Hv));
+    const int hk = static_cast<int>(udiv(static_cast<unsigned>(h), static_cast<unsigned>(Hv / a.Hk), g_m));
     const int slot = a.slots ? a.slots[b] : b;
     if (slot < 0 || slot >= a.n_slots) { // whole workgroup leaves together
         if (t < D) a.o[static_cast<size_t>(unit) * D + t] = __int_as_float(0x7fc00000);
@@ -405,7 +416,7 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
         const float bk = L.beta * kp;
         // |b k| > 2^-64 |a r| (false when both vanish: then x = 0 * z = 0)
         const bool scaled = fabsf(bk) > fabsf(ar) * kFormTiny;
-        sh.row[p] = make_float4(scaled ? ar / bk : ar, scaled ? bk : 1.0f, 0.0f,
+        sh.row[p] = make_float4(scaled ? ar * __builtin_amdgcn_rcpf(bk) : ar, scaled ? bk : 1.0f, 0.0f,
                                 __int_as_float(scaled ? 0 : D));
         const float kq = wave_sum(kp * qp);
         if ((t & 63) == 0) sh.kq[t >> 6] = kq;
@@ -420,14 +431,23 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
     finish_unit<N8>(a, sh, L, w0, w1);
 }
 
+// ceil(2^32 / d) for d >= 2, 0 for d = 1 (see udiv)
+unsigned div_magic(unsigned d) {
+    return d <= 1 ? 0u : static_cast<unsigned>(((1ull << 32) + d - 1) / d);
+}
+
 template <int N8>
 hipError_t launch_n8(bool bf16, const DecodeArgs &a, hipStream_t s) {
     const unsigned units = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.Hv);
     const int remap = (units % 8u) == 0u ? 1 : 0;
+    const unsigned hv_m = div_magic(static_cast<unsigned>(a.Hv));
+    const unsigned g_m = div_magic(static_cast<unsigned>(a.Hv / a.Hk));
     if (bf16)
-        hipLaunchKernelGGL((decode128_kernel<N8, uint16_t>), dim3(units), dim3(256), 0, s, a, remap);
+        hipLaunchKernelGGL((decode128_kernel<N8, uint16_t>), dim3(units), dim3(256), 0, s, a, remap,
+                           hv_m, g_m);
     else
-        hipLaunchKernelGGL((decode128_kernel<N8, float>), dim3(units), dim3(256), 0, s, a, remap);
+        hipLaunchKernelGGL((decode128_kernel<N8, float>), dim3(units), dim3(256), 0, s, a, remap,
+                           hv_m, g_m);
     return hipGetLastError();
 }
 
