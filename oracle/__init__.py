@@ -17,6 +17,11 @@ Parity status of each function (what pins it is in ``tests/test_oracle_pins.py``
                  Proposition 1 identity, half-step bound, S0 = 0 closed form
   fp_step        pinned: App. B.1 norm identity, App. B.3 isolated-row read error
   calib_*        pinned: numpy max / stable argsort (library routines)
+  pack_refit,    pinned: exact recovery of the column factors of an exactly
+  step_refit,            representable state, covariance under column scaling,
+  dequant_cs             weighted least-squares optimality (App. C.1 objective),
+                         zero-column rule, fixed point
+  impact_*       pinned: closed forms for unit-vector keys and queries
 """
 from __future__ import annotations
 
@@ -64,8 +69,15 @@ def _bind(path: Path):
     lib.oracle_calib_cols.argtypes = [L, I, I, I, P, P]
     lib.oracle_calib_rows.argtypes = [L, I, I, I, P, P]
     lib.oracle_calib_finalize.argtypes = [I, I, I, I, P, P, P, P]
+    lib.oracle_dequant_cs.argtypes = [I, I, I, I, I, P, P, P, P, P, P, I]
+    lib.oracle_pack_refit.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, P, I]
+    lib.oracle_step_refit.argtypes = [I, I, I, I, I, I] + [P] * 17 + [I]
+    lib.oracle_impact_accumulate.argtypes = [I, I, I, I, P, P, P, P, P]
+    lib.oracle_impact_weights.argtypes = [I, I, P, P]
     for name in ("oracle_dequant", "oracle_pack", "oracle_step", "oracle_fp_step",
-                 "oracle_calib_cols", "oracle_calib_rows", "oracle_calib_finalize"):
+                 "oracle_calib_cols", "oracle_calib_rows", "oracle_calib_finalize",
+                 "oracle_dequant_cs", "oracle_pack_refit", "oracle_step_refit",
+                 "oracle_impact_accumulate", "oracle_impact_weights"):
         getattr(lib, name).restype = I
     return lib
 
@@ -232,6 +244,96 @@ class Oracle:
         return c, perm
 
 
+    # ---- per-state column factors with the online refit (App. C.1; Table C2
+    # step 5; reading R14)
+    def dequant_cs(self, pool8, pool4, r, cs, perm, *, n8: int, nthreads: int = 1):
+        """S_ij = r_i cs_j z_ij with per-state column factors cs [B][Hv][dv]."""
+        r = _c(r, np.float32)
+        B, hv, dk = r.shape
+        cs = _c(cs, np.float32)
+        dv = cs.shape[2]
+        pool8 = _c(pool8, np.int8).reshape(B, hv, n8, dv)
+        pool4 = _c(pool4, np.uint8).reshape(B, hv, dk - n8, dv // 2)
+        perm = _c(perm, np.int32)
+        S = np.empty((B, hv, dk, dv), np.float64)
+        rc = self.lib().oracle_dequant_cs(B, hv, dk, dv, n8, _ptr(pool8), _ptr(pool4), _ptr(r),
+                                          _ptr(cs), _ptr(perm), _ptr(S), nthreads)
+        assert rc == 0
+        return S
+
+    def pack_refit(self, S, c0, perm, w2, *, n8: int, nthreads: int = 1):
+        """Codes and row factors against c0 [Hv][dv], then the per-state column
+        refit (weights w2 [Hv][dk], logical rows).  Returns pool8, pool4, r, cs."""
+        S = _c(S, np.float32)
+        B, hv, dk, dv = S.shape
+        c0 = _c(c0, np.float32)
+        perm = _c(perm, np.int32)
+        w2 = _c(w2, np.float32)
+        pool8 = np.zeros((B, hv, n8, dv), np.int8)
+        pool4 = np.zeros((B, hv, dk - n8, dv // 2), np.uint8)
+        r = np.empty((B, hv, dk), np.float32)
+        cs = np.empty((B, hv, dv), np.float32)
+        rc = self.lib().oracle_pack_refit(B, hv, dk, dv, n8, _ptr(S), _ptr(c0), _ptr(perm),
+                                          _ptr(w2), _ptr(pool8), _ptr(pool4), _ptr(r), _ptr(cs),
+                                          nthreads)
+        assert rc == 0
+        return pool8, pool4, r, cs
+
+    def step_refit(self, pool8, pool4, r, cs, perm, w2, q, k, v, alpha, beta, *, n8: int,
+                   want_X: bool = False, nthreads: int = 1):
+        """One decode step with per-state column factors and the online column
+        refit (Table C2 steps 1-6).  Returns dict pool8, pool4, r, cs, o (and X)."""
+        r = _c(r, np.float32)
+        B, hv, dk = r.shape
+        cs = _c(cs, np.float32)
+        dv = cs.shape[2]
+        q = _c(q, np.float32)
+        hk = q.shape[1]
+        k = _c(k, np.float32)
+        v = _c(v, np.float32)
+        alpha = _c(alpha, np.float32)
+        beta = _c(beta, np.float32)
+        pool8 = _c(pool8, np.int8).reshape(B, hv, n8, dv)
+        pool4 = _c(pool4, np.uint8).reshape(B, hv, dk - n8, dv // 2)
+        perm = _c(perm, np.int32)
+        w2 = _c(w2, np.float32)
+        out = {"pool8": np.zeros_like(pool8), "pool4": np.zeros_like(pool4),
+               "r": np.empty_like(r), "cs": np.empty_like(cs),
+               "o": np.empty((B, hv, dv), np.float32)}
+        X = np.empty((B, hv, dk, dv), np.float64) if want_X else None
+        rc = self.lib().oracle_step_refit(
+            B, hv, hk, dk, dv, n8, _ptr(pool8), _ptr(pool4), _ptr(r), _ptr(cs), _ptr(perm),
+            _ptr(w2), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(out["pool8"]),
+            _ptr(out["pool4"]), _ptr(out["r"]), _ptr(out["cs"]), _ptr(out["o"]), _ptr(X),
+            nthreads)
+        assert rc == 0
+        if want_X:
+            out["X"] = X
+        return out
+
+    def impact_accumulate(self, q, k, alpha, beta, omega, *, hv: int):
+        """omega[h][i] += sum over the batch of (alpha (q_i - beta k_i k.q))^2
+        (Sec. 4.1 row impact with the scalar gate; App. C.1).  omega [Hv][dk] f64."""
+        q = _c(q, np.float32)
+        B, hk, dk = q.shape
+        k = _c(k, np.float32)
+        alpha = _c(alpha, np.float32)
+        beta = _c(beta, np.float32)
+        assert omega.dtype == np.float64 and omega.shape == (hv, dk)
+        assert self.lib().oracle_impact_accumulate(B, hv, hk, dk, _ptr(q), _ptr(k), _ptr(alpha),
+                                                   _ptr(beta), _ptr(omega)) == 0
+
+    def impact_weights(self, omega):
+        """Squared row-impact weights w2 = (omega / mean omega)^(1/4) per head
+        (App. B.3: w proportional to omega^(1/8)), floored at 2^-32; an
+        all-zero head gives 1."""
+        omega = _c(omega, np.float64)
+        hv, dk = omega.shape
+        w2 = np.empty((hv, dk), np.float32)
+        assert self.lib().oracle_impact_weights(hv, dk, _ptr(omega), _ptr(w2)) == 0
+        return w2
+
+
 _default = Oracle()
 rhe = _default.rhe
 dequant = _default.dequant
@@ -241,3 +343,8 @@ fp_step = _default.fp_step
 calib_cols = _default.calib_cols
 calib_rows = _default.calib_rows
 calib_finalize = _default.calib_finalize
+dequant_cs = _default.dequant_cs
+pack_refit = _default.pack_refit
+step_refit = _default.step_refit
+impact_accumulate = _default.impact_accumulate
+impact_weights = _default.impact_weights

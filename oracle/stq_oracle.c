@@ -29,6 +29,16 @@
  *   R6  x_ij = X_ij / c_j is formed first (it feeds the row max), then x_ij / r_i.
  *   R7  codes are two's complement; 8-bit rows are int8, 4-bit rows are nibbles
  *       with the even column in the low nibble.
+ *   R14 the refit variant keeps column factors per state and, after the row
+ *       factors and codes of a step are taken against the current ones, refits
+ *       them once with the codes held fixed (App. C.1 fixed-code update; Table
+ *       C2 step 5) over all rows of the head, weights w2 = w^2; the new factor
+ *       is rounded to fp32 and floored at 2^-126, a zero denominator keeps the
+ *       old one.  The stored codes are those taken against the old factors.
+ *   R15 row-impact weights: omega_i = sum over calibration samples of
+ *       (alpha (q_i - beta k_i k.q))^2 (Sec. 4.1 with the scalar gate), and
+ *       w2_i = (omega_i / mean omega)^(1/4) (App. B.3: w ~ omega^(1/8)),
+ *       floored at 2^-32; an all-zero head gets w2 = 1.
  *
  * Arithmetic: every intermediate is an IEEE double; the persisted quantities
  * (r, o) are rounded once to fp32.  Build with -ffp-contract=off so that the
@@ -170,6 +180,35 @@ static void unit_requant(const orc_shape *s, const double *X, const float *c,
             if (z > qb) z = qb;
             if (z < -qb) z = -qb;
             write_code(p8, p4, s->n8, s->dv, p, j, (int)z);
+        }
+    }
+}
+
+/* Online column refit of one head (App. C.1, the fixed-code update; Table C2
+ * step 5; reading R14): with the codes z and row factors r just written for
+ * the updated state X (logical order) and the squared row-impact weights w2
+ * (logical order), every column factor becomes the weighted least-squares fit
+ * of X by v = r z with the codes held fixed,
+ *   c_j = sum_i w2_i v_ij X_ij / sum_i w2_i v_ij^2,   v_ij = r_i z_ij,
+ * rounded to fp32 and floored at 2^-126; a zero denominator keeps the
+ * previous c_j.  Sums run over physical rows in ascending order. */
+static void unit_refit(const orc_shape *s, const double *X, const int32_t *perm,
+                       const float *w2, const int8_t *p8, const uint8_t *p4,
+                       const float *r, float *c) {
+    const double floor_c = ldexp(1.0, -126);
+    for (int j = 0; j < s->dv; ++j) {
+        double num = 0.0, den = 0.0;
+        for (int p = 0; p < s->dk; ++p) {
+            int i = perm[p];
+            double vij = (double)r[p] * (double)read_code(p8, p4, s->n8, s->dv, p, j);
+            double wt = (double)w2[i];
+            num += wt * vij * X[(size_t)i * s->dv + j];
+            den += wt * vij * vij;
+        }
+        if (den > 0.0) {
+            double cn = (double)(float)(num / den);
+            if (cn < floor_c) cn = floor_c;
+            c[j] = (float)cn;
         }
     }
 }
@@ -392,6 +431,203 @@ int oracle_fp_step(int B, int hv, int hk, int dk, int dv, double *S,
     fp_ctx x = {{hv, hk, dk, dv, 0}, S, q, k, v, alpha, beta, o};
     if (check_shape(&x.s)) return -1;
     for_units((long)B * hv, nthreads, fp_unit, &x);
+    return 0;
+}
+
+/* ---------------------------------------------- per-state column factors -- */
+/* The refit variant keeps one column-factor vector per state, cs[B][Hv][dv],
+ * instead of one per head (App. C.1: the shared scales are refit to each
+ * updated state; reading R14). */
+
+typedef struct {
+    orc_shape s;
+    const int8_t *pool8;
+    const uint8_t *pool4;
+    const float *r, *cs;
+    const int32_t *perm;
+    double *S;
+} dequant_cs_ctx;
+
+static void dequant_cs_unit(void *vctx, long u) {
+    dequant_cs_ctx *x = (dequant_cs_ctx *)vctx;
+    const orc_shape *s = &x->s;
+    int h = (int)(u % s->hv);
+    unit_dequant(s, x->pool8 + u * unit8_bytes(s), x->pool4 + u * unit4_bytes(s),
+                 x->r + u * s->dk, x->cs + (size_t)u * s->dv, x->perm + (size_t)h * s->dk,
+                 x->S + (size_t)u * s->dk * s->dv);
+}
+
+/* Dequantize states whose column factors are per state (cs[B][Hv][dv]). */
+int oracle_dequant_cs(int B, int hv, int dk, int dv, int n8, const int8_t *pool8,
+                      const uint8_t *pool4, const float *r, const float *cs,
+                      const int32_t *perm, double *S, int nthreads) {
+    dequant_cs_ctx x = {{hv, 1, dk, dv, n8}, pool8, pool4, r, cs, perm, S};
+    if (check_shape(&x.s)) return -1;
+    for_units((long)B * hv, nthreads, dequant_cs_unit, &x);
+    return 0;
+}
+
+typedef struct {
+    orc_shape s;
+    const float *S;
+    const float *c0;
+    const int32_t *perm;
+    const float *w2;
+    int8_t *pool8;
+    uint8_t *pool4;
+    float *r, *cs;
+} pack_refit_ctx;
+
+static void pack_refit_unit(void *vctx, long u) {
+    pack_refit_ctx *x = (pack_refit_ctx *)vctx;
+    const orc_shape *s = &x->s;
+    int h = (int)(u % s->hv);
+    size_t n = (size_t)s->dk * s->dv;
+    double *X = (double *)malloc(n * sizeof(double));
+    for (size_t e = 0; e < n; ++e) X[e] = (double)x->S[(size_t)u * n + e];
+    float *c = x->cs + (size_t)u * s->dv;
+    memcpy(c, x->c0 + (size_t)h * s->dv, (size_t)s->dv * sizeof(float));
+    const int32_t *perm = x->perm + (size_t)h * s->dk;
+    int8_t *p8 = x->pool8 + u * unit8_bytes(s);
+    uint8_t *p4 = x->pool4 + u * unit4_bytes(s);
+    float *r = x->r + u * s->dk;
+    unit_requant(s, X, c, perm, p8, p4, r);
+    unit_refit(s, X, perm, x->w2 + (size_t)h * s->dk, p8, p4, r, c);
+    free(X);
+}
+
+/* Pack fp32 states with the refit: codes and row factors against the
+ * calibrated column factors c0[Hv][dv], then each state's own column factors
+ * refit to it (Table C2 steps 4-6 applied to a given state). */
+int oracle_pack_refit(int B, int hv, int dk, int dv, int n8, const float *S,
+                      const float *c0, const int32_t *perm, const float *w2,
+                      int8_t *pool8, uint8_t *pool4, float *r, float *cs,
+                      int nthreads) {
+    pack_refit_ctx x = {{hv, 1, dk, dv, n8}, S, c0, perm, w2, pool8, pool4, r, cs};
+    if (check_shape(&x.s)) return -1;
+    for_units((long)B * hv, nthreads, pack_refit_unit, &x);
+    return 0;
+}
+
+typedef struct {
+    orc_shape s;
+    const int8_t *pool8;
+    const uint8_t *pool4;
+    const float *r, *cs;
+    const int32_t *perm;
+    const float *w2;
+    const float *q, *k, *v, *alpha, *beta;
+    int8_t *pool8_out;
+    uint8_t *pool4_out;
+    float *r_out, *cs_out, *o;
+    double *X_out;
+} step_refit_ctx;
+
+static void step_refit_unit(void *vctx, long u) {
+    step_refit_ctx *x = (step_refit_ctx *)vctx;
+    const orc_shape *s = &x->s;
+    long b = u / s->hv;
+    int h = (int)(u % s->hv);
+    int hk = h / (s->hv / s->hk); /* reading R5 */
+    size_t n = (size_t)s->dk * s->dv;
+    double *S = (double *)calloc(n, sizeof(double));
+    double *q = (double *)calloc((size_t)s->dk, sizeof(double));
+    double *k = (double *)calloc((size_t)s->dk, sizeof(double));
+    double *v = (double *)calloc((size_t)s->dv, sizeof(double));
+    double *o = (double *)calloc((size_t)s->dv, sizeof(double));
+    const int32_t *perm = x->perm + (size_t)h * s->dk;
+    float *c = x->cs_out + (size_t)u * s->dv;
+    memcpy(c, x->cs + (size_t)u * s->dv, (size_t)s->dv * sizeof(float));
+
+    /* Table C2 step 1: reconstruct with this state's own column factors. */
+    unit_dequant(s, x->pool8 + u * unit8_bytes(s), x->pool4 + u * unit4_bytes(s),
+                 x->r + u * s->dk, c, perm, S);
+    for (int i = 0; i < s->dk; ++i) {
+        q[i] = (double)x->q[((size_t)b * s->hk + hk) * s->dk + i];
+        k[i] = (double)x->k[((size_t)b * s->hk + hk) * s->dk + i];
+    }
+    for (int j = 0; j < s->dv; ++j) v[j] = (double)x->v[(size_t)u * s->dv + j];
+    /* Table C2 steps 2-3. */
+    unit_delta_step(s->dk, s->dv, S, q, k, v, (double)x->alpha[u],
+                    (double)x->beta[u], o);
+    for (int j = 0; j < s->dv; ++j) x->o[(size_t)u * s->dv + j] = (float)o[j];
+    if (x->X_out) memcpy(x->X_out + (size_t)u * n, S, n * sizeof(double));
+    /* Table C2 step 4: row factors and codes against the current column
+     * factors; step 5: refit the column factors to the codes; step 6: store. */
+    int8_t *p8 = x->pool8_out + u * unit8_bytes(s);
+    uint8_t *p4 = x->pool4_out + u * unit4_bytes(s);
+    float *r = x->r_out + u * s->dk;
+    unit_requant(s, S, c, perm, p8, p4, r);
+    unit_refit(s, S, perm, x->w2 + (size_t)h * s->dk, p8, p4, r, c);
+    free(S);
+    free(q);
+    free(k);
+    free(v);
+    free(o);
+}
+
+/* One quantized decode step with per-state column factors and the online
+ * column refit (Table C2 steps 1-6).  cs / cs_out: [B][Hv][dv]; w2:
+ * [Hv][dk] squared row-impact weights in logical row order. */
+int oracle_step_refit(int B, int hv, int hk, int dk, int dv, int n8,
+                      const int8_t *pool8, const uint8_t *pool4, const float *r,
+                      const float *cs, const int32_t *perm, const float *w2,
+                      const float *q, const float *k, const float *v,
+                      const float *alpha, const float *beta, int8_t *pool8_out,
+                      uint8_t *pool4_out, float *r_out, float *cs_out, float *o,
+                      double *X_out, int nthreads) {
+    step_refit_ctx x = {{hv, hk, dk, dv, n8}, pool8, pool4, r, cs, perm, w2, q, k, v,
+                        alpha, beta, pool8_out, pool4_out, r_out, cs_out, o, X_out};
+    if (check_shape(&x.s)) return -1;
+    for_units((long)B * hv, nthreads, step_refit_unit, &x);
+    return 0;
+}
+
+/* Row impact (Sec. 4.1; App. C.1 with the scalar gate of reading R4): the
+ * readout error caused by an error in key row i of the previous state is
+ * carried by g_i = (A_t^T q_t)_i = alpha (q_i - beta k_i (k.q)), and
+ * omega_i = E[g_i^2] over calibration samples.  omega[Hv][dk] (logical rows)
+ * accumulates sum over the B samples of g_i^2 for every value head. */
+int oracle_impact_accumulate(int B, int hv, int hk, int dk, const float *q,
+                             const float *k, const float *alpha,
+                             const float *beta, double *omega) {
+    if (hv <= 0 || hk <= 0 || hv % hk != 0 || dk <= 0) return -1;
+    for (long b = 0; b < B; ++b)
+        for (int h = 0; h < hv; ++h) {
+            int g = h / (hv / hk);
+            const float *qq = q + ((size_t)b * hk + g) * dk;
+            const float *kk = k + ((size_t)b * hk + g) * dk;
+            double kq = 0.0;
+            for (int i = 0; i < dk; ++i) kq += (double)kk[i] * (double)qq[i];
+            double a = (double)alpha[(size_t)b * hv + h];
+            double be = (double)beta[(size_t)b * hv + h];
+            for (int i = 0; i < dk; ++i) {
+                double gi = a * ((double)qq[i] - be * (double)kk[i] * kq);
+                omega[(size_t)h * dk + i] += gi * gi;
+            }
+        }
+    return 0;
+}
+
+/* Squared row-impact weights from the accumulated omega (App. B.3: the row
+ * factor scales as omega^(1/8), so its square as omega^(1/4); the per-head
+ * normalisation cancels in the fit): w2_i = fl32((omega_i / mean omega)^(1/4))
+ * floored at 2^-32; a head whose omega is all zero gets w2 = 1. */
+int oracle_impact_weights(int hv, int dk, const double *omega, float *w2) {
+    const double floor_w = ldexp(1.0, -32);
+    for (int h = 0; h < hv; ++h) {
+        double mean = 0.0;
+        for (int i = 0; i < dk; ++i) mean += omega[(size_t)h * dk + i];
+        mean /= (double)dk;
+        for (int i = 0; i < dk; ++i) {
+            double w = 1.0;
+            if (mean > 0.0) {
+                w = (double)(float)pow(omega[(size_t)h * dk + i] / mean, 0.25);
+                if (w < floor_w) w = floor_w;
+            }
+            w2[(size_t)h * dk + i] = (float)w;
+        }
+    }
     return 0;
 }
 

@@ -12,6 +12,7 @@ import pytest
 
 import oracle as oracle_pkg
 from tests import test_oracle_pins as pins
+from tests import test_oracle_refit_pins as rpins
 
 SRC = Path(oracle_pkg.__file__).resolve().parent / "stq_oracle.c"
 
@@ -47,6 +48,19 @@ MUTANTS = [
     ("zero column kept at 0", "(m > 0.0) ? (float)m : 1.0f", "(float)m"),
     ("bit width from the logical row", "int qb = qmax_of_bits(row_bits(p, s->n8));",
      "int qb = qmax_of_bits(row_bits(i, s->n8));"),
+    ("refit weights dropped", "double wt = (double)w2[i];", "double wt = 1.0;"),
+    ("refit weight by physical row", "double wt = (double)w2[i];", "double wt = (double)w2[p];"),
+    ("refit denominator unweighted", "den += wt * vij * vij;", "den += vij * vij;"),
+    ("refit v includes the old column factor",
+     "double vij = (double)r[p] * (double)read_code(p8, p4, s->n8, s->dv, p, j);",
+     "double vij = (double)r[p] * (double)c[j] * (double)read_code(p8, p4, s->n8, s->dv, p, j);"),
+    ("refit on a zero denominator", "if (den > 0.0) {", "if (den >= 0.0) {"),
+    ("impact without beta", "double gi = a * ((double)qq[i] - be * (double)kk[i] * kq);",
+     "double gi = a * ((double)qq[i] - (double)kk[i] * kq);"),
+    ("impact without the gate", "double gi = a * ((double)qq[i] - be * (double)kk[i] * kq);",
+     "double gi = ((double)qq[i] - be * (double)kk[i] * kq);"),
+    ("impact weight exponent 1/8", "pow(omega[(size_t)h * dk + i] / mean, 0.25)",
+     "pow(omega[(size_t)h * dk + i] / mean, 0.125)"),
 ]
 
 
@@ -68,6 +82,13 @@ def _pin_cases():
         (pins.test_isolated_row_read_error, {"d": 16}),
         (pins.test_error_recursion_and_drift_bound, {}),
         (pins.test_calibration_matches_numpy_max_and_stable_argsort, {}),
+        (rpins.test_refit_recovers_exact_column_factors, {"d": 16, "n8": 8}),
+        (rpins.test_refit_covariant_under_column_scaling, {"lam": 4.0}),
+        (rpins.test_refit_minimises_weighted_objective, {}),
+        (rpins.test_refit_zero_column_keeps_previous_factor, {}),
+        (rpins.test_refit_step_fixed_point, {"d": 16, "n8": 8}),
+        (rpins.test_impact_closed_form_unit_vectors, {}),
+        (rpins.test_impact_weights_fourth_root_of_normalised_impact, {}),
     ]
 
 
