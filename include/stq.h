@@ -69,7 +69,10 @@ typedef enum {
     STQ_FMT_MIXED48 = 0, /* 4/8-bit key rows, fp32 r, calibrated c and perm */
     STQ_FMT_INT8ROW = 1, /* uniform symmetric rowwise-absmax INT8: n8 = d_k,
                             c = 1, identity row order (Sec. 5.1 baseline) */
-    STQ_FMT_FP32 = 2     /* unquantized fp32 state (the FP32-state baseline) */
+    STQ_FMT_FP32 = 2,    /* unquantized fp32 state (the FP32-state baseline) */
+    STQ_FMT_REFIT = 3    /* MIXED48 codes and row factors with column factors
+                            kept per state and refit at every step (App. C.1,
+                            Table C2 step 5); see "Online column refit" */
 } stq_format;
 
 typedef enum { STQ_F32 = 0, STQ_BF16 = 1 } stq_dtype;
@@ -106,11 +109,28 @@ typedef struct {
     float *cal_colpart; /* [Hv][STQ_CAL_CHUNKS][dv] per-chunk partials */
     double *cal_rowpart;/* [Hv][STQ_CAL_CHUNKS][dk] per-chunk partials */
     float *s32;         /* [n_slots][Hv][dk][dv]  FP32 format only */
+    float *cs;          /* [n_slots][Hv][dv]  REFIT: per-state column factors */
+    float *w2;          /* [Hv][dk]  REFIT: squared row-impact weights,
+                           logical rows (1 until calibrated) */
+    double *impact;     /* [Hv][dk]  REFIT calibration: accumulated row impact */
     int32_t calibrated; /* host flag: c and perm hold a calibration */
     int32_t reserved;
 } stq_state;
 
 #define STQ_CAL_CHUNKS 64
+
+/* Online column refit (format STQ_FMT_REFIT; the paper's online Key-Row-Aware
+ * Dual-axis Fitting, Sec. 4.3 "Column factors", App. C.1 fixed-code update,
+ * App. C.3 Table C2 step 5).  The state keeps its own column factors cs.  A
+ * decode step reconstructs with them, takes row factors and codes against
+ * them exactly as the MIXED48 step does, and then refits them once with the
+ * new codes held fixed:
+ *   c'_j = sum_i w2_i v_ij X_ij / sum_i w2_i v_ij^2,   v_ij = r'_i z'_ij,
+ * rounded to fp32 and floored at 2^-126 (a zero denominator keeps c_j).  The
+ * stored state is (z', r', c').  w2 are squared row-impact weights
+ * (stq_calibrate_impact), 1 until calibrated.  Packing a state (prefill
+ * boundary) starts from the calibrated per-head c and refits the same way.
+ * Decoding this format needs d_k = 128 and n8 a multiple of 16. */
 
 /* Bytes of device memory a state with this geometry needs (host arithmetic
  * only, no device call); 0 if the descriptor is invalid or unsupported. */
@@ -118,10 +138,11 @@ size_t stq_state_bytes(const stq_desc *desc);
 
 /* Carve a state out of the caller's device buffer `dev` (256-byte aligned,
  * `bytes` >= stq_state_bytes) and queue its initialisation on `stream`:
- * codes 0, r = 2^-126 (the state S = 0), c = 1, perm = identity, fp32 state 0,
- * statistics 0.  INT8ROW and FP32 states are ready to decode at once; a MIXED48
- * state must be calibrated (stq_calibrate with STQ_CAL_FINALIZE, or
- * stq_set_calibration) before stq_decode_step accepts it.
+ * codes 0, r = 2^-126 (the state S = 0), c = 1, cs = 1, w2 = 1,
+ * perm = identity, fp32 state 0, statistics 0.  INT8ROW and FP32 states are
+ * ready to decode at once; a MIXED48 or REFIT state must be calibrated
+ * (stq_calibrate with STQ_CAL_FINALIZE, or stq_set_calibration) before
+ * stq_decode_step accepts it.
  * Errors: STQ_E_ARG (null/misaligned), STQ_E_SHAPE / STQ_E_UNSUPPORTED (desc),
  * STQ_E_SPACE (short buffer), STQ_E_DEVICE (launch failed). */
 stq_status stq_alloc_state(const stq_desc *desc, void *dev, size_t bytes,
@@ -140,22 +161,40 @@ stq_status stq_alloc_state(const stq_desc *desc, void *dev, size_t bytes,
  * FINALIZE rewrites c and perm, which invalidates packed contents: pack the
  * state again afterwards.  The statistics are reduced in a fixed order, so the
  * result does not depend on scheduling.
- * Errors: STQ_E_ARG (null state/records, unknown flags, format not MIXED48),
+ * Errors: STQ_E_ARG (null state/records, unknown flags, format not MIXED48
+ * or REFIT),
  * STQ_E_SHAPE (n_rec < 0), STQ_E_DEVICE. */
 stq_status stq_calibrate(stq_state *st, const float *records, int64_t n_rec,
                          uint32_t flags, stq_stream_t stream);
 
+/* Row-impact calibration of a REFIT state (Sec. 4.1; App. C.1 with the
+ * scalar gate; App. B.3 for the exponent): for B calibration samples of one
+ * step (q, k [B][Hk][dk] fp32 or bf16 by `dtype`, alpha, beta [B][Hv] fp32),
+ * accumulate impact[h][i] += sum_b (alpha (q_i - beta k_i (k.q)))^2 in
+ * double, value head h reading key head h / (Hv / Hk).  Flags: STQ_CAL_RESET
+ * zeroes the sums first; STQ_CAL_FINALIZE sets the weights
+ *   w2[h][i] = fl32((impact_i / mean_i impact_i)^(1/4)), floored at 2^-32
+ * (all-zero head: 1).  B may be 0 with only RESET and/or FINALIZE.  The
+ * accumulation order is fixed, so results do not depend on scheduling.
+ * Errors: STQ_E_ARG (format not REFIT, null or misaligned inputs, unknown
+ * flags or dtype), STQ_E_SHAPE (B < 0), STQ_E_DEVICE. */
+stq_status stq_calibrate_impact(stq_state *st, const void *q, const void *k,
+                                int32_t dtype, const float *alpha, const float *beta,
+                                int32_t B, uint32_t flags, stq_stream_t stream);
+
 /* Install a calibration computed elsewhere: copies c [Hv][dv] (each > 0) and
  * perm [Hv][dk] (a permutation of 0..dk-1 per head) from device memory and
  * marks the state calibrated.  Like FINALIZE it invalidates packed contents.
- * Errors: STQ_E_ARG (null, format not MIXED48), STQ_E_DEVICE. */
+ * Errors: STQ_E_ARG (null, format not MIXED48 or REFIT), STQ_E_DEVICE. */
 stq_status stq_set_calibration(stq_state *st, const float *c, const int32_t *perm,
                                stq_stream_t stream);
 
 /* Pack fp32 states S [B][Hv][dk][dv] (logical order) into slots[b] (slots: a
  * device int32 array of B distinct slots, or NULL for slots 0..B-1): the
  * requantization half of a decode step applied to a given state (the
- * prefill-boundary pack).  FP32 format: copies S.
+ * prefill-boundary pack).  FP32 format: copies S.  REFIT: codes and row
+ * factors against the calibrated per-head c, then each state's column factors
+ * refit (see "Online column refit").
  * Errors: STQ_E_ARG, STQ_E_SHAPE (B < 1 or B > n_slots), STQ_E_STATE
  * (MIXED48 not calibrated), STQ_E_DEVICE. */
 stq_status stq_pack_state(const stq_state *st, const float *S, const int32_t *slots,
@@ -167,11 +206,14 @@ stq_status stq_pack_state(const stq_state *st, const float *S, const int32_t *sl
  *   S_hat = r c z;  u = S_hat^T k;  X = a S_hat + b k (v - a u)^T;  o = X^T q
  *   r'_i = max(fl32(max_j |X_ij / c_j| / q_b), 2^-126);
  *   z'_ij = clip(rhe(X_ij / c_j / r'_i), -q_b, q_b)
+ * REFIT format: c is the state's own cs, refit after the codes are taken.
  * q, k, v are fp32 or bf16 (`dtype`); alpha, beta and o are fp32.
  * Preconditions: slots distinct within a call (not checked on the device);
  * a slot outside [0, n_slots) is skipped and its o is filled with NaN.
  * Errors: STQ_E_ARG (null/misaligned pointer, bad dtype), STQ_E_SHAPE (B < 1
- * or B > n_slots), STQ_E_STATE (MIXED48 not calibrated), STQ_E_DEVICE. */
+ * or B > n_slots), STQ_E_STATE (MIXED48 or REFIT not calibrated),
+ * STQ_E_UNSUPPORTED (REFIT with d_k != 128 or n8 not a multiple of 16),
+ * STQ_E_DEVICE. */
 stq_status stq_decode_step(const stq_state *st, const int32_t *slots, int32_t B,
                            const void *q, const void *k, const void *v, int32_t dtype,
                            const float *alpha, const float *beta, float *o,
@@ -185,6 +227,7 @@ stq_status stq_decode_step(const stq_state *st, const int32_t *slots, int32_t B,
  * dst must have the same descriptor as src.  The step reads c and perm from
  * src only, so the codes written to dst are relative to src's calibration:
  * give dst the same c and perm before reading it back or decoding from it.
+ * REFIT: the refit column factors are written to dst's cs.
  * dst == src is the in-place step; pools that overlap partially are rejected.
  * Errors: as stq_decode_step; STQ_E_SHAPE if the descriptors differ,
  * STQ_E_ARG for partially overlapping pools. */
@@ -195,7 +238,8 @@ stq_status stq_decode_step_into(const stq_state *src, const stq_state *dst,
                                 stq_stream_t stream);
 
 /* Reconstruct S_ij = r_i c_j z_ij (Sec. 4.3) of slots[b] into fp32
- * S_out [B][Hv][dk][dv] in logical row order (FP32 format: copies the state).
+ * S_out [B][Hv][dk][dv] in logical row order (FP32 format: copies the state;
+ * REFIT: c is the state's own cs).
  * Errors: STQ_E_ARG, STQ_E_SHAPE, STQ_E_DEVICE. */
 stq_status stq_dequant_state(const stq_state *st, const int32_t *slots, int32_t B,
                              float *S_out, stq_stream_t stream);
@@ -209,7 +253,8 @@ stq_status stq_stream_copy(const void *src, void *dst, size_t bytes, stq_stream_
 /* Human-readable name of a status code (static string, never NULL). */
 const char *stq_status_str(int32_t status);
 
-/* Library ABI version (bumped on any change to the declarations above). */
+/* Library ABI version (bumped on any change to the declarations above):
+ * 2 since the REFIT format and its state fields. */
 int32_t stq_abi_version(void);
 
 #ifdef __cplusplus

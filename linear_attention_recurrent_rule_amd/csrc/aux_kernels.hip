@@ -36,43 +36,52 @@ template <int WIDTH> __device__ __forceinline__ float group_sum(float v) {
 }
 
 // Pack: x = S / c, r = max(fl32(max|x| / q_b), 2^-126), z = rhe(x / r)
-// (Sec. 2.2 and Sec. 4.3; IEEE divisions, this path is not timed).
-template <int D>
+// (Sec. 2.2 and Sec. 4.3; IEEE divisions, this path is not timed).  With
+// REFIT, each state's column factors are then refit to its codes (App. C.1
+// fixed-code update): c'_j = sum_i w2_i v_ij S_ij / sum_i w2_i v_ij^2 with
+// v = r z, summed over the unit's rows through LDS in a fixed order.
+template <int D, bool REFIT>
 __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     using G = Geo<D>;
     constexpr int C8 = G::C8, TPU = G::TPU, UPW = G::UPW;
+    __shared__ float2 red[REFIT ? UPW * C8 * D : 1]; // [unit][row group g][column]
     const int lt = threadIdx.x % TPU;
     const int ul = threadIdx.x / TPU;
     const int c = lt % C8;
     const int g = lt / C8;
     const long unit = static_cast<long>(blockIdx.x) * UPW + ul;
-    if (unit >= static_cast<long>(a.B) * a.Hv) return; // no barriers below
-    const int b = static_cast<int>(unit / a.Hv);
-    const int h = static_cast<int>(unit % a.Hv);
-    const int slot = a.slots ? a.slots[b] : b;
-    if (slot < 0 || slot >= a.n_slots) return;
+    const bool active = unit < static_cast<long>(a.B) * a.Hv;
+    const int b = active ? static_cast<int>(unit / a.Hv) : 0;
+    const int h = active ? static_cast<int>(unit % a.Hv) : 0;
+    const int slot = active ? (a.slots ? a.slots[b] : b) : -1;
+    const bool live = slot >= 0 && slot < a.n_slots; // whole units, no early exit
     const int n8 = a.n8;
-    const size_t ubase = static_cast<size_t>(slot) * a.Hv + h;
+    const size_t ubase = static_cast<size_t>(live ? slot : 0) * a.Hv + h;
     int8_t *p8 = a.pool8 + ubase * static_cast<size_t>(n8) * D;
     uint8_t *p4 = a.pool4 + ubase * static_cast<size_t>(D - n8) * (D / 2);
     float *rr = a.r + ubase * D;
-    const float *S = a.S_in + static_cast<size_t>(unit) * D * D;
+    const float *S = a.S_in + static_cast<size_t>(live ? unit : 0) * D * D;
     const float *cc = a.c + static_cast<size_t>(h) * D;
-    float cj[8];
+    float cj[8], num[8], den[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) cj[e] = cc[8 * c + e];
+    for (int e = 0; e < 8; ++e) {
+        cj[e] = cc[8 * c + e];
+        num[e] = 0.0f;
+        den[e] = 0.0f;
+    }
 
 #pragma unroll 1
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < 8 && live; ++m) {
         const int p = g + C8 * m;
         const int i = a.perm[static_cast<size_t>(h) * D + p] & (D - 1);
         const float4 s0 = *reinterpret_cast<const float4 *>(S + static_cast<size_t>(i) * D + 8 * c);
         const float4 s1 = *reinterpret_cast<const float4 *>(S + static_cast<size_t>(i) * D + 8 * c + 4);
-        float x[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        float x[8];
         float mx = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            x[e] = x[e] / cj[e];
+            x[e] = sv[e] / cj[e];
             mx = fmaxf(mx, fabsf(x[e]));
         }
         mx = group_max<C8>(mx);
@@ -87,6 +96,15 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
             y = fminf(fmaxf(y, -qb), qb);
             zq[e] = static_cast<int>(y);
         }
+        if (REFIT) {
+            const float wr = a.w2[static_cast<size_t>(h) * D + i] * rn;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float zf = static_cast<float>(zq[e]);
+                num[e] = __builtin_fmaf(wr * zf, sv[e], num[e]);
+                den[e] = __builtin_fmaf((wr * rn) * zf, zf, den[e]);
+            }
+        }
         if (is8) {
             uint2 t;
             t.x = (zq[0] & 0xFF) | ((zq[1] & 0xFF) << 8) | ((zq[2] & 0xFF) << 16) | ((zq[3] & 0xFF) << 24);
@@ -99,9 +117,25 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
             *reinterpret_cast<uint32_t *>(p4 + static_cast<size_t>(p - n8) * (D / 2) + 4 * c) = t;
         }
     }
+    if (REFIT) {
+        float2 *ru = red + static_cast<size_t>(ul) * C8 * D;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ru[g * D + 8 * c + e] = make_float2(num[e], den[e]);
+        __syncthreads();
+        if (live) {
+            for (int j = lt; j < D; j += TPU) {
+                float ns = 0.0f, ds = 0.0f;
+                for (int q = 0; q < C8; ++q) {
+                    const float2 f = ru[q * D + j];
+                    ns += f.x;
+                    ds += f.y;
+                }
+                a.cs[ubase * D + j] = ds > 0.0f ? fmaxf(ns / ds, kRowFloor) : cc[j];
+            }
+        }
+    }
 }
 
-// Dequantized read-back: S_ij = (r_p c_j) z_pj at logical row i = perm[p].
 template <int D>
 __global__ __launch_bounds__(256) void dequant_kernel(PackArgs a) {
     using G = Geo<D>;
@@ -122,7 +156,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(PackArgs a) {
     const int8_t *p8 = a.pool8 + ubase * static_cast<size_t>(n8) * D;
     const uint8_t *p4 = a.pool4 + ubase * static_cast<size_t>(D - n8) * (D / 2);
     const float *rr = a.r + ubase * D;
-    const float *cc = a.c + static_cast<size_t>(h) * D;
+    const float *cc = a.cs ? a.cs + ubase * D : a.c + static_cast<size_t>(h) * D;
 #pragma unroll 1
     for (int m = 0; m < 8; ++m) {
         const int p = g + C8 * m;
@@ -322,6 +356,67 @@ __global__ __launch_bounds__(256) void copy_kernel(const uint4 *__restrict__ src
     if (i < n) dst[i] = src[i];
 }
 
+// Row impact (Sec. 4.1; App. C.1 with the scalar gate): one workgroup per
+// value head walks the B samples in order; lane i accumulates
+// g_i^2 = (alpha (q_i - beta k_i k.q))^2 in double, with k.q reduced in a
+// fixed tree, so the sums do not depend on scheduling.
+template <typename T> __device__ __forceinline__ float load_in(const void *p, size_t i);
+template <> __device__ __forceinline__ float load_in<float>(const void *p, size_t i) {
+    return static_cast<const float *>(p)[i];
+}
+template <> __device__ __forceinline__ float load_in<uint16_t>(const void *p, size_t i) {
+    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(p)[i]) << 16);
+}
+
+__device__ __forceinline__ double block_sum128(double v, double *tmp) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = v;
+    __syncthreads();
+    const double s = tmp[0] + tmp[1];
+    __syncthreads();
+    return s;
+}
+
+template <int D, typename TIn>
+__global__ __launch_bounds__(128) void impact_accumulate_kernel(ImpactArgs a) {
+    __shared__ double tmp[2];
+    const int h = blockIdx.x;
+    const int i = threadIdx.x;
+    const int hk = h / (a.Hv / a.Hk);
+    double acc = 0.0;
+    for (int b = 0; b < a.B; ++b) {
+        const size_t base = (static_cast<size_t>(b) * a.Hk + hk) * D;
+        const double qi = i < D ? static_cast<double>(load_in<TIn>(a.q, base + i)) : 0.0;
+        const double ki = i < D ? static_cast<double>(load_in<TIn>(a.k, base + i)) : 0.0;
+        const double kq = block_sum128(ki * qi, tmp);
+        const double al = a.alpha[static_cast<size_t>(b) * a.Hv + h];
+        const double be = a.beta[static_cast<size_t>(b) * a.Hv + h];
+        const double g = al * (qi - be * ki * kq);
+        acc += g * g;
+    }
+    if (i < D) a.impact[static_cast<size_t>(h) * D + i] += acc;
+}
+
+// w2_i = fl32((impact_i / mean impact)^(1/4)), floored at 2^-32; an all-zero
+// head gets 1 (App. B.3: the row factor scales as impact^(1/8)).
+template <int D>
+__global__ __launch_bounds__(128) void impact_finalize_kernel(ImpactArgs a) {
+    __shared__ double tmp[2];
+    const int h = blockIdx.x;
+    const int i = threadIdx.x;
+    const double om = i < D ? a.impact[static_cast<size_t>(h) * D + i] : 0.0;
+    const double mean = block_sum128(om, tmp) / D;
+    if (i < D) {
+        float w = 1.0f;
+        if (mean > 0.0) {
+            w = static_cast<float>(sqrt(sqrt(om / mean)));
+            w = fmaxf(w, 2.3283064365386963e-10f); // 2^-32
+        }
+        a.w2[static_cast<size_t>(h) * D + i] = w;
+    }
+}
+
 unsigned grid_for(size_t n, unsigned cap = 4096) {
     size_t g = (n + 255) / 256;
     if (g < 1) g = 1;
@@ -346,7 +441,25 @@ template <int D> unsigned unit_grid(long units) {
 
 hipError_t launch_pack(int D, const PackArgs &a, hipStream_t s) {
     const long units = static_cast<long>(a.B) * a.Hv;
-    STQ_DISPATCH_D(D, hipLaunchKernelGGL((pack_kernel<DD>), dim3(unit_grid<DD>(units)), dim3(256), 0, s, a));
+    if (a.cs) {
+        STQ_DISPATCH_D(D, hipLaunchKernelGGL((pack_kernel<DD, true>), dim3(unit_grid<DD>(units)), dim3(256), 0, s, a));
+    } else {
+        STQ_DISPATCH_D(D, hipLaunchKernelGGL((pack_kernel<DD, false>), dim3(unit_grid<DD>(units)), dim3(256), 0, s, a));
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_impact_accumulate(int D, bool bf16, const ImpactArgs &a, hipStream_t s) {
+    if (bf16) {
+        STQ_DISPATCH_D(D, hipLaunchKernelGGL((impact_accumulate_kernel<DD, uint16_t>), dim3(a.Hv), dim3(128), 0, s, a));
+    } else {
+        STQ_DISPATCH_D(D, hipLaunchKernelGGL((impact_accumulate_kernel<DD, float>), dim3(a.Hv), dim3(128), 0, s, a));
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_impact_finalize(int D, const ImpactArgs &a, hipStream_t s) {
+    STQ_DISPATCH_D(D, hipLaunchKernelGGL((impact_finalize_kernel<DD>), dim3(a.Hv), dim3(128), 0, s, a));
     return hipGetLastError();
 }
 

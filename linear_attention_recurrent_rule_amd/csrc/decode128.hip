@@ -90,12 +90,13 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 // 8 state rows, then a zero row for the unused outputs.
 struct Smem {
     uint16_t coef[4][4][7][8];
-    float4 row[D];          // {P, s, -, offset of E in ez} per physical row
+    float4 row[D];          // {P, s, w2, offset of E in ez} per physical row
     float v[D], c[D];
     float ez[2 * D];        // e, then a zero vector; each as [e/4][c][e%4]
     float4 red[4][8][2][16]; // per wave, column offset e, lane group, chunk c
     float kq[2];
     float mul[16][8];       // per row group: code multipliers of its 8 rows
+    float ra[16][8], rb[16][8]; // column refit: w2 r' s and w2 r'^2 per row
 };
 
 // Round-to-nearest-even fp32 -> bf16 bit pattern (finite inputs).
@@ -134,6 +135,7 @@ struct Lane {
     uint8_t *q4;
     const float *rr;   // row factors read ...
     float *rw;         // ... and written
+    float *cw;         // refit column factors written (REFIT format)
 };
 
 // Fetch this lane's packed rows (Table C2 step 1).
@@ -155,7 +157,7 @@ __device__ __forceinline__ void load_codes(const Lane &L, uint32_t (&w0)[8], uin
 }
 
 // Everything after the staging barrier.
-template <int N8>
+template <int N8, bool REFIT>
 __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const Lane &L,
                                             const uint32_t (&w0)[8], const uint32_t (&w1)[8]) {
     constexpr int M8 = N8 / 16;
@@ -309,6 +311,11 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
         if ((c & 1) == 0) {
             L.rw[p] = rn;
             sh.mul[g][mm] = mul;
+            if (REFIT) {
+                const float w2 = sh.row[p].z;
+                sh.ra[g][mm] = (w2 * rn) * sc;
+                sh.rb[g][mm] = (w2 * rn) * rn;
+            }
         }
     }
     __syncthreads();
@@ -321,12 +328,33 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
         mulv[0] = m0.x; mulv[1] = m0.y; mulv[2] = m0.z; mulv[3] = m0.w;
         mulv[4] = m1.x; mulv[5] = m1.y; mulv[6] = m1.z; mulv[7] = m1.w;
     }
+    // column refit partial sums over this lane's 8 rows (REFIT): with
+    // x = s y, X = c x and v = r' z', sum_i w2 v X = c sum_i (w2 r' s) z' y
+    // and sum_i w2 v^2 = sum_i (w2 r'^2) z'^2
+    float num[8], den[8], rav[8], rbv[8];
+    if (REFIT) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            num[e] = 0.0f;
+            den[e] = 0.0f;
+            rav[e] = sh.ra[g][e];
+            rbv[e] = sh.rb[g][e];
+        }
+    }
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
         const unsigned p = static_cast<unsigned>(g + 16 * m);
         uint32_t bt[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) bt[e] = __float_as_uint(__builtin_fmaf(z[m][e], mulv[m], kRoundMagic));
+        if (REFIT) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float zq = __uint_as_float(bt[e]) - kRoundMagic; // the code, exactly
+                num[e] = __builtin_fmaf(rav[m] * zq, z[m][e], num[e]);
+                den[e] = __builtin_fmaf(rbv[m] * zq, zq, den[e]);
+            }
+        }
         if (m < M8) {
             const uint32_t a01 = __builtin_amdgcn_perm(bt[1], bt[0], 0x0C0C0400u);
             const uint32_t a23 = __builtin_amdgcn_perm(bt[3], bt[2], 0x04000C0Cu);
@@ -345,9 +373,34 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
             *reinterpret_cast<uint32_t *>(L.q4 + ((p - N8) * (D / 2) + 4 * c)) = word;
         }
     }
+    if (REFIT) {
+        // ---- Table C2 step 5: the column factors refit to the new codes
+        // (App. C.1 fixed-code update).  Partials per (wave, lane group,
+        // chunk c, column offset e) go through the MFMA reduction buffer,
+        // free since the column sums were read.
+        float2 *red2 = reinterpret_cast<float2 *>(&sh.red[0][0][0][0]); // [4][4][16][8]
+        float4 *mine = reinterpret_cast<float4 *>(red2 + ((w * 4 + gl) * 16 + c) * 8);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) mine[e / 2] = make_float4(num[e], den[e], num[e + 1], den[e + 1]);
+        __syncthreads();
+        if (t < D) {
+            const int cc = t & 15;
+            const int ce = (t >> 4) & 7;
+            const int jcol = 8 * cc + ce;
+            float nsum = 0.0f, dsum = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const float2 f = red2[(q * 16 + cc) * 8 + ce];
+                nsum += f.x;
+                dsum += f.y;
+            }
+            const float cold = sh.c[jcol];
+            L.cw[jcol] = dsum > 0.0f ? fmaxf(cold * (nsum / dsum), kRowFloor) : cold;
+        }
+    }
 }
 
-template <int N8, typename TIn>
+template <int N8, typename TIn, bool REFIT>
 __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_remap, unsigned hv_m,
                                                         unsigned g_m) {
     static_assert(N8 % 16 == 0 && N8 >= 0 && N8 <= D, "n8 must be a multiple of 16");
@@ -385,6 +438,7 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
     L.q8 = a.pool8_out + ub * (N8 * D);
     L.q4 = a.pool4_out + ub * ((D - N8) * (D / 2));
     L.rw = a.r_out + ub * D;
+    L.cw = REFIT ? a.cs_out + ub * D : nullptr;
 
     // ---- Table C2 step 1: issue the loads of this lane's packed rows
     uint32_t w0[8], w1[8];
@@ -416,19 +470,20 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
         const float bk = L.beta * kp;
         // |b k| > 2^-64 |a r| (false when both vanish: then x = 0 * z = 0)
         const bool scaled = fabsf(bk) > fabsf(ar) * kFormTiny;
-        sh.row[p] = make_float4(scaled ? ar * __builtin_amdgcn_rcpf(bk) : ar, scaled ? bk : 1.0f, 0.0f,
+        const float w2 = REFIT ? a.w2[h * D + i] : 0.0f;
+        sh.row[p] = make_float4(scaled ? ar * __builtin_amdgcn_rcpf(bk) : ar, scaled ? bk : 1.0f, w2,
                                 __int_as_float(scaled ? 0 : D));
         const float kq = wave_sum(kp * qp);
         if ((t & 63) == 0) sh.kq[t >> 6] = kq;
     } else {
         const int j = t - D;
         sh.v[j] = In<TIn>::get(a.v, static_cast<unsigned>((b * Hv + h) * D + j));
-        sh.c[j] = a.c[h * D + j];
+        sh.c[j] = REFIT ? a.cs[ub * D + j] : a.c[h * D + j];
         sh.ez[D + j] = 0.0f;
         if (j < 16) *reinterpret_cast<uint4 *>(&sh.coef[j >> 2][j & 3][6][0]) = make_uint4(0u, 0u, 0u, 0u);
     }
     __syncthreads();
-    finish_unit<N8>(a, sh, L, w0, w1);
+    finish_unit<N8, REFIT>(a, sh, L, w0, w1);
 }
 
 // ceil(2^32 / d) for d >= 2, 0 for d = 1 (see udiv)
@@ -442,12 +497,19 @@ hipError_t launch_n8(bool bf16, const DecodeArgs &a, hipStream_t s) {
     const int remap = (units % 8u) == 0u ? 1 : 0;
     const unsigned hv_m = div_magic(static_cast<unsigned>(a.Hv));
     const unsigned g_m = div_magic(static_cast<unsigned>(a.Hv / a.Hk));
-    if (bf16)
-        hipLaunchKernelGGL((decode128_kernel<N8, uint16_t>), dim3(units), dim3(256), 0, s, a, remap,
-                           hv_m, g_m);
+    const bool refit = a.cs != nullptr;
+    if (bf16 && refit)
+        hipLaunchKernelGGL((decode128_kernel<N8, uint16_t, true>), dim3(units), dim3(256), 0, s, a,
+                           remap, hv_m, g_m);
+    else if (bf16)
+        hipLaunchKernelGGL((decode128_kernel<N8, uint16_t, false>), dim3(units), dim3(256), 0, s, a,
+                           remap, hv_m, g_m);
+    else if (refit)
+        hipLaunchKernelGGL((decode128_kernel<N8, float, true>), dim3(units), dim3(256), 0, s, a,
+                           remap, hv_m, g_m);
     else
-        hipLaunchKernelGGL((decode128_kernel<N8, float>), dim3(units), dim3(256), 0, s, a, remap,
-                           hv_m, g_m);
+        hipLaunchKernelGGL((decode128_kernel<N8, float, false>), dim3(units), dim3(256), 0, s, a,
+                           remap, hv_m, g_m);
     return hipGetLastError();
 }
 

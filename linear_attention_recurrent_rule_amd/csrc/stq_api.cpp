@@ -21,18 +21,21 @@ bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 bool supported_d(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
 struct Layout {
-    size_t pool8, pool4, r, c, perm, colmax, rowscore, colpart, rowpart, s32, total;
+    size_t pool8, pool4, r, c, perm, colmax, rowscore, colpart, rowpart, s32, cs, w2, impact,
+        total;
 };
+
+bool calibrated_format(int32_t fmt) { return fmt == STQ_FMT_MIXED48 || fmt == STQ_FMT_REFIT; }
 
 // Validates a descriptor; fills byte sizes of each region (0 = absent).
 stq_status describe(const stq_desc *d, Layout *L) {
     if (!d) return STQ_E_ARG;
-    if (d->fmt < STQ_FMT_MIXED48 || d->fmt > STQ_FMT_FP32) return STQ_E_ARG;
+    if (d->fmt < STQ_FMT_MIXED48 || d->fmt > STQ_FMT_REFIT) return STQ_E_ARG;
     if (d->n_slots < 1 || d->n_heads_v < 1 || d->n_heads_k < 1) return STQ_E_SHAPE;
     if (d->n_heads_v % d->n_heads_k != 0) return STQ_E_SHAPE;
     if (d->d_k < 1 || d->d_v < 1) return STQ_E_SHAPE;
     if (d->d_k != d->d_v || !supported_d(d->d_k)) return STQ_E_UNSUPPORTED;
-    if (d->fmt == STQ_FMT_MIXED48 && (d->n8 < 0 || d->n8 > d->d_k)) return STQ_E_SHAPE;
+    if (calibrated_format(d->fmt) && (d->n8 < 0 || d->n8 > d->d_k)) return STQ_E_SHAPE;
     if (d->fmt == STQ_FMT_INT8ROW && d->n8 != d->d_k) return STQ_E_SHAPE;
     const size_t S = static_cast<size_t>(d->n_slots), H = static_cast<size_t>(d->n_heads_v);
     const size_t D = static_cast<size_t>(d->d_k);
@@ -47,15 +50,21 @@ stq_status describe(const stq_desc *d, Layout *L) {
     }
     L->c = H * D * sizeof(float);
     L->perm = H * D * sizeof(int32_t);
-    if (d->fmt == STQ_FMT_MIXED48) {
+    if (calibrated_format(d->fmt)) {
         L->colmax = H * D * sizeof(float);
         L->rowscore = H * D * sizeof(double);
         L->colpart = H * stq::kCalChunks * D * sizeof(float);
         L->rowpart = H * stq::kCalChunks * D * sizeof(double);
     }
+    if (d->fmt == STQ_FMT_REFIT) {
+        L->cs = S * H * D * sizeof(float);
+        L->w2 = H * D * sizeof(float);
+        L->impact = H * D * sizeof(double);
+    }
     L->total = round_up(L->pool8) + round_up(L->pool4) + round_up(L->r) + round_up(L->c) +
                round_up(L->perm) + round_up(L->colmax) + round_up(L->rowscore) +
-               round_up(L->colpart) + round_up(L->rowpart) + round_up(L->s32);
+               round_up(L->colpart) + round_up(L->rowpart) + round_up(L->s32) +
+               round_up(L->cs) + round_up(L->w2) + round_up(L->impact);
     return STQ_OK;
 }
 
@@ -72,8 +81,11 @@ stq_status check_state(const stq_state *st) {
         if (!st->r || !aligned(st->pool8, 16) || !aligned(st->pool4, 16)) return STQ_E_ARG;
         if ((L.pool8 && !st->pool8) || (L.pool4 && !st->pool4)) return STQ_E_ARG;
     }
-    if (st->desc.fmt == STQ_FMT_MIXED48 &&
+    if (calibrated_format(st->desc.fmt) &&
         (!st->colmax || !st->rowscore || !st->cal_colpart || !st->cal_rowpart))
+        return STQ_E_ARG;
+    if (st->desc.fmt == STQ_FMT_REFIT && (!st->cs || !st->w2 || !st->impact ||
+                                          !aligned(st->cs, 16) || !aligned(st->w2, 16)))
         return STQ_E_ARG;
     return STQ_OK;
 }
@@ -84,7 +96,7 @@ stq_status dev(hipError_t e) { return e == hipSuccess ? STQ_OK : STQ_E_DEVICE; }
 
 extern "C" {
 
-int32_t stq_abi_version(void) { return 1; }
+int32_t stq_abi_version(void) { return 2; }
 
 const char *stq_status_str(int32_t s) {
     switch (s) {
@@ -133,7 +145,10 @@ stq_status stq_alloc_state(const stq_desc *desc, void *devp, size_t bytes, stq_s
     st.cal_colpart = static_cast<float *>(take(L.colpart));
     st.cal_rowpart = static_cast<double *>(take(L.rowpart));
     st.s32 = static_cast<float *>(take(L.s32));
-    st.calibrated = desc->fmt == STQ_FMT_MIXED48 ? 0 : 1;
+    st.cs = static_cast<float *>(take(L.cs));
+    st.w2 = static_cast<float *>(take(L.w2));
+    st.impact = static_cast<double *>(take(L.impact));
+    st.calibrated = calibrated_format(desc->fmt) ? 0 : 1;
 
     const int D = desc->d_k;
     hipError_t he = hipSuccess;
@@ -148,6 +163,9 @@ stq_status stq_alloc_state(const stq_desc *desc, void *devp, size_t bytes, stq_s
     if (L.colmax) run(stq::launch_fill_u32(reinterpret_cast<uint32_t *>(st.colmax), L.colmax / 4, 0u, s));
     if (L.rowscore) run(stq::launch_fill_u64(reinterpret_cast<uint64_t *>(st.rowscore), L.rowscore / 8, 0u, s));
     if (L.s32) run(stq::launch_fill_u32(reinterpret_cast<uint32_t *>(st.s32), L.s32 / 4, 0u, s));
+    if (L.cs) run(stq::launch_fill_u32(reinterpret_cast<uint32_t *>(st.cs), L.cs / 4, kOneBits, s));
+    if (L.w2) run(stq::launch_fill_u32(reinterpret_cast<uint32_t *>(st.w2), L.w2 / 4, kOneBits, s));
+    if (L.impact) run(stq::launch_fill_u64(reinterpret_cast<uint64_t *>(st.impact), L.impact / 8, 0u, s));
     if (he != hipSuccess) return STQ_E_DEVICE;
     *out = st;
     return STQ_OK;
@@ -157,7 +175,7 @@ stq_status stq_calibrate(stq_state *st, const float *records, int64_t n_rec, uin
                          stq_stream_t stream) {
     stq_status e = check_state(st);
     if (e != STQ_OK) return e;
-    if (st->desc.fmt != STQ_FMT_MIXED48) return STQ_E_ARG;
+    if (!calibrated_format(st->desc.fmt)) return STQ_E_ARG;
     if (flags & ~(STQ_CAL_RESET | STQ_CAL_COLS | STQ_CAL_ROWS | STQ_CAL_FINALIZE)) return STQ_E_ARG;
     if (n_rec < 0) return STQ_E_SHAPE;
     const bool accumulate = (flags & (STQ_CAL_COLS | STQ_CAL_ROWS)) != 0;
@@ -198,13 +216,49 @@ stq_status stq_set_calibration(stq_state *st, const float *c, const int32_t *per
                                stq_stream_t stream) {
     stq_status e = check_state(st);
     if (e != STQ_OK) return e;
-    if (st->desc.fmt != STQ_FMT_MIXED48) return STQ_E_ARG;
+    if (!calibrated_format(st->desc.fmt)) return STQ_E_ARG;
     if (!c || !perm || !aligned(c, 16) || !aligned(perm, 16)) return STQ_E_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t n = static_cast<size_t>(st->desc.n_heads_v) * st->desc.d_k * 4;
     if ((e = dev(stq::launch_copy_bytes(c, st->c, n, s))) != STQ_OK) return e;
     if ((e = dev(stq::launch_copy_bytes(perm, st->perm, n, s))) != STQ_OK) return e;
     st->calibrated = 1;
+    return STQ_OK;
+}
+
+stq_status stq_calibrate_impact(stq_state *st, const void *q, const void *k, int32_t dtype,
+                                const float *alpha, const float *beta, int32_t B, uint32_t flags,
+                                stq_stream_t stream) {
+    stq_status e = check_state(st);
+    if (e != STQ_OK) return e;
+    if (st->desc.fmt != STQ_FMT_REFIT) return STQ_E_ARG;
+    if (flags & ~(STQ_CAL_RESET | STQ_CAL_FINALIZE)) return STQ_E_ARG;
+    if (B < 0) return STQ_E_SHAPE;
+    if (dtype != STQ_F32 && dtype != STQ_BF16) return STQ_E_ARG;
+    const size_t el = dtype == STQ_F32 ? 4 : 2;
+    if (B > 0 && (!q || !k || !alpha || !beta || !aligned(q, el) || !aligned(k, el) ||
+                  !aligned(alpha, 4) || !aligned(beta, 4)))
+        return STQ_E_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int D = st->desc.d_k, H = st->desc.n_heads_v;
+    stq::ImpactArgs a;
+    a.q = q;
+    a.k = k;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.B = B;
+    a.Hv = H;
+    a.Hk = st->desc.n_heads_k;
+    a.impact = st->impact;
+    a.w2 = st->w2;
+    if (flags & STQ_CAL_RESET)
+        if ((e = dev(stq::launch_fill_u64(reinterpret_cast<uint64_t *>(st->impact),
+                                          static_cast<size_t>(H) * D, 0u, s))) != STQ_OK)
+            return e;
+    if (B > 0)
+        if ((e = dev(stq::launch_impact_accumulate(D, dtype == STQ_BF16, a, s))) != STQ_OK) return e;
+    if (flags & STQ_CAL_FINALIZE)
+        if ((e = dev(stq::launch_impact_finalize(D, a, s))) != STQ_OK) return e;
     return STQ_OK;
 }
 
@@ -228,6 +282,8 @@ stq::PackArgs pack_args(const stq_state *st, const int32_t *slots, int32_t B) {
     a.slots = slots;
     a.S_in = nullptr;
     a.S_out = nullptr;
+    a.cs = st->desc.fmt == STQ_FMT_REFIT ? st->cs : nullptr;
+    a.w2 = st->desc.fmt == STQ_FMT_REFIT ? st->w2 : nullptr;
     a.B = B;
     a.Hv = st->desc.n_heads_v;
     a.n8 = st->desc.n8;
@@ -242,7 +298,7 @@ stq_status stq_pack_state(const stq_state *st, const float *S, const int32_t *sl
     stq_status e = batch_args(st, slots, B);
     if (e != STQ_OK) return e;
     if (!S || !aligned(S, 16)) return STQ_E_ARG;
-    if (st->desc.fmt == STQ_FMT_MIXED48 && !st->calibrated) return STQ_E_STATE;
+    if (calibrated_format(st->desc.fmt) && !st->calibrated) return STQ_E_STATE;
     stq::PackArgs a = pack_args(st, slots, B);
     a.S_in = S;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -289,11 +345,15 @@ stq_status decode(const stq_state *src, const stq_state *dst, const int32_t *slo
     if (!aligned(q, el) || !aligned(k, el) || !aligned(v, el) || !aligned(alpha, 4) ||
         !aligned(beta, 4) || !aligned(o, 4))
         return STQ_E_ARG;
-    if (src->desc.fmt == STQ_FMT_MIXED48 && !src->calibrated) return STQ_E_STATE;
+    if (calibrated_format(src->desc.fmt) && !src->calibrated) return STQ_E_STATE;
+    const bool refit = src->desc.fmt == STQ_FMT_REFIT;
+    if (refit && !(src->desc.d_k == 128 && stq::decode128_supported(src->desc.n8)))
+        return STQ_E_UNSUPPORTED;
     Layout L;
     describe(&src->desc, &L);
     if (partial_overlap(src->pool8, dst->pool8, L.pool8) || partial_overlap(src->pool4, dst->pool4, L.pool4) ||
-        partial_overlap(src->r, dst->r, L.r) || partial_overlap(src->s32, dst->s32, L.s32))
+        partial_overlap(src->r, dst->r, L.r) || partial_overlap(src->s32, dst->s32, L.s32) ||
+        partial_overlap(src->cs, dst->cs, L.cs))
         return STQ_E_ARG;
     stq::DecodeArgs a;
     a.pool8 = src->pool8;
@@ -306,6 +366,9 @@ stq_status decode(const stq_state *src, const stq_state *dst, const int32_t *slo
     a.s32_out = dst->s32;
     a.c = src->c;
     a.perm = src->perm;
+    a.cs = refit ? src->cs : nullptr;
+    a.cs_out = refit ? dst->cs : nullptr;
+    a.w2 = refit ? src->w2 : nullptr;
     a.slots = slots;
     a.q = q;
     a.k = k;

@@ -20,6 +20,9 @@ struct DecodeArgs {
     float *s32_out;       //                                      written
     const float *c;       // [Hv][D]
     const int32_t *perm;  // [Hv][D]
+    const float *cs;      // [n_slots][Hv][D] per-state column factors read
+    float *cs_out;        //                  and refit (REFIT format; else null)
+    const float *w2;      // [Hv][D] squared row-impact weights, logical rows
     const int32_t *slots; // [B] or nullptr (identity)
     const void *q;        // [B][Hk][D]
     const void *k;        // [B][Hk][D]
@@ -40,7 +43,20 @@ struct PackArgs {
     const int32_t *slots;
     const float *S_in; // pack: [B][Hv][D][D] logical order
     float *S_out;      // dequant: [B][Hv][D][D] logical order
+    float *cs;         // REFIT: [n_slots][Hv][D] per-state column factors
+                       // (pack writes them, dequant reads them); else null
+    const float *w2;   // REFIT: [Hv][D] squared row-impact weights
     int32_t B, Hv, n8, n_slots;
+};
+
+// Row-impact calibration of the refit format.
+struct ImpactArgs {
+    const void *q, *k;    // [B][Hk][D]
+    const float *alpha;   // [B][Hv]
+    const float *beta;    // [B][Hv]
+    int32_t B, Hv, Hk;
+    double *impact;       // [Hv][D] accumulated
+    float *w2;            // [Hv][D]
 };
 
 struct CalibArgs {
@@ -70,6 +86,8 @@ hipError_t launch_copy_slots_fp32(int D, const PackArgs &a, bool to_state, float
                                   hipStream_t s);
 hipError_t launch_calib_accumulate(int D, const CalibArgs &a, hipStream_t s);
 hipError_t launch_calib_finalize(int D, const CalibArgs &a, hipStream_t s);
+hipError_t launch_impact_accumulate(int D, bool bf16, const ImpactArgs &a, hipStream_t s);
+hipError_t launch_impact_finalize(int D, const ImpactArgs &a, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *dst, size_t n, uint32_t value, hipStream_t s);
 hipError_t launch_fill_u64(uint64_t *dst, size_t n, uint64_t value, hipStream_t s);
 hipError_t launch_iota_rows(int32_t *perm, int rows, int D, hipStream_t s);

@@ -20,7 +20,7 @@ STQ_OK = 0
 STATUS_NAMES = {0: "STQ_OK", 1: "STQ_E_ARG", 2: "STQ_E_SHAPE", 3: "STQ_E_UNSUPPORTED",
                 4: "STQ_E_SPACE", 5: "STQ_E_STATE", 6: "STQ_E_DEVICE"}
 
-FMT_MIXED48, FMT_INT8ROW, FMT_FP32 = 0, 1, 2
+FMT_MIXED48, FMT_INT8ROW, FMT_FP32, FMT_REFIT = 0, 1, 2, 3
 F32, BF16 = 0, 1
 CAL_RESET, CAL_COLS, CAL_ROWS, CAL_FINALIZE = 1, 2, 4, 8
 CAL_CHUNKS = 64
@@ -43,14 +43,15 @@ class CState(ctypes.Structure):
                 ("r", ctypes.c_void_p), ("c", ctypes.c_void_p), ("perm", ctypes.c_void_p),
                 ("colmax", ctypes.c_void_p), ("rowscore", ctypes.c_void_p),
                 ("cal_colpart", ctypes.c_void_p), ("cal_rowpart", ctypes.c_void_p),
-                ("s32", ctypes.c_void_p), ("calibrated", ctypes.c_int32),
+                ("s32", ctypes.c_void_p), ("cs", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("impact", ctypes.c_void_p), ("calibrated", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
 
 
 _LIB = None
-EXPORTS = ("stq_state_bytes", "stq_alloc_state", "stq_calibrate", "stq_set_calibration",
-           "stq_pack_state", "stq_decode_step", "stq_decode_step_into", "stq_dequant_state",
-           "stq_stream_copy", "stq_status_str", "stq_abi_version")
+EXPORTS = ("stq_state_bytes", "stq_alloc_state", "stq_calibrate", "stq_calibrate_impact",
+           "stq_set_calibration", "stq_pack_state", "stq_decode_step", "stq_decode_step_into",
+           "stq_dequant_state", "stq_stream_copy", "stq_status_str", "stq_abi_version")
 
 
 def _lib():
@@ -68,6 +69,7 @@ def _lib():
         lib.stq_alloc_state.argtypes = [ctypes.POINTER(Desc), P, SZ, P, ctypes.POINTER(CState)]
         lib.stq_calibrate.argtypes = [ctypes.POINTER(CState), P, I64, U32, P]
         lib.stq_set_calibration.argtypes = [ctypes.POINTER(CState), P, P, P]
+        lib.stq_calibrate_impact.argtypes = [ctypes.POINTER(CState), P, P, I32, P, P, I32, U32, P]
         lib.stq_pack_state.argtypes = [ctypes.POINTER(CState), P, P, I32, P]
         lib.stq_decode_step.argtypes = [ctypes.POINTER(CState), P, I32, P, P, P, I32, P, P, P, P]
         lib.stq_decode_step_into.argtypes = [ctypes.POINTER(CState), ctypes.POINTER(CState), P,
@@ -77,7 +79,8 @@ def _lib():
         lib.stq_status_str.argtypes = [I32]
         lib.stq_status_str.restype = ctypes.c_char_p
         lib.stq_abi_version.restype = I32
-        for name in ("stq_alloc_state", "stq_calibrate", "stq_set_calibration",
+        for name in ("stq_alloc_state", "stq_calibrate", "stq_calibrate_impact",
+                     "stq_set_calibration",
                      "stq_pack_state", "stq_decode_step", "stq_decode_step_into",
                      "stq_dequant_state", "stq_stream_copy"):
             getattr(lib, name).restype = I32
@@ -193,6 +196,21 @@ class State:
         return self._view("rowscore", torch.float64, (g.n_heads_v, g.d))
 
     @property
+    def cs(self):
+        g = self.geo
+        return self._view("cs", torch.float32, (g.n_slots, g.n_heads_v, g.d))
+
+    @property
+    def w2(self):
+        g = self.geo
+        return self._view("w2", torch.float32, (g.n_heads_v, g.d))
+
+    @property
+    def impact(self):
+        g = self.geo
+        return self._view("impact", torch.float64, (g.n_heads_v, g.d))
+
+    @property
     def calibrated(self) -> bool:
         return bool(self.c_state.calibrated)
 
@@ -201,6 +219,19 @@ class State:
         n = 0 if records is None else int(records.shape[0])
         _check(_lib().stq_calibrate(ctypes.byref(self.c_state), _dev_ptr(records, "records"),
                                     n, flags, _stream(stream)), "stq_calibrate")
+
+    def calibrate_impact(self, q, k, alpha, beta, flags: int, stream=None):
+        """Accumulate row impact over one step's samples (q, k [B][Hk][d], alpha,
+        beta [B][Hv]); CAL_RESET / CAL_FINALIZE as in stq_calibrate_impact."""
+        if q is None:
+            B, dt = 0, F32
+        else:
+            B = int(q.shape[0])
+            dt = BF16 if q.dtype == torch.bfloat16 else F32
+        _check(_lib().stq_calibrate_impact(ctypes.byref(self.c_state), _dev_ptr(q, "q"),
+                                           _dev_ptr(k, "k"), dt, _dev_ptr(alpha, "alpha"),
+                                           _dev_ptr(beta, "beta"), B, flags, _stream(stream)),
+               "stq_calibrate_impact")
 
     def set_calibration(self, c: torch.Tensor, perm: torch.Tensor, stream=None):
         _check(_lib().stq_set_calibration(ctypes.byref(self.c_state), _dev_ptr(c, "c"),

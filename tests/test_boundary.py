@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     assert "stq_decode_step" in names and len(names) >= 8
     for n in names:
         assert hasattr(lib, n), f"libstq.so does not export {n}"
-    assert lib.stq_abi_version() == 1
+    assert lib.stq_abi_version() == 2
 
 
 def _desc(n_slots=4, hv=4, hk=2, d=64, n8=32, fmt=stq.FMT_MIXED48, dv=None):
@@ -192,3 +192,35 @@ def test_decode_into_rejections():
     uncal = _fake_state(calibrated=0)
     assert into(ctypes.byref(uncal), ctypes.byref(src)) == E_STATE
     assert into(ctypes.byref(src), ctypes.byref(src), B=0) == E_SHAPE
+
+
+def test_refit_layout_and_rejections():
+    lib = stq.lib()
+    S, H, D, n8 = 64, 4, 128, 64
+    mixed = _bytes(n_slots=S, hv=H, hk=2, d=D, n8=n8)
+    refit = _bytes(n_slots=S, hv=H, hk=2, d=D, n8=n8, fmt=stq.FMT_REFIT)
+    # per-state column factors, squared row weights, accumulated impact
+    assert refit == mixed + _r(S * H * D * 4) + _r(H * D * 4) + _r(H * D * 8)
+    # decode of the refit format needs d = 128 and n8 a multiple of 16
+    for d, nn in ((64, 32), (128, 40)):
+        st = _fake_state(fmt=stq.FMT_REFIT, calibrated=1, n8=nn, d=d)
+        for i, f in enumerate(("cs", "w2", "impact")):
+            setattr(st, f, FAKE + 0x1000000 * (11 + i))
+        assert _decode(st) == E_UNSUPPORTED
+    st = _fake_state(fmt=stq.FMT_REFIT, calibrated=1, n8=64, d=128)
+    assert _decode(st) == E_ARG  # refit buffers missing
+    for i, f in enumerate(("cs", "w2", "impact")):
+        setattr(st, f, FAKE + 0x1000000 * (11 + i))
+    st.calibrated = 0
+    assert _decode(st) == E_STATE
+    # row-impact calibration: REFIT only, flags RESET | FINALIZE, B >= 0
+    st.calibrated = 1
+    ci = lambda s_, B, flags, q=FAKE, dtype=0: lib.stq_calibrate_impact(  # noqa: E731
+        ctypes.byref(s_), q, FAKE, dtype, FAKE, FAKE, B, flags, None)
+    assert ci(st, -1, stq.CAL_RESET) == E_SHAPE
+    assert ci(st, 2, stq.CAL_COLS) == E_ARG
+    assert ci(st, 2, 0, q=None) == E_ARG
+    assert ci(st, 2, 0, dtype=5) == E_ARG
+    assert ci(st, 2, 0, q=FAKE + 2) == E_ARG
+    mixed_st = _fake_state(calibrated=1)
+    assert ci(mixed_st, 0, stq.CAL_RESET) == E_ARG

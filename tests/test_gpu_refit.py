@@ -1,0 +1,221 @@
+"""GPU parity of the refit format (per-state column factors refit at every
+step: the STEPQuant paper's App. C.1 fixed-code update, App. C.3 Table C2
+step 5) against the CPU oracle, through the C ABI.
+
+Bar: codes and row factors as for the fixed-factor format (>= 99.99 % of codes
+identical, the rest +-1; r within 1e-6 relative); the refit column factors
+within 1e-5 relative: each is a quotient of two fp32 sums over 128 rows of
+non-negative terms (relative error at most 128 * 2^-24 = 7.6e-6 each, in
+practice far less); readout within 1e-4 relative L2; row impact within 1e-10
+relative (double sums), its weights within 1e-6.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from linear_attention_recurrent_rule_amd import workloads as wl
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("no GPU", allow_module_level=True)
+
+from linear_attention_recurrent_rule_amd import stq  # noqa: E402
+from tests import gpu_util as gu  # noqa: E402
+
+CS_RTOL = 1e-5
+
+
+def _calibration(g, hv, d):
+    c = g.lognormal(0, 0.7, size=(hv, d)).astype(np.float32)
+    perm = np.stack([g.permutation(d) for _ in range(hv)]).astype(np.int32)
+    w2 = (g.uniform(0.05, 1.0, size=(hv, d)) ** 0.5).astype(np.float32)
+    return c, perm, w2
+
+
+def _refit_state(B, hv, hk, d, n8, c, perm, w2, n_slots=None):
+    st = gu.make_state(B, hv, hk, d, n8, fmt=stq.FMT_REFIT, n_slots=n_slots)
+    st.set_calibration(gu.dev(c), gu.dev(perm))
+    st.w2.copy_(gu.dev(w2))
+    torch.cuda.synchronize()
+    return st
+
+
+def _load(st, p8, p4, r, cs):
+    if st.pool8 is not None and p8.size:
+        st.pool8.copy_(gu.dev(p8))
+    if st.pool4 is not None and p4.size:
+        st.pool4.copy_(gu.dev(p4))
+    st.r.copy_(gu.dev(r))
+    st.cs.copy_(gu.dev(cs))
+    torch.cuda.synchronize()
+
+
+def _refit_from(X, z, r, perm, w2, cs_old):
+    """The fixed-code fit restated for given codes (physical rows) and row
+    factors: c_j = sum_i w2_i v_ij X_ij / sum_i w2_i v_ij^2, v = r z; a zero
+    denominator keeps the old factor."""
+    B, hv, d, _ = X.shape
+    num = np.zeros((B, hv, d))
+    den = np.zeros((B, hv, d))
+    for h in range(hv):
+        i = perm[h]
+        v = r[:, h, :, None].astype(np.float64) * z[:, h].astype(np.float64)
+        wt = w2[h, i].astype(np.float64)[None, :, None]
+        num[:, h] = np.sum(wt * v * X[:, h][:, i, :], axis=1)
+        den[:, h] = np.sum(wt * v * v, axis=1)
+    out = np.where(den > 0, num / np.where(den > 0, den, 1), cs_old)
+    return np.maximum(out, 2.0 ** -126)
+
+
+def _compare_cs(got, ref, label="", *, X=None, z=None, zref=None, r=None, perm=None, w2=None,
+                cs_old=None):
+    """Column factors: where every code of a column matches the oracle's the
+    fit is unique and must agree to CS_RTOL; in a column where a code differs
+    by one (allowed at rounding ties), the fit of the GPU's own codes is
+    checked instead (X from the oracle)."""
+    ref = ref.astype(np.float64)
+    expect = ref
+    if X is not None:
+        differs = np.any(z != zref, axis=2)  # [B][Hv][d]: a code of column j differs
+        if differs.any():
+            alt = _refit_from(X, z, r, perm, w2, cs_old)
+            expect = np.where(differs, alt, ref)
+    rel = np.abs(got.astype(np.float64) - expect) / np.abs(expect)
+    assert rel.max() <= CS_RTOL, f"{label}: column factor rel diff {rel.max():.3g}"
+    return float(rel.max())
+
+
+@pytest.mark.parametrize("d,n8", [(16, 8), (32, 13), (64, 32), (128, 64), (128, 16), (128, 0)])
+def test_refit_pack_parity(oracle_mod, d, n8):
+    B, hv, hk = 3, 4, 2
+    print(f"[case] refit pack d={d} n8={n8}", flush=True)
+    g = wl.rng_for(801, d + n8)
+    c, perm, w2 = _calibration(g, hv, d)
+    S = wl.random_states(B, hv, d, seed=801 + d, outlier_sigma=1.0)
+    st = _refit_state(B, hv, hk, d, n8, c, perm, w2)
+    st.pack(gu.dev(S))
+    p8, p4, r = gu.read_packed(st)
+    cs = st.cs.cpu().numpy()
+    R8, R4, RR, RCS = oracle_mod.pack_refit(S, c, perm, w2, n8=n8)
+    zg = wl.unpack_codes(p8, p4).astype(np.int32)
+    zr = wl.unpack_codes(R8, R4).astype(np.int32)
+    assert np.mean(zg == zr) >= gu.CODE_MATCH_MIN and np.abs(zg - zr).max() <= 1
+    np.testing.assert_allclose(r, RR, rtol=gu.R_RTOL, atol=0)
+    c0 = np.ascontiguousarray(np.broadcast_to(c, (B, hv, d)))
+    print("max cs rel", _compare_cs(cs, RCS, f"pack d={d}", X=S.astype(np.float64), z=zg,
+                                    zref=zr, r=r, perm=perm, w2=w2, cs_old=c0))
+
+
+@pytest.mark.parametrize("n8,dtype", [(64, "bf16"), (64, "f32"), (16, "bf16"), (0, "f32"),
+                                      (128, "bf16")])
+def test_refit_step_parity(oracle_mod, n8, dtype):
+    B, hv, hk, d = 5, 8, 4, 128
+    print(f"[case] refit step n8={n8} {dtype}", flush=True)
+    g = wl.rng_for(802, n8)
+    c, perm, w2 = _calibration(g, hv, d)
+    S = wl.random_states(B, hv, d, seed=802 + n8, outlier_sigma=1.0)
+    P8, P4, R, CS = oracle_mod.pack_refit(S, c, perm, w2, n8=n8)
+    st = _refit_state(B, hv, hk, d, n8, c, perm, w2)
+    _load(st, P8, P4, R, CS)
+    x = wl.draw_inputs(B, hk, hv, d, dtype=dtype, seed=802, step=0)
+    o = gu.gpu_step(st, x)
+    p8, p4, r = gu.read_packed(st)
+    cs = st.cs.cpu().numpy()
+    ref = oracle_mod.step_refit(P8, P4, R, CS, perm, w2, x.q, x.k, x.v, x.alpha, x.beta, n8=n8,
+                                want_X=True)
+    stats = gu.compare_step(dict(pool8=p8, pool4=p4, r=r, o=o), ref, n8=n8, d=d,
+                            label=f"refit n8={n8}")
+    stats["max_cs_rel"] = _compare_cs(
+        cs, ref["cs"], f"refit step n8={n8}", X=ref["X"], z=wl.unpack_codes(p8, p4),
+        zref=wl.unpack_codes(ref["pool8"], ref["pool4"]), r=r, perm=perm, w2=w2, cs_old=CS)
+    print(stats)
+
+
+def test_refit_dequant_parity(oracle_mod):
+    B, hv, hk, d, n8 = 3, 4, 2, 64, 32
+    g = wl.rng_for(803, 0)
+    c, perm, w2 = _calibration(g, hv, d)
+    S = wl.random_states(B, hv, d, seed=803)
+    P8, P4, R, CS = oracle_mod.pack_refit(S, c, perm, w2, n8=n8)
+    st = _refit_state(B, hv, hk, d, n8, c, perm, w2)
+    _load(st, P8, P4, R, CS)
+    got = st.dequant().cpu().numpy()
+    ref = oracle_mod.dequant_cs(P8, P4, R, CS, perm, n8=n8)
+    np.testing.assert_allclose(got, ref, rtol=2e-7, atol=1e-30)
+
+
+def test_refit_trajectory_per_step(oracle_mod):
+    """Per-step parity along a trajectory: the GPU is fed the oracle's state
+    at every step (never the other way round)."""
+    B, hv, hk, d, n8 = 2, 4, 2, 128, 64
+    g = wl.rng_for(804, 0)
+    c, perm, w2 = _calibration(g, hv, d)
+    S = wl.random_states(B, hv, d, seed=804, outlier_sigma=1.0)
+    P8, P4, R, CS = oracle_mod.pack_refit(S, c, perm, w2, n8=n8)
+    st = _refit_state(B, hv, hk, d, n8, c, perm, w2)
+    for t in range(12):
+        print(f"[case] refit trajectory step {t}", flush=True)
+        _load(st, P8, P4, R, CS)
+        x = wl.draw_inputs(B, hk, hv, d, dtype="bf16", seed=804, step=t)
+        o = gu.gpu_step(st, x)
+        p8, p4, r = gu.read_packed(st)
+        ref = oracle_mod.step_refit(P8, P4, R, CS, perm, w2, x.q, x.k, x.v, x.alpha, x.beta,
+                                    n8=n8, want_X=True)
+        gu.compare_step(dict(pool8=p8, pool4=p4, r=r, o=o), ref, n8=n8, d=d, label=f"t={t}")
+        _compare_cs(st.cs.cpu().numpy(), ref["cs"], f"t={t}", X=ref["X"],
+                    z=wl.unpack_codes(p8, p4), zref=wl.unpack_codes(ref["pool8"], ref["pool4"]),
+                    r=r, perm=perm, w2=w2, cs_old=CS)
+        P8, P4, R, CS = ref["pool8"], ref["pool4"], ref["r"], ref["cs"]
+
+
+def test_refit_decode_into_writes_destination_factors(oracle_mod):
+    B, hv, hk, d, n8 = 3, 4, 2, 128, 64
+    g = wl.rng_for(805, 0)
+    c, perm, w2 = _calibration(g, hv, d)
+    S = wl.random_states(B, hv, d, seed=805)
+    P8, P4, R, CS = oracle_mod.pack_refit(S, c, perm, w2, n8=n8)
+    src = _refit_state(B, hv, hk, d, n8, c, perm, w2)
+    dst = _refit_state(B, hv, hk, d, n8, c, perm, w2)
+    ref_st = _refit_state(B, hv, hk, d, n8, c, perm, w2)
+    _load(src, P8, P4, R, CS)
+    _load(ref_st, P8, P4, R, CS)
+    x = wl.draw_inputs(B, hk, hv, d, dtype="bf16", seed=805, step=0)
+    q, k, v, a, b = gu.inputs_to_device(x)
+    o1 = src.decode_step_into(dst, q, k, v, a, b)
+    o2 = ref_st.decode_step(q, k, v, a, b)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(dst.cs, ref_st.cs) and torch.equal(dst.r, ref_st.r)
+    np.testing.assert_array_equal(src.cs.cpu().numpy(), CS)  # source untouched
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_impact_calibration_parity(oracle_mod, dtype):
+    B, hv, hk, d, n8 = 6, 8, 4, 64, 32
+    st = gu.make_state(B, hv, hk, d, n8, fmt=stq.FMT_REFIT)
+    om = np.zeros((hv, d))
+    st.calibrate_impact(None, None, None, None, stq.CAL_RESET)
+    for t in range(3):
+        x = wl.draw_inputs(B, hk, hv, d, dtype=dtype, seed=806, step=t)
+        q, k, v, a, b = gu.inputs_to_device(x)
+        st.calibrate_impact(q, k, a, b, 0)
+        oracle_mod.impact_accumulate(x.q, x.k, x.alpha, x.beta, om, hv=hv)
+    st.calibrate_impact(None, None, None, None, stq.CAL_FINALIZE)
+    torch.cuda.synchronize()
+    got = st.impact.cpu().numpy()
+    np.testing.assert_allclose(got, om, rtol=1e-10, atol=0)
+    np.testing.assert_allclose(st.w2.cpu().numpy(), oracle_mod.impact_weights(om), rtol=1e-6,
+                               atol=0)
+
+
+def test_refit_decode_rejects_unsupported_geometry():
+    st = gu.make_state(2, 4, 2, 64, 32, fmt=stq.FMT_REFIT)
+    st.set_calibration(gu.dev(np.ones((4, 64), np.float32)),
+                       gu.dev(np.tile(np.arange(64, dtype=np.int32), (4, 1))))
+    x = wl.draw_inputs(2, 2, 4, 64, dtype="f32", seed=1, step=0)
+    with pytest.raises(stq.StqError) as ei:
+        gu.gpu_step(st, x)
+    assert ei.value.status == 3
