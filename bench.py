@@ -67,6 +67,9 @@ def parse():
                    help="instead of timing: run the workload's T steps on the packed state and "
                         "on an FP32 state from the same S0 and print the drift as one JSON line")
     p.add_argument("--layers", type=int, default=None, help="layers for --drift (default: all)")
+    p.add_argument("--refit", action="store_true",
+                   help="--drift with the refit format (per-state column factors refit every "
+                        "step, row-impact weights from the calibration steps)")
     p.add_argument("--drift-steps", type=int, default=None, help="T for --drift (default: the "
                    "workload's)")
     return p.parse_args()
@@ -77,6 +80,8 @@ def unit_state_bytes(fmt: str, d: int, n8: int) -> int:
         return 4 * d * d
     if fmt == "int8row":
         return d * d + 4 * d
+    if fmt == "refit":  # plus the state's own column factors
+        return n8 * d + (d - n8) * d // 2 + 8 * d
     return n8 * d + (d - n8) * d // 2 + 4 * d
 
 
@@ -166,7 +171,7 @@ def main():
         pools = []
         for _ in range(n):
             st = stq.State(stq.Geometry(B, hv, hk, d, n8, fmt))
-            if fmt == stq.FMT_MIXED48:
+            if fmt in (stq.FMT_MIXED48, stq.FMT_REFIT):
                 st.set_calibration(c, perm)
             st.pack(S0)
             pools.append(st)
@@ -234,6 +239,9 @@ def main():
                                                    args.steps, args.warmup)
         variants["int8row"] = measure("int8row", stq.FMT_INT8ROW, d, args.pools, args.steps,
                                       args.warmup)
+        if d == 128 and w.n8 % 16 == 0:
+            variants["refit_column_factors"] = measure("refit", stq.FMT_REFIT, w.n8, args.pools,
+                                                       args.steps, args.warmup)
         variants["fp32_state"] = measure("fp32", stq.FMT_FP32, 0, 2, args.steps, args.warmup)
         for k_, v_ in variants.items():
             log(f"[bench] {k_}: {v_['updates_per_s'] / 1e6:.1f} M updates/s, "
@@ -382,17 +390,26 @@ def run_drift(args, np, torch, stq, wl, w) -> dict:
         if w.calib_seed is None:  # all rows 8-bit, c = 1 (uniform rowwise INT8)
             qs = stq.State(stq.Geometry(w.B, w.hv, w.hk, w.d, w.d, stq.FMT_INT8ROW))
         else:
-            cal = stq.State(stq.Geometry(1, w.hv, w.hk, w.d, n8, stq.FMT_MIXED48))
+            fmt = stq.FMT_REFIT if args.refit else stq.FMT_MIXED48
+            cal = stq.State(stq.Geometry(1, w.hv, w.hk, w.d, n8, fmt))
             cal.calibrate(None, stq.CAL_RESET)
+            if args.refit:
+                cal.calibrate_impact(None, None, None, None, stq.CAL_RESET)
             fpc = stq.State(stq.Geometry(w.B, w.hv, w.hk, w.d, 0, stq.FMT_FP32))
             fpc.pack(S0)
             for t in range(w.calib_steps):
-                fpc.decode_step(*inputs(layer, t, calibration=True))
+                x = inputs(layer, t, calibration=True)
+                fpc.decode_step(*x)
+                if args.refit:
+                    cal.calibrate_impact(x[0], x[1], x[3], x[4], 0)
                 last = t == w.calib_steps - 1
                 cal.calibrate(fpc.s32, stq.CAL_COLS | (stq.CAL_ROWS if last else 0))
             cal.calibrate(None, stq.CAL_FINALIZE)
-            qs = stq.State(stq.Geometry(w.B, w.hv, w.hk, w.d, n8, stq.FMT_MIXED48))
+            qs = stq.State(stq.Geometry(w.B, w.hv, w.hk, w.d, n8, fmt))
             qs.set_calibration(cal.c.clone(), cal.perm.clone())
+            if args.refit:
+                cal.calibrate_impact(None, None, None, None, stq.CAL_FINALIZE)
+                qs.w2.copy_(cal.w2)
             del fpc, cal
         qs.pack(S0)
         del S0
@@ -441,7 +458,8 @@ def run_drift(args, np, torch, stq, wl, w) -> dict:
     o_all = (o_err_sum / o_ref_sum).sqrt().cpu().numpy()
     return {"drift": {"workload": w.name, "layers": layers, "steps": T,
                       "inputs": "host generator" if host else "device generator",
-                      "state": "packed" if w.calib_seed is not None else "int8row",
+                      "state": ("int8row" if w.calib_seed is None
+                                else "packed, refit column factors" if args.refit else "packed"),
                       "n8": w.n8 if w.calib_seed is not None else w.d,
                       "checkpoints": points,
                       "readout_rel_l2_over_all_steps_mean": float(np.mean(o_all)),
