@@ -129,8 +129,7 @@ typedef struct {
  * rounded to fp32 and floored at 2^-126 (a zero denominator keeps c_j).  The
  * stored state is (z', r', c').  w2 are squared row-impact weights
  * (stq_calibrate_impact), 1 until calibrated.  Packing a state (prefill
- * boundary) starts from the calibrated per-head c and refits the same way.
- * Decoding this format needs d_k = 128 and n8 a multiple of 16. */
+ * boundary) starts from the calibrated per-head c and refits the same way. */
 
 /* Bytes of device memory a state with this geometry needs (host arithmetic
  * only, no device call); 0 if the descriptor is invalid or unsupported. */
@@ -212,7 +211,6 @@ stq_status stq_pack_state(const stq_state *st, const float *S, const int32_t *sl
  * a slot outside [0, n_slots) is skipped and its o is filled with NaN.
  * Errors: STQ_E_ARG (null/misaligned pointer, bad dtype), STQ_E_SHAPE (B < 1
  * or B > n_slots), STQ_E_STATE (MIXED48 or REFIT not calibrated),
- * STQ_E_UNSUPPORTED (REFIT with d_k != 128 or n8 not a multiple of 16),
  * STQ_E_DEVICE. */
 stq_status stq_decode_step(const stq_state *st, const int32_t *slots, int32_t B,
                            const void *q, const void *k, const void *v, int32_t dtype,

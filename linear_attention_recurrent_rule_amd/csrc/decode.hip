@@ -68,7 +68,7 @@ template <int D> struct Geo {
     static constexpr int UPW = 256 / TPU;  // units per 256-lane workgroup
 };
 
-template <int D, typename TIn>
+template <int D, typename TIn, bool REFIT>
 __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
     using G = Geo<D>;
     constexpr int C8 = G::C8, TPU = G::TPU, UPW = G::UPW;
@@ -79,6 +79,7 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
     __shared__ float s_e[UPW][D];
     __shared__ float s_red[UPW][2][C8][D];
     __shared__ float s_kq[UPW][C8];
+    __shared__ float s_w2[REFIT ? UPW : 1][D]; // squared row-impact weights, physical rows
 
     const int lt = threadIdx.x % TPU;
     const int ul = threadIdx.x / TPU;
@@ -123,19 +124,21 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
     }
     // Stage q, k (permuted to physical row order), v and c in LDS.
     for (int idx = lt; idx < D; idx += TPU) {
-        float kv = 0.0f, qv = 0.0f, vv = 0.0f, cv = 1.0f;
+        float kv = 0.0f, qv = 0.0f, vv = 0.0f, cv = 1.0f, wv = 0.0f;
         if (live) {
             const int i = a.perm[static_cast<size_t>(h) * D + idx] & (D - 1);
             const size_t kb = (static_cast<size_t>(b) * a.Hk + hk) * D;
             kv = In<TIn>::get(a.k, kb + i);
             qv = In<TIn>::get(a.q, kb + i);
             vv = In<TIn>::get(a.v, (static_cast<size_t>(b) * a.Hv + h) * D + idx);
-            cv = a.c[static_cast<size_t>(h) * D + idx];
+            cv = REFIT ? a.cs[ubase * D + idx] : a.c[static_cast<size_t>(h) * D + idx];
+            if (REFIT) wv = a.w2[static_cast<size_t>(h) * D + i];
         }
         s_k[ul][idx] = kv;
         s_q[ul][idx] = qv;
         s_v[ul][idx] = vv;
         s_c[ul][idx] = cv;
+        if (REFIT) s_w2[ul][idx] = wv;
     }
     __syncthreads();
 
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
     float ev[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) ev[e] = s_e[ul][8 * c + e];
-    float inv[8];
+    float inv[8], rnv[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
         const int p = g + C8 * m;
@@ -232,9 +235,18 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
         const float qinv = (p < n8) ? (1.0f / 127.0f) : (1.0f / 7.0f);
         const float rn = fmaxf(mx * qinv, kRowFloor);
         inv[m] = __builtin_amdgcn_rcpf(rn);
+        rnv[m] = rn;
         if (live && (m % C8) == (c % 8) && c < 8) rw[p] = rn;
     }
     // Table C2 step 6: codes against the stored factor, pack, write in place.
+    // With REFIT, also this lane's share of the column refit sums (App. C.1):
+    // sum_i w2 r' z' X = c sum_i (w2 r') z' x and sum_i w2 r'^2 z'^2.
+    float num[8], den[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        num[e] = 0.0f;
+        den[e] = 0.0f;
+    }
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
         const int p = g + C8 * m;
@@ -242,6 +254,15 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             bits[e] = __float_as_uint(__builtin_fmaf(z[m][e], inv[m], kRoundMagic));
+        if (REFIT) {
+            const float wr = s_w2[ul][p] * rnv[m];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float zq = __uint_as_float(bits[e]) - kRoundMagic; // the code, exactly
+                num[e] = __builtin_fmaf(wr * zq, z[m][e], num[e]);
+                den[e] = __builtin_fmaf((wr * rnv[m]) * zq, zq, den[e]);
+            }
+        }
         if (!live) continue;
         if (p < n8) {
             uint2 t;
@@ -253,6 +274,27 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) t |= (bits[e] & 0xFu) << (4 * e);
             *reinterpret_cast<uint32_t *>(q4 + static_cast<size_t>(p - n8) * (D / 2) + 4 * c) = t;
+        }
+    }
+    if (REFIT) {
+        // Table C2 step 5: refit the column factors to the new codes.
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            s_red[ul][0][g][8 * c + e] = num[e];
+            s_red[ul][1][g][8 * c + e] = den[e];
+        }
+        __syncthreads();
+        if (live) {
+            for (int j = lt; j < D; j += TPU) {
+                float ns = 0.0f, ds = 0.0f;
+#pragma unroll
+                for (int gg = 0; gg < C8; ++gg) {
+                    ns += s_red[ul][0][gg][j];
+                    ds += s_red[ul][1][gg][j];
+                }
+                const float cold = s_c[ul][j];
+                a.cs_out[ubase * D + j] = ds > 0.0f ? fmaxf(cold * (ns / ds), kRowFloor) : cold;
+            }
         }
     }
 }
@@ -380,10 +422,15 @@ template <int D>
 hipError_t launch_mixed_d(bool bf16, const DecodeArgs &a, hipStream_t s) {
     const long units = static_cast<long>(a.B) * a.Hv;
     const unsigned grid = static_cast<unsigned>((units + Geo<D>::UPW - 1) / Geo<D>::UPW);
-    if (bf16)
-        hipLaunchKernelGGL((decode_mixed_kernel<D, uint16_t>), dim3(grid), dim3(256), 0, s, a);
+    const bool refit = a.cs != nullptr;
+    if (bf16 && refit)
+        hipLaunchKernelGGL((decode_mixed_kernel<D, uint16_t, true>), dim3(grid), dim3(256), 0, s, a);
+    else if (bf16)
+        hipLaunchKernelGGL((decode_mixed_kernel<D, uint16_t, false>), dim3(grid), dim3(256), 0, s, a);
+    else if (refit)
+        hipLaunchKernelGGL((decode_mixed_kernel<D, float, true>), dim3(grid), dim3(256), 0, s, a);
     else
-        hipLaunchKernelGGL((decode_mixed_kernel<D, float>), dim3(grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((decode_mixed_kernel<D, float, false>), dim3(grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

@@ -347,8 +347,6 @@ stq_status decode(const stq_state *src, const stq_state *dst, const int32_t *slo
         return STQ_E_ARG;
     if (calibrated_format(src->desc.fmt) && !src->calibrated) return STQ_E_STATE;
     const bool refit = src->desc.fmt == STQ_FMT_REFIT;
-    if (refit && !(src->desc.d_k == 128 && stq::decode128_supported(src->desc.n8)))
-        return STQ_E_UNSUPPORTED;
     Layout L;
     describe(&src->desc, &L);
     if (partial_overlap(src->pool8, dst->pool8, L.pool8) || partial_overlap(src->pool4, dst->pool4, L.pool4) ||
