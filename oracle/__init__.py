@@ -74,10 +74,16 @@ def _bind(path: Path):
     lib.oracle_step_refit.argtypes = [I, I, I, I, I, I] + [P] * 17 + [I]
     lib.oracle_impact_accumulate.argtypes = [I, I, I, I, P, P, P, P, P]
     lib.oracle_impact_weights.argtypes = [I, I, P, P]
+    lib.oracle_step_gated.argtypes = [I, I, I, I, I, I] + [P] * 15 + [I]
+    lib.oracle_fp_step_gated.argtypes = [I, I, I, I, I] + [P] * 7 + [I]
+    lib.oracle_step_refit_gated.argtypes = [I, I, I, I, I, I] + [P] * 17 + [I]
+    lib.oracle_impact_accumulate_gated.argtypes = [I, I, I, I, P, P, P, P, P]
     for name in ("oracle_dequant", "oracle_pack", "oracle_step", "oracle_fp_step",
                  "oracle_calib_cols", "oracle_calib_rows", "oracle_calib_finalize",
                  "oracle_dequant_cs", "oracle_pack_refit", "oracle_step_refit",
-                 "oracle_impact_accumulate", "oracle_impact_weights"):
+                 "oracle_impact_accumulate", "oracle_impact_weights", "oracle_step_gated",
+                 "oracle_fp_step_gated", "oracle_step_refit_gated",
+                 "oracle_impact_accumulate_gated"):
         getattr(lib, name).restype = I
     return lib
 
@@ -158,12 +164,14 @@ class Oracle:
         return pool8, pool4, r
 
     def step(self, pool8, pool4, r, c, perm, q, k, v, alpha, beta, *, n8: int,
-             want_X: bool = False, nthreads: int = 1):
+             want_X: bool = False, nthreads: int = 1, gate=None):
         """One quantized decode step (Table C2; Sec. 2.1 Eq. (1) with D = alpha I).
 
         q, k [B][Hk][dk], v [B][Hv][dv], alpha, beta [B][Hv] (fp32 values; bf16
         inputs are passed widened).  Returns dict with pool8, pool4, r, o and,
-        if want_X, the pre-requantization state X [B][Hv][dk][dv] (f64)."""
+        if want_X, the pre-requantization state X [B][Hv][dk][dv] (f64).  With
+        gate [B][Hv][dk] (logical rows) the diagonal gate D = diag(gate) of the
+        KDA form replaces alpha."""
         r = _c(r, np.float32)
         B, hv, dk = r.shape
         c = _c(c, np.float32)
@@ -172,10 +180,15 @@ class Oracle:
         hk = q.shape[1]
         k = _c(k, np.float32)
         v = _c(v, np.float32)
-        alpha = _c(alpha, np.float32)
         beta = _c(beta, np.float32)
+        if gate is not None:
+            g_or_a = _c(gate, np.float32)
+            assert g_or_a.shape == (B, hv, dk)
+        else:
+            g_or_a = _c(alpha, np.float32)
+            assert g_or_a.shape == (B, hv)
         assert q.shape == (B, hk, dk) and k.shape == (B, hk, dk)
-        assert v.shape == (B, hv, dv) and alpha.shape == (B, hv) and beta.shape == (B, hv)
+        assert v.shape == (B, hv, dv) and beta.shape == (B, hv)
         pool8 = _c(pool8, np.int8).reshape(B, hv, n8, dv)
         pool4 = _c(pool4, np.uint8).reshape(B, hv, dk - n8, dv // 2)
         perm = _c(perm, np.int32)
@@ -186,9 +199,10 @@ class Oracle:
             "o": np.empty((B, hv, dv), np.float32),
         }
         X = np.empty((B, hv, dk, dv), np.float64) if want_X else None
-        rc = self.lib().oracle_step(B, hv, hk, dk, dv, n8, _ptr(pool8), _ptr(pool4), _ptr(r),
+        fn = self.lib().oracle_step_gated if gate is not None else self.lib().oracle_step
+        rc = fn(B, hv, hk, dk, dv, n8, _ptr(pool8), _ptr(pool4), _ptr(r),
                                  _ptr(c), _ptr(perm), _ptr(q), _ptr(k), _ptr(v),
-                                 _ptr(alpha), _ptr(beta), _ptr(out["pool8"]),
+                                 _ptr(g_or_a), _ptr(beta), _ptr(out["pool8"]),
                                  _ptr(out["pool4"]), _ptr(out["r"]), _ptr(out["o"]),
                                  _ptr(X), nthreads)
         assert rc == 0
@@ -196,7 +210,7 @@ class Oracle:
             out["X"] = X
         return out
 
-    def fp_step(self, S, q, k, v, alpha, beta, *, nthreads: int = 1):
+    def fp_step(self, S, q, k, v, alpha, beta, *, nthreads: int = 1, gate=None):
         """Unquantized gated delta-rule step (Sec. 2.1 Eq. (1), D = alpha I).
 
         S [B][Hv][dk][dv] f64 is updated IN PLACE; returns o [B][Hv][dv] f64."""
@@ -206,11 +220,12 @@ class Oracle:
         hk = q.shape[1]
         k = _c(k, np.float32)
         v = _c(v, np.float32)
-        alpha = _c(alpha, np.float32)
+        g_or_a = _c(gate if gate is not None else alpha, np.float32)
         beta = _c(beta, np.float32)
         o = np.empty((B, hv, dv), np.float64)
-        rc = self.lib().oracle_fp_step(B, hv, hk, dk, dv, _ptr(S), _ptr(q), _ptr(k), _ptr(v),
-                                    _ptr(alpha), _ptr(beta), _ptr(o), nthreads)
+        fn = self.lib().oracle_fp_step_gated if gate is not None else self.lib().oracle_fp_step
+        rc = fn(B, hv, hk, dk, dv, _ptr(S), _ptr(q), _ptr(k), _ptr(v),
+                _ptr(g_or_a), _ptr(beta), _ptr(o), nthreads)
         assert rc == 0
         return o
 
@@ -280,7 +295,7 @@ class Oracle:
         return pool8, pool4, r, cs
 
     def step_refit(self, pool8, pool4, r, cs, perm, w2, q, k, v, alpha, beta, *, n8: int,
-                   want_X: bool = False, nthreads: int = 1):
+                   want_X: bool = False, nthreads: int = 1, gate=None):
         """One decode step with per-state column factors and the online column
         refit (Table C2 steps 1-6).  Returns dict pool8, pool4, r, cs, o (and X)."""
         r = _c(r, np.float32)
@@ -291,7 +306,7 @@ class Oracle:
         hk = q.shape[1]
         k = _c(k, np.float32)
         v = _c(v, np.float32)
-        alpha = _c(alpha, np.float32)
+        g_or_a = _c(gate if gate is not None else alpha, np.float32)
         beta = _c(beta, np.float32)
         pool8 = _c(pool8, np.int8).reshape(B, hv, n8, dv)
         pool4 = _c(pool4, np.uint8).reshape(B, hv, dk - n8, dv // 2)
@@ -301,9 +316,10 @@ class Oracle:
                "r": np.empty_like(r), "cs": np.empty_like(cs),
                "o": np.empty((B, hv, dv), np.float32)}
         X = np.empty((B, hv, dk, dv), np.float64) if want_X else None
-        rc = self.lib().oracle_step_refit(
+        fn = self.lib().oracle_step_refit_gated if gate is not None else self.lib().oracle_step_refit
+        rc = fn(
             B, hv, hk, dk, dv, n8, _ptr(pool8), _ptr(pool4), _ptr(r), _ptr(cs), _ptr(perm),
-            _ptr(w2), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(out["pool8"]),
+            _ptr(w2), _ptr(q), _ptr(k), _ptr(v), _ptr(g_or_a), _ptr(beta), _ptr(out["pool8"]),
             _ptr(out["pool4"]), _ptr(out["r"]), _ptr(out["cs"]), _ptr(out["o"]), _ptr(X),
             nthreads)
         assert rc == 0
@@ -311,17 +327,18 @@ class Oracle:
             out["X"] = X
         return out
 
-    def impact_accumulate(self, q, k, alpha, beta, omega, *, hv: int):
+    def impact_accumulate(self, q, k, alpha, beta, omega, *, hv: int, gate=None):
         """omega[h][i] += sum over the batch of (alpha (q_i - beta k_i k.q))^2
         (Sec. 4.1 row impact with the scalar gate; App. C.1).  omega [Hv][dk] f64."""
         q = _c(q, np.float32)
         B, hk, dk = q.shape
         k = _c(k, np.float32)
-        alpha = _c(alpha, np.float32)
+        g_or_a = _c(gate if gate is not None else alpha, np.float32)
         beta = _c(beta, np.float32)
         assert omega.dtype == np.float64 and omega.shape == (hv, dk)
-        assert self.lib().oracle_impact_accumulate(B, hv, hk, dk, _ptr(q), _ptr(k), _ptr(alpha),
-                                                   _ptr(beta), _ptr(omega)) == 0
+        fn = (self.lib().oracle_impact_accumulate_gated if gate is not None
+              else self.lib().oracle_impact_accumulate)
+        assert fn(B, hv, hk, dk, _ptr(q), _ptr(k), _ptr(g_or_a), _ptr(beta), _ptr(omega)) == 0
 
     def impact_weights(self, omega):
         """Squared row-impact weights w2 = (omega / mean omega)^(1/4) per head

@@ -35,6 +35,8 @@
  *       C2 step 5) over all rows of the head, weights w2 = w^2; the new factor
  *       is rounded to fp32 and floored at 2^-126, a zero denominator keeps the
  *       old one.  The stored codes are those taken against the old factors.
+ *   R16 the diagonal gate (KDA form) is one fp32 value per (sequence, value
+ *       head, logical key row); it scales row i of the previous state.
  *   R15 row-impact weights: omega_i = sum over calibration samples of
  *       (alpha (q_i - beta k_i k.q))^2 (Sec. 4.1 with the scalar gate), and
  *       w2_i = (omega_i / mean omega)^(1/4) (App. B.3: w ~ omega^(1/8)),
@@ -151,6 +153,46 @@ static void unit_delta_step(int dk, int dv, double *S, const double *q,
         o[j] = acc;
     }
     free(u);
+}
+
+/* The same step with a diagonal gate D_t = diag(d) over the key rows (Sec. 2.1
+ * Eq. (1) with a per-channel gate, the KDA form named in Sec. 6.1 and App.
+ * C.1), d in logical row order:
+ *   u = (D S)^T k;  S <- D S + beta * k (v - u)^T;  o = S^T q            */
+static void unit_delta_step_diag(int dk, int dv, double *S, const double *q,
+                                 const double *k, const double *v,
+                                 const double *d, double beta, double *o) {
+    double *u = (double *)calloc((size_t)dv, sizeof(double));
+    for (int j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < dk; ++i) acc += d[i] * S[(size_t)i * dv + j] * k[i];
+        u[j] = acc;
+    }
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j) {
+            double *x = &S[(size_t)i * dv + j];
+            *x = d[i] * (*x) + beta * k[i] * (v[j] - u[j]);
+        }
+    for (int j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < dk; ++i) acc += S[(size_t)i * dv + j] * q[i];
+        o[j] = acc;
+    }
+    free(u);
+}
+
+/* Either gate: the scalar alpha of unit u, or the row gate gate[u][dk]. */
+static void unit_update(int dk, int dv, double *S, const double *q, const double *k,
+                        const double *v, const float *alpha, const float *gate, long u,
+                        double beta, double *o) {
+    if (!gate) {
+        unit_delta_step(dk, dv, S, q, k, v, (double)alpha[u], beta, o);
+        return;
+    }
+    double *d = (double *)calloc((size_t)dk, sizeof(double));
+    for (int i = 0; i < dk; ++i) d[i] = (double)gate[(size_t)u * dk + i];
+    unit_delta_step_diag(dk, dv, S, q, k, v, d, beta, o);
+    free(d);
 }
 
 /* Requantize a logical-order double matrix X into one head's packed rows
@@ -333,6 +375,7 @@ typedef struct {
     uint8_t *pool4_out;
     float *r_out, *o;
     double *X_out;
+    const float *gate; /* [B][Hv][dk] row gate, or NULL for the scalar alpha */
 } step_ctx;
 
 static void step_unit(void *vctx, long u) {
@@ -360,8 +403,7 @@ static void step_unit(void *vctx, long u) {
     for (int j = 0; j < s->dv; ++j) v[j] = (double)x->v[(size_t)u * s->dv + j];
     /* Table C2 steps 2-3: update, then emit the readout of the updated state
      * before it is requantized. */
-    unit_delta_step(s->dk, s->dv, S, q, k, v, (double)x->alpha[u],
-                    (double)x->beta[u], o);
+    unit_update(s->dk, s->dv, S, q, k, v, x->alpha, x->gate, u, (double)x->beta[u], o);
     for (int j = 0; j < s->dv; ++j) x->o[(size_t)u * s->dv + j] = (float)o[j];
     if (x->X_out) memcpy(x->X_out + (size_t)u * n, S, n * sizeof(double));
     /* Table C2 steps 4 and 6: row factors, codes, pack. */
@@ -386,8 +428,23 @@ int oracle_step(int B, int hv, int hk, int dk, int dv, int n8,
                 const float *beta, int8_t *pool8_out, uint8_t *pool4_out,
                 float *r_out, float *o, double *X_out, int nthreads) {
     step_ctx x = {{hv, hk, dk, dv, n8}, pool8, pool4, r, c, perm, q, k, v,
-                  alpha, beta, pool8_out, pool4_out, r_out, o, X_out};
+                  alpha, beta, pool8_out, pool4_out, r_out, o, X_out, NULL};
     if (check_shape(&x.s)) return -1;
+    for_units((long)B * hv, nthreads, step_unit, &x);
+    return 0;
+}
+
+/* oracle_step with the row gate gate[B][Hv][dk] (logical rows) in place of
+ * the scalar alpha (Eq. (1) with a diagonal D_t). */
+int oracle_step_gated(int B, int hv, int hk, int dk, int dv, int n8,
+                      const int8_t *pool8, const uint8_t *pool4, const float *r,
+                      const float *c, const int32_t *perm, const float *q,
+                      const float *k, const float *v, const float *gate,
+                      const float *beta, int8_t *pool8_out, uint8_t *pool4_out,
+                      float *r_out, float *o, double *X_out, int nthreads) {
+    step_ctx x = {{hv, hk, dk, dv, n8}, pool8, pool4, r, c, perm, q, k, v,
+                  NULL, beta, pool8_out, pool4_out, r_out, o, X_out, gate};
+    if (check_shape(&x.s) || !gate) return -1;
     for_units((long)B * hv, nthreads, step_unit, &x);
     return 0;
 }
@@ -397,6 +454,7 @@ typedef struct {
     double *S;
     const float *q, *k, *v, *alpha, *beta;
     double *o;
+    const float *gate;
 } fp_ctx;
 
 static void fp_unit(void *vctx, long u) {
@@ -413,9 +471,8 @@ static void fp_unit(void *vctx, long u) {
         k[i] = (double)x->k[((size_t)b * s->hk + hk) * s->dk + i];
     }
     for (int j = 0; j < s->dv; ++j) v[j] = (double)x->v[(size_t)u * s->dv + j];
-    unit_delta_step(s->dk, s->dv, x->S + (size_t)u * s->dk * s->dv, q, k, v,
-                    (double)x->alpha[u], (double)x->beta[u],
-                    x->o + (size_t)u * s->dv);
+    unit_update(s->dk, s->dv, x->S + (size_t)u * s->dk * s->dv, q, k, v, x->alpha, x->gate,
+                u, (double)x->beta[u], x->o + (size_t)u * s->dv);
     free(q);
     free(k);
     free(v);
@@ -428,8 +485,19 @@ int oracle_fp_step(int B, int hv, int hk, int dk, int dv, double *S,
                    const float *q, const float *k, const float *v,
                    const float *alpha, const float *beta, double *o,
                    int nthreads) {
-    fp_ctx x = {{hv, hk, dk, dv, 0}, S, q, k, v, alpha, beta, o};
+    fp_ctx x = {{hv, hk, dk, dv, 0}, S, q, k, v, alpha, beta, o, NULL};
     if (check_shape(&x.s)) return -1;
+    for_units((long)B * hv, nthreads, fp_unit, &x);
+    return 0;
+}
+
+/* oracle_fp_step with the row gate gate[B][Hv][dk] (logical rows). */
+int oracle_fp_step_gated(int B, int hv, int hk, int dk, int dv, double *S,
+                         const float *q, const float *k, const float *v,
+                         const float *gate, const float *beta, double *o,
+                         int nthreads) {
+    fp_ctx x = {{hv, hk, dk, dv, 0}, S, q, k, v, NULL, beta, o, gate};
+    if (check_shape(&x.s) || !gate) return -1;
     for_units((long)B * hv, nthreads, fp_unit, &x);
     return 0;
 }
@@ -521,6 +589,7 @@ typedef struct {
     uint8_t *pool4_out;
     float *r_out, *cs_out, *o;
     double *X_out;
+    const float *gate;
 } step_refit_ctx;
 
 static void step_refit_unit(void *vctx, long u) {
@@ -548,8 +617,7 @@ static void step_refit_unit(void *vctx, long u) {
     }
     for (int j = 0; j < s->dv; ++j) v[j] = (double)x->v[(size_t)u * s->dv + j];
     /* Table C2 steps 2-3. */
-    unit_delta_step(s->dk, s->dv, S, q, k, v, (double)x->alpha[u],
-                    (double)x->beta[u], o);
+    unit_update(s->dk, s->dv, S, q, k, v, x->alpha, x->gate, u, (double)x->beta[u], o);
     for (int j = 0; j < s->dv; ++j) x->o[(size_t)u * s->dv + j] = (float)o[j];
     if (x->X_out) memcpy(x->X_out + (size_t)u * n, S, n * sizeof(double));
     /* Table C2 step 4: row factors and codes against the current column
@@ -577,8 +645,23 @@ int oracle_step_refit(int B, int hv, int hk, int dk, int dv, int n8,
                       uint8_t *pool4_out, float *r_out, float *cs_out, float *o,
                       double *X_out, int nthreads) {
     step_refit_ctx x = {{hv, hk, dk, dv, n8}, pool8, pool4, r, cs, perm, w2, q, k, v,
-                        alpha, beta, pool8_out, pool4_out, r_out, cs_out, o, X_out};
+                        alpha, beta, pool8_out, pool4_out, r_out, cs_out, o, X_out, NULL};
     if (check_shape(&x.s)) return -1;
+    for_units((long)B * hv, nthreads, step_refit_unit, &x);
+    return 0;
+}
+
+/* oracle_step_refit with the row gate gate[B][Hv][dk] (logical rows). */
+int oracle_step_refit_gated(int B, int hv, int hk, int dk, int dv, int n8,
+                            const int8_t *pool8, const uint8_t *pool4, const float *r,
+                            const float *cs, const int32_t *perm, const float *w2,
+                            const float *q, const float *k, const float *v,
+                            const float *gate, const float *beta, int8_t *pool8_out,
+                            uint8_t *pool4_out, float *r_out, float *cs_out, float *o,
+                            double *X_out, int nthreads) {
+    step_refit_ctx x = {{hv, hk, dk, dv, n8}, pool8, pool4, r, cs, perm, w2, q, k, v,
+                        NULL, beta, pool8_out, pool4_out, r_out, cs_out, o, X_out, gate};
+    if (check_shape(&x.s) || !gate) return -1;
     for_units((long)B * hv, nthreads, step_refit_unit, &x);
     return 0;
 }
@@ -588,8 +671,8 @@ int oracle_step_refit(int B, int hv, int hk, int dk, int dv, int n8,
  * carried by g_i = (A_t^T q_t)_i = alpha (q_i - beta k_i (k.q)), and
  * omega_i = E[g_i^2] over calibration samples.  omega[Hv][dk] (logical rows)
  * accumulates sum over the B samples of g_i^2 for every value head. */
-int oracle_impact_accumulate(int B, int hv, int hk, int dk, const float *q,
-                             const float *k, const float *alpha,
+static int impact_accumulate(int B, int hv, int hk, int dk, const float *q,
+                             const float *k, const float *alpha, const float *gate,
                              const float *beta, double *omega) {
     if (hv <= 0 || hk <= 0 || hv % hk != 0 || dk <= 0) return -1;
     for (long b = 0; b < B; ++b)
@@ -599,14 +682,30 @@ int oracle_impact_accumulate(int B, int hv, int hk, int dk, const float *q,
             const float *kk = k + ((size_t)b * hk + g) * dk;
             double kq = 0.0;
             for (int i = 0; i < dk; ++i) kq += (double)kk[i] * (double)qq[i];
-            double a = (double)alpha[(size_t)b * hv + h];
             double be = (double)beta[(size_t)b * hv + h];
             for (int i = 0; i < dk; ++i) {
+                double a = gate ? (double)gate[((size_t)b * hv + h) * dk + i]
+                                : (double)alpha[(size_t)b * hv + h];
                 double gi = a * ((double)qq[i] - be * (double)kk[i] * kq);
                 omega[(size_t)h * dk + i] += gi * gi;
             }
         }
     return 0;
+}
+
+int oracle_impact_accumulate(int B, int hv, int hk, int dk, const float *q,
+                             const float *k, const float *alpha,
+                             const float *beta, double *omega) {
+    return impact_accumulate(B, hv, hk, dk, q, k, alpha, NULL, beta, omega);
+}
+
+/* The same with the row gate (App. C.1: g_i = d_i (q_i - beta k_i k.q)),
+ * gate[B][Hv][dk] in logical row order. */
+int oracle_impact_accumulate_gated(int B, int hv, int hk, int dk, const float *q,
+                                   const float *k, const float *gate,
+                                   const float *beta, double *omega) {
+    if (!gate) return -1;
+    return impact_accumulate(B, hv, hk, dk, q, k, NULL, gate, beta, omega);
 }
 
 /* Squared row-impact weights from the accumulated omega (App. B.3: the row

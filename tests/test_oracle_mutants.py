@@ -12,6 +12,7 @@ import pytest
 
 import oracle as oracle_pkg
 from tests import test_oracle_pins as pins
+from tests import test_oracle_gate_pins as gpins
 from tests import test_oracle_refit_pins as rpins
 
 SRC = Path(oracle_pkg.__file__).resolve().parent / "stq_oracle.c"
@@ -59,6 +60,14 @@ MUTANTS = [
      "double gi = a * ((double)qq[i] - (double)kk[i] * kq);"),
     ("impact without the gate", "double gi = a * ((double)qq[i] - be * (double)kk[i] * kq);",
      "double gi = ((double)qq[i] - be * (double)kk[i] * kq);"),
+    ("row gate dropped on S^T k", "acc += d[i] * S[(size_t)i * dv + j] * k[i];",
+     "acc += S[(size_t)i * dv + j] * k[i];"),
+    ("row gate dropped on S", "*x = d[i] * (*x) + ", "*x = (*x) + "),
+    ("row gate applied by column", "*x = d[i] * (*x) + ", "*x = d[j] * (*x) + "),
+    ("row gate read in reversed row order", "d[i] = (double)gate[(size_t)u * dk + i];",
+     "d[i] = (double)gate[(size_t)u * dk + (dk - 1 - i)];"),
+    ("impact row gate from row 0", "double a = gate ? (double)gate[((size_t)b * hv + h) * dk + i]",
+     "double a = gate ? (double)gate[((size_t)b * hv + h) * dk + 0]"),
     ("impact weight exponent 1/8", "pow(omega[(size_t)h * dk + i] / mean, 0.25)",
      "pow(omega[(size_t)h * dk + i] / mean, 0.125)"),
 ]
@@ -89,6 +98,12 @@ def _pin_cases():
         (rpins.test_refit_step_fixed_point, {"d": 16, "n8": 8}),
         (rpins.test_impact_closed_form_unit_vectors, {}),
         (rpins.test_impact_weights_fourth_root_of_normalised_impact, {}),
+        (gpins.test_uniform_gate_is_the_scalar_gate, {"d": 16, "n8": 8}),
+        (gpins.test_one_hot_gate_keeps_one_logical_row, {}),
+        (gpins.test_gated_delta_write_closed_form, {"d": 16, "n8": 16}),
+        (gpins.test_gated_fp_step_one_hot, {}),
+        (gpins.test_gated_impact_closed_form, {}),
+        (gpins.test_gated_refit_uniform_gate_is_scalar, {}),
     ]
 
 
