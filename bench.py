@@ -85,11 +85,14 @@ def unit_state_bytes(fmt: str, d: int, n8: int) -> int:
     return n8 * d + (d - n8) * d // 2 + 4 * d
 
 
-def algorithmic_bytes(fmt: str, B: int, hv: int, hk: int, d: int, n8: int, in_el: int) -> int:
+def algorithmic_bytes(fmt: str, B: int, hv: int, hk: int, d: int, n8: int, in_el: int,
+                      gated: bool = False) -> int:
     """Bytes one decode launch must move: read + write of every state, q and k
-    once per key head, v, alpha, beta once per value head, o written once."""
+    once per key head, v, alpha (or the fp32 row gate), beta once per value
+    head, o written once."""
     state = 2 * unit_state_bytes(fmt, d, n8) * B * hv
-    vecs = B * hk * 2 * d * in_el + B * hv * (d * in_el + 8 + 4 * d)
+    gate = 4 * d if gated else 4
+    vecs = B * hk * 2 * d * in_el + B * hv * (d * in_el + gate + 4 + 4 * d)
     return state + vecs
 
 
@@ -178,10 +181,15 @@ def main():
         torch.cuda.synchronize()
         return pools
 
+    gates = None
+
     def launch(pools, t, into):
         q, k, v, a, b = window[t % len(window)]
         src = pools[t % len(pools)]
-        if into:
+        if gates is not None:
+            dst = pools[(t + 1) % len(pools)] if into else None
+            src.decode_step_gated(q, k, v, gates[t % len(gates)], b, o=o, dst=dst)
+        elif into:
             src.decode_step_into(pools[(t + 1) % len(pools)], q, k, v, a, b, o=o)
         else:
             src.decode_step(q, k, v, a, b, o=o)
@@ -204,10 +212,15 @@ def main():
         return total_ms, total_ms / steps
 
     def measure(fmt_name: str, fmt: int, n8: int, npools: int, steps: int, warmup: int,
-                into: bool = False):
+                into: bool = False, gated: bool = False):
+        nonlocal gates
         pools = make_pools(fmt, n8, npools)
+        if gated:  # per-key-row gates of the KDA form, one per window step
+            gates = [dev(wl.draw_gate(B, hv, d, seed=w.seed, step=t))
+                     for t in range(len(window))]
         total_ms, mean_ms = time_decode(pools, steps, warmup, into)
-        nbytes = algorithmic_bytes(fmt_name, B, hv, hk, d, n8, in_el)
+        gates = None
+        nbytes = algorithmic_bytes(fmt_name, B, hv, hk, d, n8, in_el, gated)
         res = dict(updates_per_s=B * hv * steps / (total_ms / 1e3), ms_per_step=total_ms / steps,
                    kernel_ms_mean=mean_ms,
                    algorithmic_bytes_per_launch=nbytes,
@@ -242,6 +255,8 @@ def main():
         if d == 128 and w.n8 % 16 == 0:
             variants["refit_column_factors"] = measure("refit", stq.FMT_REFIT, w.n8, args.pools,
                                                        args.steps, args.warmup)
+        variants["row_gate_kda"] = measure("mixed", stq.FMT_MIXED48, w.n8, args.pools, args.steps,
+                                           args.warmup, gated=True)
         variants["fp32_state"] = measure("fp32", stq.FMT_FP32, 0, 2, args.steps, args.warmup)
         for k_, v_ in variants.items():
             log(f"[bench] {k_}: {v_['updates_per_s'] / 1e6:.1f} M updates/s, "

@@ -13,7 +13,10 @@
  *     c_j fixed offline (Sec. 3.2 / Sec. 4.4: the precision map is calibrated
  *     offline and fixed across requests);
  *   - in the order of App. C.3 Table C2: reconstruct, update, emit the readout
- *     before requantization, derive row factors, pack and write back.
+ *     before requantization, derive row factors, pack and write back;
+ *   - and the same step with a per-key-row (diagonal) gate, Eq. (1) with
+ *     D_t = diag(d) (the KDA form, Sec. 6.1 and App. C.1):
+ *       X = D S + b k (v - (D S)^T k)^T,    o = X^T q.
  * Quantizer (Sec. 2.2): z = clip(round(x / s), -q_b, q_b), q_b = 2^(b-1) - 1,
  * with round = round-half-to-even; row factor r_i = max(fl32(max_j |X_ij / c_j|
  * / q_b), 2^-126); the code of X_ij is taken against the stored r_i.
@@ -181,6 +184,15 @@ stq_status stq_calibrate_impact(stq_state *st, const void *q, const void *k,
                                 int32_t dtype, const float *alpha, const float *beta,
                                 int32_t B, uint32_t flags, stq_stream_t stream);
 
+/* Row-impact calibration with a per-key-row gate (App. C.1: g_i = d_i (q_i -
+ * beta k_i (k.q))): as stq_calibrate_impact with alpha replaced by
+ * gate [B][Hv][dk] fp32 in logical key-row order,
+ *   impact[h][i] += sum_b (gate[b][h][i] (q_i - beta k_i (k.q)))^2.
+ * Errors: as stq_calibrate_impact; STQ_E_ARG for a null gate with B > 0. */
+stq_status stq_calibrate_impact_gated(stq_state *st, const void *q, const void *k,
+                                      int32_t dtype, const float *gate, const float *beta,
+                                      int32_t B, uint32_t flags, stq_stream_t stream);
+
 /* Install a calibration computed elsewhere: copies c [Hv][dv] (each > 0) and
  * perm [Hv][dk] (a permutation of 0..dk-1 per head) from device memory and
  * marks the state calibrated.  Like FINALIZE it invalidates packed contents.
@@ -235,6 +247,22 @@ stq_status stq_decode_step_into(const stq_state *src, const stq_state *dst,
                                 const float *alpha, const float *beta, float *o,
                                 stq_stream_t stream);
 
+/* The decode step with a per-key-row gate (Sec. 2.1 Eq. (1) with
+ * D_t = diag(d), the KDA form of Sec. 6.1), reading slots[b] of `src` and
+ * writing `dst` as stq_decode_step_into (dst == src: in place):
+ *   S_hat = r c z;  u = (D S_hat)^T k;  X = D S_hat + b k (v - u)^T;  o = X^T q
+ * then r', z' (and for REFIT the column refit) exactly as stq_decode_step.
+ * gate is fp32 [B][Hv][dk]: gate[b][h][i] multiplies LOGICAL key row i of
+ * value head h (the row the caller's q and k index, not the physical row).
+ * A uniform gate d = a 1 gives the scalar-gate step.  Every format is
+ * supported.
+ * Errors: as stq_decode_step_into; STQ_E_ARG for a null or misaligned gate. */
+stq_status stq_decode_step_gated(const stq_state *src, const stq_state *dst,
+                                 const int32_t *slots, int32_t B, const void *q,
+                                 const void *k, const void *v, int32_t dtype,
+                                 const float *gate, const float *beta, float *o,
+                                 stq_stream_t stream);
+
 /* Reconstruct S_ij = r_i c_j z_ij (Sec. 4.3) of slots[b] into fp32
  * S_out [B][Hv][dk][dv] in logical row order (FP32 format: copies the state;
  * REFIT: c is the state's own cs).
@@ -252,7 +280,8 @@ stq_status stq_stream_copy(const void *src, void *dst, size_t bytes, stq_stream_
 const char *stq_status_str(int32_t status);
 
 /* Library ABI version (bumped on any change to the declarations above):
- * 2 since the REFIT format and its state fields. */
+ * 2 since the REFIT format and its state fields; 3 since the per-key-row
+ * gate entry points. */
 int32_t stq_abi_version(void);
 
 #ifdef __cplusplus

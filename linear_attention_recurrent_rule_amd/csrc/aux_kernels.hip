@@ -390,7 +390,9 @@ __global__ __launch_bounds__(128) void impact_accumulate_kernel(ImpactArgs a) {
         const double qi = i < D ? static_cast<double>(load_in<TIn>(a.q, base + i)) : 0.0;
         const double ki = i < D ? static_cast<double>(load_in<TIn>(a.k, base + i)) : 0.0;
         const double kq = block_sum128(ki * qi, tmp);
-        const double al = a.alpha[static_cast<size_t>(b) * a.Hv + h];
+        // scalar gate, or the row gate d_i of the KDA form (App. C.1: g_i = d_i (q_i - b k_i k.q))
+        const double al = a.gate ? (i < D ? static_cast<double>(a.gate[(static_cast<size_t>(b) * a.Hv + h) * D + i]) : 0.0)
+                                 : static_cast<double>(a.alpha[static_cast<size_t>(b) * a.Hv + h]);
         const double be = a.beta[static_cast<size_t>(b) * a.Hv + h];
         const double g = al * (qi - be * ki * kq);
         acc += g * g;

@@ -80,6 +80,7 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
     __shared__ float s_red[UPW][2][C8][D];
     __shared__ float s_kq[UPW][C8];
     __shared__ float s_w2[REFIT ? UPW : 1][D]; // squared row-impact weights, physical rows
+    __shared__ float s_g[UPW][D];      // row gate in physical row order (1 for a scalar gate)
 
     const int lt = threadIdx.x % TPU;
     const int ul = threadIdx.x / TPU;
@@ -124,12 +125,13 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
     }
     // Stage q, k (permuted to physical row order), v and c in LDS.
     for (int idx = lt; idx < D; idx += TPU) {
-        float kv = 0.0f, qv = 0.0f, vv = 0.0f, cv = 1.0f, wv = 0.0f;
+        float kv = 0.0f, qv = 0.0f, vv = 0.0f, cv = 1.0f, wv = 0.0f, gv = 1.0f;
         if (live) {
             const int i = a.perm[static_cast<size_t>(h) * D + idx] & (D - 1);
             const size_t kb = (static_cast<size_t>(b) * a.Hk + hk) * D;
             kv = In<TIn>::get(a.k, kb + i);
             qv = In<TIn>::get(a.q, kb + i);
+            if (a.gate) gv = a.gate[static_cast<size_t>(unit) * D + i];
             vv = In<TIn>::get(a.v, (static_cast<size_t>(b) * a.Hv + h) * D + idx);
             cv = REFIT ? a.cs[ubase * D + idx] : a.c[static_cast<size_t>(h) * D + idx];
             if (REFIT) wv = a.w2[static_cast<size_t>(h) * D + i];
@@ -138,6 +140,7 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
         s_q[ul][idx] = qv;
         s_v[ul][idx] = vv;
         s_c[ul][idx] = cv;
+        s_g[ul][idx] = gv;
         if (REFIT) s_w2[ul][idx] = wv;
     }
     __syncthreads();
@@ -174,6 +177,8 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
             }
             scale = rrow[m] * 0.0625f;
         }
+        // a row gate d_i scales the whole reconstructed row (D S has rows d_i r_i z_i)
+        scale *= s_g[ul][p];
         rrow[m] = scale; // from here on: factor applied to the widened code
         const float rk = scale * kp;
         const float rq = scale * qp;
@@ -193,7 +198,8 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
     __syncthreads();
 
     // Column phase: finish u~, w~ and k.q; emit o (Table C2 step 3) and e.
-    const float alpha = active ? a.alpha[unit] : 0.0f;
+    // With a row gate the gate is already in the row factors: scalar gate 1.
+    const float alpha = !active ? 0.0f : (a.gate ? 1.0f : a.alpha[unit]);
     const float beta = active ? a.beta[unit] : 0.0f;
     for (int j = lt; j < D; j += TPU) {
         float u = 0.0f, w = 0.0f, kq = 0.0f;
@@ -300,7 +306,7 @@ __global__ __launch_bounds__(256) void decode_mixed_kernel(DecodeArgs a) {
 }
 
 // Unquantized comparison path: the same step on an fp32 state (Eq. (1) with
-// D_t = a I), read and written once.
+// D_t = a I, or D_t = diag(d) over the key rows), read and written once.
 template <int D, typename TIn>
 __global__ __launch_bounds__(256) void decode_fp32_kernel(DecodeArgs a) {
     using G = Geo<D>;
@@ -311,6 +317,7 @@ __global__ __launch_bounds__(256) void decode_fp32_kernel(DecodeArgs a) {
     __shared__ float s_e[UPW][D];
     __shared__ float s_red[UPW][2][C8][D];
     __shared__ float s_kq[UPW][C8];
+    __shared__ float s_g[UPW][D];      // row gate (1 for a scalar gate)
 
     const int lt = threadIdx.x % TPU;
     const int ul = threadIdx.x / TPU;
@@ -341,16 +348,18 @@ __global__ __launch_bounds__(256) void decode_fp32_kernel(DecodeArgs a) {
         }
     }
     for (int idx = lt; idx < D; idx += TPU) {
-        float kv = 0.0f, qv = 0.0f, vv = 0.0f;
+        float kv = 0.0f, qv = 0.0f, vv = 0.0f, gv = 1.0f;
         if (live) {
             const size_t kb = (static_cast<size_t>(b) * a.Hk + hk) * D;
             kv = In<TIn>::get(a.k, kb + idx);
             qv = In<TIn>::get(a.q, kb + idx);
             vv = In<TIn>::get(a.v, (static_cast<size_t>(b) * a.Hv + h) * D + idx);
+            if (a.gate) gv = a.gate[static_cast<size_t>(unit) * D + idx];
         }
         s_k[ul][idx] = kv;
         s_q[ul][idx] = qv;
         s_v[ul][idx] = vv;
+        s_g[ul][idx] = gv;
     }
     __syncthreads();
 
@@ -366,10 +375,12 @@ __global__ __launch_bounds__(256) void decode_fp32_kernel(DecodeArgs a) {
         const int i = g + C8 * m;
         const float kp = s_k[ul][i];
         const float qp = s_q[ul][i];
+        const float gk = s_g[ul][i] * kp; // (D S)^T k and (D S)^T q
+        const float gq = s_g[ul][i] * qp;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            pu[e] = __builtin_fmaf(kp, s[m][e], pu[e]);
-            pw[e] = __builtin_fmaf(qp, s[m][e], pw[e]);
+            pu[e] = __builtin_fmaf(gk, s[m][e], pu[e]);
+            pw[e] = __builtin_fmaf(gq, s[m][e], pw[e]);
         }
         kqp = __builtin_fmaf(kp, qp, kqp);
     }
@@ -381,7 +392,7 @@ __global__ __launch_bounds__(256) void decode_fp32_kernel(DecodeArgs a) {
     if (c == 0) s_kq[ul][g] = kqp;
     __syncthreads();
 
-    const float alpha = active ? a.alpha[unit] : 0.0f;
+    const float alpha = !active ? 0.0f : (a.gate ? 1.0f : a.alpha[unit]);
     const float beta = active ? a.beta[unit] : 0.0f;
     for (int j = lt; j < D; j += TPU) {
         float u = 0.0f, w = 0.0f, kq = 0.0f;
@@ -408,9 +419,10 @@ __global__ __launch_bounds__(256) void decode_fp32_kernel(DecodeArgs a) {
     for (int m = 0; m < 8; ++m) {
         const int i = g + C8 * m;
         const float bk = beta * s_k[ul][i];
+        const float ad = alpha * s_g[ul][i];
         float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(alpha, s[m][e], bk * ev[e]);
+        for (int e = 0; e < 8; ++e) x[e] = __builtin_fmaf(ad, s[m][e], bk * ev[e]);
         if (live) {
             *reinterpret_cast<float4 *>(Sw + static_cast<size_t>(i) * D + 8 * c) = make_float4(x[0], x[1], x[2], x[3]);
             *reinterpret_cast<float4 *>(Sw + static_cast<size_t>(i) * D + 8 * c + 4) = make_float4(x[4], x[5], x[6], x[7]);

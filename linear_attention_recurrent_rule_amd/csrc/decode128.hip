@@ -1,8 +1,14 @@
 // Decode step specialised for 128 x 128 heads and a compile-time 4/8-bit row
 // split (n8 a multiple of 16): the serving shapes.  Same arithmetic contract as
-// decode.hip (STEPQuant paper, Sec. 2.1 Eq. (1) with D_t = a I; Sec. 2.2
-// quantizer; Sec. 4.3 representation; App. C.3 Table C2 step order), arranged
-// to keep the vector ALU count per state entry low:
+// decode.hip (STEPQuant paper, Sec. 2.1 Eq. (1) with D_t = a I or, in the KDA
+// form, D_t = diag(d) over the key rows; Sec. 2.2 quantizer; Sec. 4.3
+// representation; App. C.3 Table C2 step order), arranged to keep the vector
+// ALU count per state entry low:
+//
+//  * a row gate d_i enters only through the row's factor: the gated state row
+//    is d_i r_i z_i, so every per-row coefficient below uses d_i r_i in place
+//    of r_i and the scalar gate is 1 (a scalar gate a keeps d_i = 1 and
+//    applies a to the column sums, as before);
 //
 //  * one workgroup of 256 lanes per (slot, head); lane (g, c), g = lane / 16,
 //    c = lane % 16, owns columns 8c..8c+7 of physical rows g + 16 m, m = 0..7;
@@ -429,7 +435,8 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
         if (t < D) a.o[static_cast<size_t>(unit) * D + t] = __int_as_float(0x7fc00000);
         return;
     }
-    L.alpha = a.alpha[unit];
+    const bool gated = a.gate != nullptr; // uniform over the launch
+    L.alpha = gated ? 1.0f : a.alpha[unit];
     L.beta = a.beta[unit];
     const size_t ub = static_cast<size_t>(slot) * Hv + h;
     L.p8 = a.pool8 + ub * (N8 * D);
@@ -451,7 +458,9 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
         const float kp = In<TIn>::get(a.k, kb + i);
         const float qp = In<TIn>::get(a.q, kb + i);
         const float rp = L.rr[p];
-        const float scale = p < N8 ? rp : rp * 0.0625f; // 4-bit codes are widened as 16 z
+        // 4-bit codes are widened as 16 z; a row gate scales the whole row
+        const float gi = gated ? a.gate[static_cast<size_t>(unit) * D + i] : 1.0f;
+        const float scale = (p < N8 ? rp : rp * 0.0625f) * gi;
         {
             // row p = 4 w + gl + 16 m of wave w, lane group gl, slot m
             uint16_t(&cf)[7][8] = sh.coef[(p & 15) >> 2][p & 3];

@@ -96,7 +96,7 @@ stq_status dev(hipError_t e) { return e == hipSuccess ? STQ_OK : STQ_E_DEVICE; }
 
 extern "C" {
 
-int32_t stq_abi_version(void) { return 2; }
+int32_t stq_abi_version(void) { return 3; }
 
 const char *stq_status_str(int32_t s) {
     switch (s) {
@@ -226,9 +226,11 @@ stq_status stq_set_calibration(stq_state *st, const float *c, const int32_t *per
     return STQ_OK;
 }
 
-stq_status stq_calibrate_impact(stq_state *st, const void *q, const void *k, int32_t dtype,
-                                const float *alpha, const float *beta, int32_t B, uint32_t flags,
-                                stq_stream_t stream) {
+namespace {
+
+stq_status calibrate_impact(stq_state *st, const void *q, const void *k, int32_t dtype,
+                            const float *alpha, const float *gate, const float *beta, int32_t B,
+                            uint32_t flags, stq_stream_t stream) {
     stq_status e = check_state(st);
     if (e != STQ_OK) return e;
     if (st->desc.fmt != STQ_FMT_REFIT) return STQ_E_ARG;
@@ -236,15 +238,17 @@ stq_status stq_calibrate_impact(stq_state *st, const void *q, const void *k, int
     if (B < 0) return STQ_E_SHAPE;
     if (dtype != STQ_F32 && dtype != STQ_BF16) return STQ_E_ARG;
     const size_t el = dtype == STQ_F32 ? 4 : 2;
-    if (B > 0 && (!q || !k || !alpha || !beta || !aligned(q, el) || !aligned(k, el) ||
-                  !aligned(alpha, 4) || !aligned(beta, 4)))
+    const float *g_or_a = gate ? gate : alpha;
+    if (B > 0 && (!q || !k || !g_or_a || !beta || !aligned(q, el) || !aligned(k, el) ||
+                  !aligned(g_or_a, 4) || !aligned(beta, 4)))
         return STQ_E_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int D = st->desc.d_k, H = st->desc.n_heads_v;
     stq::ImpactArgs a;
     a.q = q;
     a.k = k;
-    a.alpha = alpha;
+    a.alpha = gate ? nullptr : alpha;
+    a.gate = gate;
     a.beta = beta;
     a.B = B;
     a.Hv = H;
@@ -260,6 +264,21 @@ stq_status stq_calibrate_impact(stq_state *st, const void *q, const void *k, int
     if (flags & STQ_CAL_FINALIZE)
         if ((e = dev(stq::launch_impact_finalize(D, a, s))) != STQ_OK) return e;
     return STQ_OK;
+}
+
+} // namespace
+
+stq_status stq_calibrate_impact(stq_state *st, const void *q, const void *k, int32_t dtype,
+                                const float *alpha, const float *beta, int32_t B, uint32_t flags,
+                                stq_stream_t stream) {
+    return calibrate_impact(st, q, k, dtype, alpha, nullptr, beta, B, flags, stream);
+}
+
+stq_status stq_calibrate_impact_gated(stq_state *st, const void *q, const void *k, int32_t dtype,
+                                      const float *gate, const float *beta, int32_t B,
+                                      uint32_t flags, stq_stream_t stream) {
+    if (B > 0 && !gate) return STQ_E_ARG;
+    return calibrate_impact(st, q, k, dtype, nullptr, gate, beta, B, flags, stream);
 }
 
 namespace {
@@ -332,17 +351,20 @@ bool partial_overlap(const void *p, const void *q, size_t n) {
     return a < b + n && b < a + n;
 }
 
+// Exactly one of alpha (scalar gate, [B][Hv]) and gate (row gate, [B][Hv][d_k])
+// is non-null.
 stq_status decode(const stq_state *src, const stq_state *dst, const int32_t *slots, int32_t B,
                   const void *q, const void *k, const void *v, int32_t dtype, const float *alpha,
-                  const float *beta, float *o, stq_stream_t stream) {
+                  const float *gate, const float *beta, float *o, stq_stream_t stream) {
     stq_status e = batch_args(src, slots, B);
     if (e != STQ_OK) return e;
     if ((e = check_state(dst)) != STQ_OK) return e;
     if (!same_desc(src->desc, dst->desc)) return STQ_E_SHAPE;
     if (dtype != STQ_F32 && dtype != STQ_BF16) return STQ_E_ARG;
     const size_t el = dtype == STQ_F32 ? 4 : 2;
-    if (!q || !k || !v || !alpha || !beta || !o) return STQ_E_ARG;
-    if (!aligned(q, el) || !aligned(k, el) || !aligned(v, el) || !aligned(alpha, 4) ||
+    const float *g_or_a = gate ? gate : alpha;
+    if (!q || !k || !v || !g_or_a || !beta || !o) return STQ_E_ARG;
+    if (!aligned(q, el) || !aligned(k, el) || !aligned(v, el) || !aligned(g_or_a, 4) ||
         !aligned(beta, 4) || !aligned(o, 4))
         return STQ_E_ARG;
     if (calibrated_format(src->desc.fmt) && !src->calibrated) return STQ_E_STATE;
@@ -371,7 +393,8 @@ stq_status decode(const stq_state *src, const stq_state *dst, const int32_t *slo
     a.q = q;
     a.k = k;
     a.v = v;
-    a.alpha = alpha;
+    a.alpha = gate ? nullptr : alpha;
+    a.gate = gate;
     a.beta = beta;
     a.o = o;
     a.B = B;
@@ -390,15 +413,24 @@ stq_status decode(const stq_state *src, const stq_state *dst, const int32_t *slo
 stq_status stq_decode_step(const stq_state *st, const int32_t *slots, int32_t B, const void *q,
                            const void *k, const void *v, int32_t dtype, const float *alpha,
                            const float *beta, float *o, stq_stream_t stream) {
-    return decode(st, st, slots, B, q, k, v, dtype, alpha, beta, o, stream);
+    if (!alpha) return STQ_E_ARG;
+    return decode(st, st, slots, B, q, k, v, dtype, alpha, nullptr, beta, o, stream);
 }
 
 stq_status stq_decode_step_into(const stq_state *src, const stq_state *dst, const int32_t *slots,
                                 int32_t B, const void *q, const void *k, const void *v,
                                 int32_t dtype, const float *alpha, const float *beta, float *o,
                                 stq_stream_t stream) {
-    if (!src || !dst) return STQ_E_ARG;
-    return decode(src, dst, slots, B, q, k, v, dtype, alpha, beta, o, stream);
+    if (!src || !dst || !alpha) return STQ_E_ARG;
+    return decode(src, dst, slots, B, q, k, v, dtype, alpha, nullptr, beta, o, stream);
+}
+
+stq_status stq_decode_step_gated(const stq_state *src, const stq_state *dst, const int32_t *slots,
+                                 int32_t B, const void *q, const void *k, const void *v,
+                                 int32_t dtype, const float *gate, const float *beta, float *o,
+                                 stq_stream_t stream) {
+    if (!src || !dst || !gate) return STQ_E_ARG;
+    return decode(src, dst, slots, B, q, k, v, dtype, nullptr, gate, beta, o, stream);
 }
 
 stq_status stq_stream_copy(const void *src, void *dst, size_t bytes, stq_stream_t stream) {

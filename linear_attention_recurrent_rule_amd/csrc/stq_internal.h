@@ -27,7 +27,8 @@ struct DecodeArgs {
     const void *q;        // [B][Hk][D]
     const void *k;        // [B][Hk][D]
     const void *v;        // [B][Hv][D]
-    const float *alpha;   // [B][Hv]
+    const float *alpha;   // [B][Hv] scalar gate (null when gate is given)
+    const float *gate;    // [B][Hv][D] per-key-row gate, logical rows, or null
     const float *beta;    // [B][Hv]
     float *o;             // [B][Hv][D]
     int32_t B, Hv, Hk, n8, n_slots;
@@ -52,7 +53,8 @@ struct PackArgs {
 // Row-impact calibration of the refit format.
 struct ImpactArgs {
     const void *q, *k;    // [B][Hk][D]
-    const float *alpha;   // [B][Hv]
+    const float *alpha;   // [B][Hv] scalar gate (null when gate is given)
+    const float *gate;    // [B][Hv][D] per-key-row gate, logical rows, or null
     const float *beta;    // [B][Hv]
     int32_t B, Hv, Hk;
     double *impact;       // [Hv][D] accumulated

@@ -50,7 +50,8 @@ class CState(ctypes.Structure):
 
 _LIB = None
 EXPORTS = ("stq_state_bytes", "stq_alloc_state", "stq_calibrate", "stq_calibrate_impact",
-           "stq_set_calibration", "stq_pack_state", "stq_decode_step", "stq_decode_step_into",
+           "stq_calibrate_impact_gated", "stq_set_calibration", "stq_pack_state",
+           "stq_decode_step", "stq_decode_step_into", "stq_decode_step_gated",
            "stq_dequant_state", "stq_stream_copy", "stq_status_str", "stq_abi_version")
 
 
@@ -70,19 +71,21 @@ def _lib():
         lib.stq_calibrate.argtypes = [ctypes.POINTER(CState), P, I64, U32, P]
         lib.stq_set_calibration.argtypes = [ctypes.POINTER(CState), P, P, P]
         lib.stq_calibrate_impact.argtypes = [ctypes.POINTER(CState), P, P, I32, P, P, I32, U32, P]
+        lib.stq_calibrate_impact_gated.argtypes = lib.stq_calibrate_impact.argtypes
         lib.stq_pack_state.argtypes = [ctypes.POINTER(CState), P, P, I32, P]
         lib.stq_decode_step.argtypes = [ctypes.POINTER(CState), P, I32, P, P, P, I32, P, P, P, P]
         lib.stq_decode_step_into.argtypes = [ctypes.POINTER(CState), ctypes.POINTER(CState), P,
                                              I32, P, P, P, I32, P, P, P, P]
+        lib.stq_decode_step_gated.argtypes = lib.stq_decode_step_into.argtypes
         lib.stq_dequant_state.argtypes = [ctypes.POINTER(CState), P, I32, P, P]
         lib.stq_stream_copy.argtypes = [P, P, SZ, P]
         lib.stq_status_str.argtypes = [I32]
         lib.stq_status_str.restype = ctypes.c_char_p
         lib.stq_abi_version.restype = I32
         for name in ("stq_alloc_state", "stq_calibrate", "stq_calibrate_impact",
-                     "stq_set_calibration",
+                     "stq_calibrate_impact_gated", "stq_set_calibration",
                      "stq_pack_state", "stq_decode_step", "stq_decode_step_into",
-                     "stq_dequant_state", "stq_stream_copy"):
+                     "stq_decode_step_gated", "stq_dequant_state", "stq_stream_copy"):
             getattr(lib, name).restype = I32
         _LIB = lib
     return _LIB
@@ -111,6 +114,18 @@ def _dev_ptr(t: torch.Tensor | None, name: str):
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _in_dtype(q, k, v) -> int:
+    if q.dtype == torch.float32:
+        dt = F32
+    elif q.dtype == torch.bfloat16:
+        dt = BF16
+    else:
+        raise ValueError("q, k, v must be float32 or bfloat16")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype")
+    return dt
 
 
 def state_bytes(n_slots, n_heads_v, n_heads_k, d, n8, fmt) -> int:
@@ -220,14 +235,22 @@ class State:
         _check(_lib().stq_calibrate(ctypes.byref(self.c_state), _dev_ptr(records, "records"),
                                     n, flags, _stream(stream)), "stq_calibrate")
 
-    def calibrate_impact(self, q, k, alpha, beta, flags: int, stream=None):
+    def calibrate_impact(self, q, k, alpha, beta, flags: int, stream=None, gate=None):
         """Accumulate row impact over one step's samples (q, k [B][Hk][d], alpha,
-        beta [B][Hv]); CAL_RESET / CAL_FINALIZE as in stq_calibrate_impact."""
+        beta [B][Hv]); CAL_RESET / CAL_FINALIZE as in stq_calibrate_impact.
+        With gate [B][Hv][d] (logical rows) the row gate replaces alpha
+        (stq_calibrate_impact_gated)."""
         if q is None:
             B, dt = 0, F32
         else:
             B = int(q.shape[0])
             dt = BF16 if q.dtype == torch.bfloat16 else F32
+        if gate is not None:
+            _check(_lib().stq_calibrate_impact_gated(
+                ctypes.byref(self.c_state), _dev_ptr(q, "q"), _dev_ptr(k, "k"), dt,
+                _dev_ptr(gate, "gate"), _dev_ptr(beta, "beta"), B, flags, _stream(stream)),
+                "stq_calibrate_impact_gated")
+            return
         _check(_lib().stq_calibrate_impact(ctypes.byref(self.c_state), _dev_ptr(q, "q"),
                                            _dev_ptr(k, "k"), dt, _dev_ptr(alpha, "alpha"),
                                            _dev_ptr(beta, "beta"), B, flags, _stream(stream)),
@@ -284,6 +307,25 @@ class State:
                                            _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
                                            _dev_ptr(o, "o"), _stream(stream)),
                "stq_decode_step_into")
+        return o
+
+    def decode_step_gated(self, q, k, v, gate, beta, o=None, slots=None, stream=None,
+                          dst: "State | None" = None):
+        """Decode with a per-key-row gate [B][Hv][d] (logical rows, fp32),
+        in place or, with dst, into another state (stq_decode_step_gated)."""
+        dt = _in_dtype(q, k, v)
+        B = int(q.shape[0])
+        if o is None:
+            o = torch.empty((B, self.geo.n_heads_v, self.geo.d), dtype=torch.float32,
+                            device=q.device)
+        target = self if dst is None else dst
+        _check(_lib().stq_decode_step_gated(ctypes.byref(self.c_state),
+                                            ctypes.byref(target.c_state),
+                                            _dev_ptr(slots, "slots"), B, _dev_ptr(q, "q"),
+                                            _dev_ptr(k, "k"), _dev_ptr(v, "v"), dt,
+                                            _dev_ptr(gate, "gate"), _dev_ptr(beta, "beta"),
+                                            _dev_ptr(o, "o"), _stream(stream)),
+               "stq_decode_step_gated")
         return o
 
     def dequant(self, B: int | None = None, slots=None, out=None, stream=None):

@@ -17,6 +17,9 @@ Laws (per sequence b, head h, step t):
   v    ~ N(0, 1)^d                                  (value head)
   alpha ~ U(lo, 1),  beta = sigmoid(N(0, 1))        (value head)
   bf16 inputs are the fp32 draws rounded to nearest-even bf16.
+Per-key-row gates of the KDA form (draw_gate; one fp32 per sequence, value
+head and logical key row, from a stream of its own):
+  d_i = sigmoid(N(2.5, 1.5))   (median 0.92; about 5 % of rows below 0.5)
 Random packed states (for per-step parity from an arbitrary state) draw codes
 uniformly from the symmetric range of their row width, log-uniform row factors,
 log-normal column factors and a random physical row order per head.
@@ -79,6 +82,7 @@ _TAG_INPUTS = 11
 _TAG_S0 = 12
 _TAG_PACKED = 13
 _TAG_RECORDS = 14
+_TAG_GATE = 15
 
 
 def rng_for(*key: int) -> np.random.Generator:
@@ -138,6 +142,14 @@ def draw_inputs(B: int, hk: int, hv: int, d: int, *, dtype: str, seed: int, step
                           alpha, beta, dtype, qb, kb, vb)
     assert dtype == "f32"
     return StepInputs(q, k, v, alpha, beta, dtype)
+
+
+def draw_gate(B: int, hv: int, d: int, *, seed: int, step: int, layer: int = 0,
+              mu: float = 2.5, sigma: float = 1.5) -> np.ndarray:
+    """Per-key-row gate [B][Hv][d] fp32 in logical row order."""
+    g = rng_for(seed, _TAG_GATE, layer, step)
+    x = g.normal(mu, sigma, size=(B, hv, d))
+    return (1.0 / (1.0 + np.exp(-x))).astype(np.float32)
 
 
 def workload_inputs(w: Workload, step: int, *, calibration: bool = False, layer: int = 0,

@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
     assert "stq_decode_step" in names and len(names) >= 8
     for n in names:
         assert hasattr(lib, n), f"libstq.so does not export {n}"
-    assert lib.stq_abi_version() == 2
+    assert lib.stq_abi_version() == 3
 
 
 def _desc(n_slots=4, hv=4, hk=2, d=64, n8=32, fmt=stq.FMT_MIXED48, dv=None):
@@ -218,3 +218,38 @@ def test_refit_layout_and_rejections():
     assert ci(st, 2, 0, q=FAKE + 2) == E_ARG
     mixed_st = _fake_state(calibrated=1)
     assert ci(mixed_st, 0, stq.CAL_RESET) == E_ARG
+
+
+def test_gated_rejections():
+    lib = stq.lib()
+    src = _fake_state(calibrated=1)
+    p = [FAKE] * 6
+
+    def gated(a, b, gate=FAKE, B=2, dtype=0):
+        return lib.stq_decode_step_gated(a, b, None, B, p[0], p[1], p[2], dtype, gate, p[4],
+                                         p[5], None)
+
+    assert gated(ctypes.byref(src), ctypes.byref(src), gate=None) == E_ARG
+    assert gated(ctypes.byref(src), ctypes.byref(src), gate=FAKE + 2) == E_ARG
+    assert gated(None, ctypes.byref(src)) == E_ARG
+    assert gated(ctypes.byref(src), None) == E_ARG
+    assert gated(ctypes.byref(src), ctypes.byref(src), B=0) == E_SHAPE
+    assert gated(ctypes.byref(src), ctypes.byref(src), dtype=3) == E_ARG
+    other = _fake_state(calibrated=1, n8=16)
+    assert gated(ctypes.byref(src), ctypes.byref(other)) == E_SHAPE
+    uncal = _fake_state(calibrated=0)
+    assert gated(ctypes.byref(uncal), ctypes.byref(uncal)) == E_STATE
+    # the scalar entry points still need alpha
+    assert lib.stq_decode_step(ctypes.byref(src), None, 2, FAKE, FAKE, FAKE, 0, None, FAKE,
+                               FAKE, None) == E_ARG
+    # gated row-impact calibration: REFIT only, a gate whenever B > 0
+    st = _fake_state(fmt=stq.FMT_REFIT, calibrated=1, n8=64, d=128)
+    for i, f in enumerate(("cs", "w2", "impact")):
+        setattr(st, f, FAKE + 0x1000000 * (11 + i))
+    cg = lambda s_, B, flags, gate=FAKE: lib.stq_calibrate_impact_gated(  # noqa: E731
+        ctypes.byref(s_), FAKE, FAKE, 0, gate, FAKE, B, flags, None)
+    assert cg(st, 2, 0, gate=None) == E_ARG
+    assert cg(st, 2, 0, gate=FAKE + 1) == E_ARG
+    assert cg(st, -1, stq.CAL_RESET) == E_SHAPE
+    assert cg(st, 2, stq.CAL_COLS) == E_ARG
+    assert cg(_fake_state(calibrated=1), 0, stq.CAL_RESET) == E_ARG
