@@ -8,6 +8,7 @@ explicit __builtin_fmaf, so the rounding points are the ones written.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -49,14 +50,18 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> Path:
     cc = hipcc()
     objdir = PKG / "_build"
     objdir.mkdir(exist_ok=True)
-    objs = []
+    objs, cmds = [], []
     for src in SOURCES:
         obj = objdir / (src + ".o")
-        cmd = [cc, *compile_flags(), *(extra or []), "-c", str(CSRC / src), "-o", str(obj)]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
+        cmds.append([cc, *compile_flags(), *(extra or []), "-c", str(CSRC / src), "-o", str(obj)])
         objs.append(str(obj))
+    # the sources are independent translation units: compile them concurrently
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(cmds), 8)) as ex:
+        for cmd in cmds:
+            if verbose:
+                print(" ".join(cmd), flush=True)
+        for f in [ex.submit(subprocess.run, cmd, check=True) for cmd in cmds]:
+            f.result()
     tmp = LIB.with_suffix(".so.tmp")
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *objs]
     if verbose:

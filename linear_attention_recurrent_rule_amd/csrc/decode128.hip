@@ -406,7 +406,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
     }
 }
 
-template <int N8, typename TIn, bool REFIT>
+template <int N8, typename TIn, bool REFIT, bool GATED>
 __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_remap, unsigned hv_m,
                                                         unsigned g_m) {
     static_assert(N8 % 16 == 0 && N8 >= 0 && N8 <= D, "n8 must be a multiple of 16");
@@ -435,8 +435,7 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
         if (t < D) a.o[static_cast<size_t>(unit) * D + t] = __int_as_float(0x7fc00000);
         return;
     }
-    const bool gated = a.gate != nullptr; // uniform over the launch
-    L.alpha = gated ? 1.0f : a.alpha[unit];
+    L.alpha = GATED ? 1.0f : a.alpha[unit];
     L.beta = a.beta[unit];
     const size_t ub = static_cast<size_t>(slot) * Hv + h;
     L.p8 = a.pool8 + ub * (N8 * D);
@@ -459,8 +458,8 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
         const float qp = In<TIn>::get(a.q, kb + i);
         const float rp = L.rr[p];
         // 4-bit codes are widened as 16 z; a row gate scales the whole row
-        const float gi = gated ? a.gate[static_cast<size_t>(unit) * D + i] : 1.0f;
-        const float scale = (p < N8 ? rp : rp * 0.0625f) * gi;
+        float scale = p < N8 ? rp : rp * 0.0625f;
+        if (GATED) scale *= a.gate[static_cast<size_t>(unit) * D + i];
         {
             // row p = 4 w + gl + 16 m of wave w, lane group gl, slot m
             uint16_t(&cf)[7][8] = sh.coef[(p & 15) >> 2][p & 3];
@@ -500,25 +499,34 @@ unsigned div_magic(unsigned d) {
     return d <= 1 ? 0u : static_cast<unsigned>(((1ull << 32) + d - 1) / d);
 }
 
+template <int N8, typename TIn, bool REFIT, bool GATED>
+void launch_one(const DecodeArgs &a, unsigned units, int remap, unsigned hv_m, unsigned g_m,
+                hipStream_t s) {
+    hipLaunchKernelGGL((decode128_kernel<N8, TIn, REFIT, GATED>), dim3(units), dim3(256), 0, s, a,
+                       remap, hv_m, g_m);
+}
+
+template <int N8, typename TIn>
+void launch_in(const DecodeArgs &a, unsigned units, int remap, unsigned hv_m, unsigned g_m,
+               hipStream_t s) {
+    const bool refit = a.cs != nullptr;
+    const bool gated = a.gate != nullptr;
+    if (refit && gated) launch_one<N8, TIn, true, true>(a, units, remap, hv_m, g_m, s);
+    else if (refit) launch_one<N8, TIn, true, false>(a, units, remap, hv_m, g_m, s);
+    else if (gated) launch_one<N8, TIn, false, true>(a, units, remap, hv_m, g_m, s);
+    else launch_one<N8, TIn, false, false>(a, units, remap, hv_m, g_m, s);
+}
+
 template <int N8>
 hipError_t launch_n8(bool bf16, const DecodeArgs &a, hipStream_t s) {
     const unsigned units = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.Hv);
     const int remap = (units % 8u) == 0u ? 1 : 0;
     const unsigned hv_m = div_magic(static_cast<unsigned>(a.Hv));
     const unsigned g_m = div_magic(static_cast<unsigned>(a.Hv / a.Hk));
-    const bool refit = a.cs != nullptr;
-    if (bf16 && refit)
-        hipLaunchKernelGGL((decode128_kernel<N8, uint16_t, true>), dim3(units), dim3(256), 0, s, a,
-                           remap, hv_m, g_m);
-    else if (bf16)
-        hipLaunchKernelGGL((decode128_kernel<N8, uint16_t, false>), dim3(units), dim3(256), 0, s, a,
-                           remap, hv_m, g_m);
-    else if (refit)
-        hipLaunchKernelGGL((decode128_kernel<N8, float, true>), dim3(units), dim3(256), 0, s, a,
-                           remap, hv_m, g_m);
+    if (bf16)
+        launch_in<N8, uint16_t>(a, units, remap, hv_m, g_m, s);
     else
-        hipLaunchKernelGGL((decode128_kernel<N8, float, false>), dim3(units), dim3(256), 0, s, a,
-                           remap, hv_m, g_m);
+        launch_in<N8, float>(a, units, remap, hv_m, g_m, s);
     return hipGetLastError();
 }
 

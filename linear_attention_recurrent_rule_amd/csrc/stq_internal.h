@@ -28,10 +28,10 @@ struct DecodeArgs {
     const void *k;        // [B][Hk][D]
     const void *v;        // [B][Hv][D]
     const float *alpha;   // [B][Hv] scalar gate (null when gate is given)
-    const float *gate;    // [B][Hv][D] per-key-row gate, logical rows, or null
     const float *beta;    // [B][Hv]
     float *o;             // [B][Hv][D]
     int32_t B, Hv, Hk, n8, n_slots;
+    const float *gate;    // [B][Hv][D] per-key-row gate, logical rows, or null
 };
 
 // Pack / dequant of B slots.
