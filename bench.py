@@ -72,6 +72,9 @@ def parse():
                         "step, row-impact weights from the calibration steps)")
     p.add_argument("--drift-steps", type=int, default=None, help="T for --drift (default: the "
                    "workload's)")
+    p.add_argument("--gate", action="store_true",
+                   help="--drift with a per-key-row gate of the KDA form in place of alpha, "
+                        "d_i = sigmoid(N(2.5, 1.5)) per (sequence, value head, key row, step)")
     return p.parse_args()
 
 
@@ -386,14 +389,34 @@ def run_drift(args, np, torch, stq, wl, w) -> dict:
     host = layers == 1 and w.units * w.d <= 1 << 22
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
 
+    def gate_for(layer, t, calibration):
+        seed = w.calib_seed if calibration else w.seed
+        if host:
+            return dev(wl.draw_gate(w.B, w.hv, w.d, seed=seed, step=t, layer=layer))
+        g = torch.Generator(device="cuda").manual_seed(seed * 1_000_003 + layer * 10_007 + t
+                                                       + 500_009)
+        return torch.sigmoid(torch.randn(w.B, w.hv, w.d, device="cuda", generator=g) * 1.5
+                             + 2.5).contiguous()
+
     def inputs(layer, t, calibration=False):
         if not host:
-            return device_inputs(torch, w, layer, t, calibration)
-        x = wl.workload_inputs(w, t, calibration=calibration, layer=layer)
-        if x.dtype == "bf16":
-            cv = lambda bits: dev(bits.view(np.int16)).view(torch.bfloat16)  # noqa: E731
-            return cv(x.q_bits), cv(x.k_bits), cv(x.v_bits), dev(x.alpha), dev(x.beta)
-        return dev(x.q), dev(x.k), dev(x.v), dev(x.alpha), dev(x.beta)
+            x = device_inputs(torch, w, layer, t, calibration)
+        else:
+            h = wl.workload_inputs(w, t, calibration=calibration, layer=layer)
+            if h.dtype == "bf16":
+                cv = lambda bits: dev(bits.view(np.int16)).view(torch.bfloat16)  # noqa: E731
+                x = cv(h.q_bits), cv(h.k_bits), cv(h.v_bits), dev(h.alpha), dev(h.beta)
+            else:
+                x = dev(h.q), dev(h.k), dev(h.v), dev(h.alpha), dev(h.beta)
+        # with --gate, the fourth entry is the row gate [B][Hv][d] instead of alpha
+        if args.gate:
+            x = (x[0], x[1], x[2], gate_for(layer, t, calibration), x[4])
+        return x
+
+    def step(st, x, o=None):
+        if args.gate:
+            return st.decode_step_gated(*x, o=o)
+        return st.decode_step(*x, o=o)
 
     t0 = time.time()
     quant, ref = [], []
@@ -414,8 +437,10 @@ def run_drift(args, np, torch, stq, wl, w) -> dict:
             fpc.pack(S0)
             for t in range(w.calib_steps):
                 x = inputs(layer, t, calibration=True)
-                fpc.decode_step(*x)
-                if args.refit:
+                step(fpc, x)
+                if args.refit and args.gate:
+                    cal.calibrate_impact(x[0], x[1], None, x[4], 0, gate=x[3])
+                elif args.refit:
                     cal.calibrate_impact(x[0], x[1], x[3], x[4], 0)
                 last = t == w.calib_steps - 1
                 cal.calibrate(fpc.s32, stq.CAL_COLS | (stq.CAL_ROWS if last else 0))
@@ -446,8 +471,8 @@ def run_drift(args, np, torch, stq, wl, w) -> dict:
         o_rel = []
         for layer in range(layers):
             x = inputs(layer, t - 1)
-            quant[layer].decode_step(*x, o=oq)
-            ref[layer].decode_step(*x, o=of)
+            step(quant[layer], x, o=oq)
+            step(ref[layer], x, o=of)
             err = (oq - of).double().pow(2).sum()
             nrm = of.double().pow(2).sum()
             o_err_sum[layer] += err
@@ -476,6 +501,7 @@ def run_drift(args, np, torch, stq, wl, w) -> dict:
                       "state": ("int8row" if w.calib_seed is None
                                 else "packed, refit column factors" if args.refit else "packed"),
                       "n8": w.n8 if w.calib_seed is not None else w.d,
+                      "gate": "per key row (KDA form)" if args.gate else "scalar",
                       "checkpoints": points,
                       "readout_rel_l2_over_all_steps_mean": float(np.mean(o_all)),
                       "readout_rel_l2_over_all_steps_max": float(np.max(o_all))}}

@@ -35,12 +35,13 @@
  *       C2 step 5) over all rows of the head, weights w2 = w^2; the new factor
  *       is rounded to fp32 and floored at 2^-126, a zero denominator keeps the
  *       old one.  The stored codes are those taken against the old factors.
- *   R16 the diagonal gate (KDA form) is one fp32 value per (sequence, value
- *       head, logical key row); it scales row i of the previous state.
  *   R15 row-impact weights: omega_i = sum over calibration samples of
- *       (alpha (q_i - beta k_i k.q))^2 (Sec. 4.1 with the scalar gate), and
+ *       (alpha (q_i - beta k_i k.q))^2 (Sec. 4.1 with the scalar gate; with
+ *       the diagonal gate, d_i in place of alpha, App. C.1), and
  *       w2_i = (omega_i / mean omega)^(1/4) (App. B.3: w ~ omega^(1/8)),
  *       floored at 2^-32; an all-zero head gets w2 = 1.
+ *   R16 the diagonal gate (KDA form) is one fp32 value per (sequence, value
+ *       head, logical key row); it scales row i of the previous state.
  *
  * Arithmetic: every intermediate is an IEEE double; the persisted quantities
  * (r, o) are rounded once to fp32.  Build with -ffp-contract=off so that the
