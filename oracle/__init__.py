@@ -22,6 +22,11 @@ Parity status of each function (what pins it is in ``tests/test_oracle_pins.py``
   dequant_cs             weighted least-squares optimality (App. C.1 objective),
                          zero-column rule, fixed point
   impact_*       pinned: closed forms for unit-vector keys and queries
+  alloc_*        (ragged row classes, FP16 pivots, lifetime-aware assignment;
+                 ``stq_alloc_oracle.c``) pinned in ``tests/test_oracle_alloc_pins.py``:
+                 equivalence with the 4/8-bit format, brute-force round trips
+                 per class, numpy float16 rounding, step closed forms,
+                 brute-force optimality of the assignment on small cases
 """
 from __future__ import annotations
 
@@ -34,23 +39,33 @@ import numpy as np
 
 _HERE = Path(__file__).resolve().parent
 _SRC = _HERE / "stq_oracle.c"
+_ALLOC_SRC = _HERE / "stq_alloc_oracle.c"
 _LIB = _HERE / "libstq_oracle.so"
 
 
-def compile_oracle(src: Path, out: Path) -> Path:
-    """Compile an oracle source file with gcc (plain C, no GPU code)."""
+def compile_oracle(src: Path, out: Path, alloc_src: Path | None = None) -> Path:
+    """Compile the oracle sources with gcc (plain C, no GPU code): ``src`` in
+    place of ``stq_oracle.c`` and ``alloc_src`` (default: the real one) in
+    place of ``stq_alloc_oracle.c``."""
     tmp = out.with_suffix(".so.tmp")
     subprocess.run(
         ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
-         "-Wall", "-o", str(tmp), str(src), "-lm", "-lpthread"],
+         "-Wall", "-o", str(tmp), str(src), str(alloc_src or _ALLOC_SRC), "-lm", "-lpthread"],
         check=True)
     os.replace(tmp, out)
     return out
 
 
+def _stale() -> bool:
+    if not _LIB.exists():
+        return True
+    t = _LIB.stat().st_mtime
+    return t < _SRC.stat().st_mtime or t < _ALLOC_SRC.stat().st_mtime
+
+
 def build(force: bool = True) -> Path:
-    """Build ``libstq_oracle.so`` next to its source."""
-    if force or not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+    """Build ``libstq_oracle.so`` next to its sources."""
+    if force or _stale():
         compile_oracle(_SRC, _LIB)
     return _LIB
 
@@ -78,6 +93,21 @@ def _bind(path: Path):
     lib.oracle_fp_step_gated.argtypes = [I, I, I, I, I] + [P] * 7 + [I]
     lib.oracle_step_refit_gated.argtypes = [I, I, I, I, I, I] + [P] * 17 + [I]
     lib.oracle_impact_accumulate_gated.argtypes = [I, I, I, I, P, P, P, P, P]
+    lib.oracle_f16_from_double.argtypes = [ctypes.c_double]
+    lib.oracle_f16_from_double.restype = ctypes.c_uint16
+    lib.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_double.restype = ctypes.c_double
+    lib.oracle_alloc_layout.argtypes = [I, I, P, P]
+    lib.oracle_alloc_layout.restype = L
+    lib.oracle_alloc_dequant.argtypes = [I, I, I, L, P, P, P, P, P, P, P, I]
+    lib.oracle_alloc_pack.argtypes = [I, I, I, L, P, P, P, P, P, P, P, P, I]
+    lib.oracle_alloc_step.argtypes = [I, I, I, I, L] + [P] * 18 + [I]
+    lib.oracle_alloc_distortion.argtypes = [L, I, I, P, P, P]
+    lib.oracle_alloc_lifetime.argtypes = [I, I, P, ctypes.c_double, I, P]
+    lib.oracle_alloc_assign.argtypes = [I, I, P, P, I, I, I, P, P, P]
+    for name in ("oracle_alloc_dequant", "oracle_alloc_pack", "oracle_alloc_step",
+                 "oracle_alloc_distortion", "oracle_alloc_lifetime", "oracle_alloc_assign"):
+        getattr(lib, name).restype = I
     for name in ("oracle_dequant", "oracle_pack", "oracle_step", "oracle_fp_step",
                  "oracle_calib_cols", "oracle_calib_rows", "oracle_calib_finalize",
                  "oracle_dequant_cs", "oracle_pack_refit", "oracle_step_refit",
@@ -117,7 +147,7 @@ class Oracle:
     def lib(self):
         if self._lib is None:
             if self._path is None:
-                if not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+                if _stale():
                     build(force=True)
                 self._path = _LIB
             self._lib = _bind(self._path)
@@ -351,6 +381,130 @@ class Oracle:
         return w2
 
 
+    # ------------------------------------------------ ragged row classes --
+    # stq_alloc_oracle.c; classes k = 0..4 are FP16 pivots, 8, 6, 4, 2 bits.
+
+    def f16(self, x: float) -> int:
+        """IEEE binary16 bits of x, nearest even, saturating (reading R18)."""
+        return int(self.lib().oracle_f16_from_double(float(x)))
+
+    def f16_value(self, h: int) -> float:
+        return float(self.lib().oracle_f16_to_double(int(h)))
+
+    def alloc_layout(self, counts, d: int):
+        """Per-head segment offsets [Hv] and the bytes one slot needs
+        (App. C.3 Table C2 storage; reading R17)."""
+        counts = _c(counts, np.int32)
+        hv = counts.shape[0]
+        off = np.zeros(hv, np.int64)
+        need = self.lib().oracle_alloc_layout(hv, d, _ptr(counts), _ptr(off))
+        assert need >= 0, "row-class counts must sum to d"
+        return off, int(need)
+
+    def alloc_dequant(self, pool, r, counts, perm, *, c=None, cs=None, nthreads: int = 1):
+        """S [B][Hv][d][d] (logical order) from the ragged pool [B][slot_bytes]
+        (Table C2 step 1; readings R17-R19)."""
+        pool = _c(pool, np.uint8)
+        r = _c(r, np.float32)
+        B, hv, d = r.shape
+        counts = _c(counts, np.int32)
+        perm = _c(perm, np.int32)
+        S = np.empty((B, hv, d, d), np.float64)
+        c = None if c is None else _c(c, np.float32)
+        cs = None if cs is None else _c(cs, np.float32)
+        rc = self.lib().oracle_alloc_dequant(
+            B, hv, d, pool.shape[1], _ptr(counts), _ptr(perm), _ptr(pool), _ptr(r),
+            _ptr(c), _ptr(cs), _ptr(S), nthreads)
+        assert rc == 0
+        return S
+
+    def alloc_pack(self, S, counts, perm, c, slot_bytes: int, *, w2=None, refit=False,
+                   nthreads: int = 1):
+        """Pack S [B][Hv][d][d] into a ragged pool [B][slot_bytes]; returns
+        (pool, r) or, with refit, (pool, r, cs) (readings R17-R19, R14)."""
+        S = _c(S, np.float64)
+        B, hv, d, _ = S.shape
+        counts = _c(counts, np.int32)
+        perm = _c(perm, np.int32)
+        c = _c(c, np.float32)
+        pool = np.zeros((B, slot_bytes), np.uint8)
+        r = np.zeros((B, hv, d), np.float32)
+        cs = np.zeros((B, hv, d), np.float32) if refit else None
+        w2 = None if w2 is None else _c(w2, np.float32)
+        rc = self.lib().oracle_alloc_pack(
+            B, hv, d, slot_bytes, _ptr(counts), _ptr(perm), _ptr(S), _ptr(c), _ptr(w2),
+            _ptr(pool), _ptr(r), _ptr(cs), nthreads)
+        assert rc == 0
+        return (pool, r, cs) if refit else (pool, r)
+
+    def alloc_step(self, pool, r, counts, perm, q, k, v, alpha, beta, *, c=None, cs=None,
+                   w2=None, gate=None, want_X: bool = False, nthreads: int = 1):
+        """One decode step on the ragged format (Table C2 with pivots; Eq. (1)
+        with the scalar or, given gate [B][Hv][d], the row gate).  Fixed c
+        [Hv][d], or per-state cs [B][Hv][d] with the refit (w2 needed).
+        Returns dict pool, r, o (and cs, X)."""
+        pool = _c(pool, np.uint8)
+        r = _c(r, np.float32)
+        B, hv, d = r.shape
+        q = _c(q, np.float32)
+        hk = q.shape[1]
+        counts = _c(counts, np.int32)
+        perm = _c(perm, np.int32)
+        out = {"pool": np.zeros_like(pool), "r": np.zeros_like(r),
+               "o": np.empty((B, hv, d), np.float32)}
+        if cs is not None:
+            out["cs"] = np.zeros((B, hv, d), np.float32)
+        X = np.empty((B, hv, d, d), np.float64) if want_X else None
+        opt = lambda a: None if a is None else _c(a, np.float32)  # noqa: E731
+        # every converted array is held by a name until the call returns
+        c, cs, w2, alpha, gate = opt(c), opt(cs), opt(w2), opt(alpha), opt(gate)
+        k, v, beta = _c(k, np.float32), _c(v, np.float32), _c(beta, np.float32)
+        rc = self.lib().oracle_alloc_step(
+            B, hv, hk, d, pool.shape[1], _ptr(counts), _ptr(perm), _ptr(pool), _ptr(r),
+            _ptr(c), _ptr(cs), _ptr(w2), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(gate),
+            _ptr(beta), _ptr(out["pool"]), _ptr(out["r"]), _ptr(out.get("cs")), _ptr(out["o"]),
+            _ptr(X), nthreads)
+        assert rc == 0
+        if want_X:
+            out["X"] = X
+        return out
+
+    def alloc_distortion(self, S, c, dist):
+        """dist [Hv][d][5] += candidate distortions of the records S
+        [n][Hv][d][d] (App. A.3 KDA distortion; reading R20)."""
+        S = _c(S, np.float64)
+        n, hv, d, _ = S.shape
+        assert dist.dtype == np.float64 and dist.shape == (hv, d, 5)
+        c = _c(c, np.float32)
+        assert self.lib().oracle_alloc_distortion(n, hv, d, _ptr(S), _ptr(c), _ptr(dist)) == 0
+
+    def alloc_lifetime(self, logret, n: float, horizon: int):
+        """L [Hv][d] from the summed log retention over n samples (App. A.3;
+        reading R21)."""
+        logret = _c(logret, np.float64)
+        Lw = np.empty_like(logret)
+        assert self.lib().oracle_alloc_lifetime(logret.shape[0], logret.shape[1], _ptr(logret),
+                                                float(n), int(horizon), _ptr(Lw)) == 0
+        return Lw
+
+    def alloc_assign(self, dist, Lw, *, nominal: int, n_pivot: int, candidates=(8, 6, 4)):
+        """Pivots and widths per row (App. C.2; readings R22, R23).  Returns
+        bits [Hv][d], counts [Hv][5], perm [Hv][d]."""
+        dist = _c(dist, np.float64)
+        hv, d, _ = dist.shape
+        Lw = _c(Lw, np.float64)
+        mask = 0
+        for b in candidates:
+            mask |= 1 << {8: 1, 6: 2, 4: 3, 2: 4}[b]
+        bits = np.zeros((hv, d), np.int32)
+        counts = np.zeros((hv, 5), np.int32)
+        perm = np.zeros((hv, d), np.int32)
+        rc = self.lib().oracle_alloc_assign(hv, d, _ptr(dist), _ptr(Lw), mask, nominal, n_pivot,
+                                            _ptr(bits), _ptr(counts), _ptr(perm))
+        assert rc == 0, "infeasible budget or bad candidates"
+        return bits, counts, perm
+
+
 _default = Oracle()
 rhe = _default.rhe
 dequant = _default.dequant
@@ -365,3 +519,12 @@ pack_refit = _default.pack_refit
 step_refit = _default.step_refit
 impact_accumulate = _default.impact_accumulate
 impact_weights = _default.impact_weights
+f16 = _default.f16
+f16_value = _default.f16_value
+alloc_layout = _default.alloc_layout
+alloc_dequant = _default.alloc_dequant
+alloc_pack = _default.alloc_pack
+alloc_step = _default.alloc_step
+alloc_distortion = _default.alloc_distortion
+alloc_lifetime = _default.alloc_lifetime
+alloc_assign = _default.alloc_assign

@@ -182,10 +182,11 @@ static void unit_delta_step_diag(int dk, int dv, double *S, const double *q,
     free(u);
 }
 
-/* Either gate: the scalar alpha of unit u, or the row gate gate[u][dk]. */
-static void unit_update(int dk, int dv, double *S, const double *q, const double *k,
-                        const double *v, const float *alpha, const float *gate, long u,
-                        double beta, double *o) {
+/* Either gate: the scalar alpha of unit u, or the row gate gate[u][dk].
+ * Also used by the ragged-format oracle (stq_alloc_oracle.c). */
+void orc_unit_update(int dk, int dv, double *S, const double *q, const double *k,
+                     const double *v, const float *alpha, const float *gate, long u,
+                     double beta, double *o) {
     if (!gate) {
         unit_delta_step(dk, dv, S, q, k, v, (double)alpha[u], beta, o);
         return;
@@ -272,8 +273,9 @@ static void *span_run(void *arg) {
     return NULL;
 }
 
-/* Run fn over units [0, n) on nthreads threads (static contiguous split). */
-static void for_units(long n, int nthreads, unit_fn fn, void *ctx) {
+/* Run fn over units [0, n) on nthreads threads (static contiguous split).
+ * Also used by the ragged-format oracle. */
+void orc_for_units(long n, int nthreads, unit_fn fn, void *ctx) {
     if (nthreads < 1) nthreads = 1;
     if (nthreads > n) nthreads = (int)(n > 0 ? n : 1);
     pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
@@ -326,7 +328,7 @@ int oracle_dequant(int B, int hv, int dk, int dv, int n8, const int8_t *pool8,
                    const int32_t *perm, double *S, int nthreads) {
     dequant_ctx x = {{hv, 1, dk, dv, n8}, pool8, pool4, r, c, perm, S};
     if (check_shape(&x.s)) return -1;
-    for_units((long)B * hv, nthreads, dequant_unit, &x);
+    orc_for_units((long)B * hv, nthreads, dequant_unit, &x);
     return 0;
 }
 
@@ -361,7 +363,7 @@ int oracle_pack(int B, int hv, int dk, int dv, int n8, const float *S,
                 uint8_t *pool4, float *r, int nthreads) {
     pack_ctx x = {{hv, 1, dk, dv, n8}, S, c, perm, pool8, pool4, r};
     if (check_shape(&x.s)) return -1;
-    for_units((long)B * hv, nthreads, pack_unit, &x);
+    orc_for_units((long)B * hv, nthreads, pack_unit, &x);
     return 0;
 }
 
@@ -404,7 +406,7 @@ static void step_unit(void *vctx, long u) {
     for (int j = 0; j < s->dv; ++j) v[j] = (double)x->v[(size_t)u * s->dv + j];
     /* Table C2 steps 2-3: update, then emit the readout of the updated state
      * before it is requantized. */
-    unit_update(s->dk, s->dv, S, q, k, v, x->alpha, x->gate, u, (double)x->beta[u], o);
+    orc_unit_update(s->dk, s->dv, S, q, k, v, x->alpha, x->gate, u, (double)x->beta[u], o);
     for (int j = 0; j < s->dv; ++j) x->o[(size_t)u * s->dv + j] = (float)o[j];
     if (x->X_out) memcpy(x->X_out + (size_t)u * n, S, n * sizeof(double));
     /* Table C2 steps 4 and 6: row factors, codes, pack. */
@@ -431,7 +433,7 @@ int oracle_step(int B, int hv, int hk, int dk, int dv, int n8,
     step_ctx x = {{hv, hk, dk, dv, n8}, pool8, pool4, r, c, perm, q, k, v,
                   alpha, beta, pool8_out, pool4_out, r_out, o, X_out, NULL};
     if (check_shape(&x.s)) return -1;
-    for_units((long)B * hv, nthreads, step_unit, &x);
+    orc_for_units((long)B * hv, nthreads, step_unit, &x);
     return 0;
 }
 
@@ -446,7 +448,7 @@ int oracle_step_gated(int B, int hv, int hk, int dk, int dv, int n8,
     step_ctx x = {{hv, hk, dk, dv, n8}, pool8, pool4, r, c, perm, q, k, v,
                   NULL, beta, pool8_out, pool4_out, r_out, o, X_out, gate};
     if (check_shape(&x.s) || !gate) return -1;
-    for_units((long)B * hv, nthreads, step_unit, &x);
+    orc_for_units((long)B * hv, nthreads, step_unit, &x);
     return 0;
 }
 
@@ -472,7 +474,7 @@ static void fp_unit(void *vctx, long u) {
         k[i] = (double)x->k[((size_t)b * s->hk + hk) * s->dk + i];
     }
     for (int j = 0; j < s->dv; ++j) v[j] = (double)x->v[(size_t)u * s->dv + j];
-    unit_update(s->dk, s->dv, x->S + (size_t)u * s->dk * s->dv, q, k, v, x->alpha, x->gate,
+    orc_unit_update(s->dk, s->dv, x->S + (size_t)u * s->dk * s->dv, q, k, v, x->alpha, x->gate,
                 u, (double)x->beta[u], x->o + (size_t)u * s->dv);
     free(q);
     free(k);
@@ -488,7 +490,7 @@ int oracle_fp_step(int B, int hv, int hk, int dk, int dv, double *S,
                    int nthreads) {
     fp_ctx x = {{hv, hk, dk, dv, 0}, S, q, k, v, alpha, beta, o, NULL};
     if (check_shape(&x.s)) return -1;
-    for_units((long)B * hv, nthreads, fp_unit, &x);
+    orc_for_units((long)B * hv, nthreads, fp_unit, &x);
     return 0;
 }
 
@@ -499,7 +501,7 @@ int oracle_fp_step_gated(int B, int hv, int hk, int dk, int dv, double *S,
                          int nthreads) {
     fp_ctx x = {{hv, hk, dk, dv, 0}, S, q, k, v, NULL, beta, o, gate};
     if (check_shape(&x.s) || !gate) return -1;
-    for_units((long)B * hv, nthreads, fp_unit, &x);
+    orc_for_units((long)B * hv, nthreads, fp_unit, &x);
     return 0;
 }
 
@@ -532,7 +534,7 @@ int oracle_dequant_cs(int B, int hv, int dk, int dv, int n8, const int8_t *pool8
                       const int32_t *perm, double *S, int nthreads) {
     dequant_cs_ctx x = {{hv, 1, dk, dv, n8}, pool8, pool4, r, cs, perm, S};
     if (check_shape(&x.s)) return -1;
-    for_units((long)B * hv, nthreads, dequant_cs_unit, &x);
+    orc_for_units((long)B * hv, nthreads, dequant_cs_unit, &x);
     return 0;
 }
 
@@ -574,7 +576,7 @@ int oracle_pack_refit(int B, int hv, int dk, int dv, int n8, const float *S,
                       int nthreads) {
     pack_refit_ctx x = {{hv, 1, dk, dv, n8}, S, c0, perm, w2, pool8, pool4, r, cs};
     if (check_shape(&x.s)) return -1;
-    for_units((long)B * hv, nthreads, pack_refit_unit, &x);
+    orc_for_units((long)B * hv, nthreads, pack_refit_unit, &x);
     return 0;
 }
 
@@ -618,7 +620,7 @@ static void step_refit_unit(void *vctx, long u) {
     }
     for (int j = 0; j < s->dv; ++j) v[j] = (double)x->v[(size_t)u * s->dv + j];
     /* Table C2 steps 2-3. */
-    unit_update(s->dk, s->dv, S, q, k, v, x->alpha, x->gate, u, (double)x->beta[u], o);
+    orc_unit_update(s->dk, s->dv, S, q, k, v, x->alpha, x->gate, u, (double)x->beta[u], o);
     for (int j = 0; j < s->dv; ++j) x->o[(size_t)u * s->dv + j] = (float)o[j];
     if (x->X_out) memcpy(x->X_out + (size_t)u * n, S, n * sizeof(double));
     /* Table C2 step 4: row factors and codes against the current column
@@ -648,7 +650,7 @@ int oracle_step_refit(int B, int hv, int hk, int dk, int dv, int n8,
     step_refit_ctx x = {{hv, hk, dk, dv, n8}, pool8, pool4, r, cs, perm, w2, q, k, v,
                         alpha, beta, pool8_out, pool4_out, r_out, cs_out, o, X_out, NULL};
     if (check_shape(&x.s)) return -1;
-    for_units((long)B * hv, nthreads, step_refit_unit, &x);
+    orc_for_units((long)B * hv, nthreads, step_refit_unit, &x);
     return 0;
 }
 
@@ -663,7 +665,7 @@ int oracle_step_refit_gated(int B, int hv, int hk, int dk, int dv, int n8,
     step_refit_ctx x = {{hv, hk, dk, dv, n8}, pool8, pool4, r, cs, perm, w2, q, k, v,
                         NULL, beta, pool8_out, pool4_out, r_out, cs_out, o, X_out, gate};
     if (check_shape(&x.s) || !gate) return -1;
-    for_units((long)B * hv, nthreads, step_refit_unit, &x);
+    orc_for_units((long)B * hv, nthreads, step_refit_unit, &x);
     return 0;
 }
 

@@ -12,10 +12,12 @@ import pytest
 
 import oracle as oracle_pkg
 from tests import test_oracle_pins as pins
+from tests import test_oracle_alloc_pins as apins
 from tests import test_oracle_gate_pins as gpins
 from tests import test_oracle_refit_pins as rpins
 
 SRC = Path(oracle_pkg.__file__).resolve().parent / "stq_oracle.c"
+ALLOC_SRC = Path(oracle_pkg.__file__).resolve().parent / "stq_alloc_oracle.c"
 
 # (name, text in the oracle source, replacement)
 MUTANTS = [
@@ -123,5 +125,68 @@ def test_pins_catch_planted_mistake(tmp_path, name, old, new):
         except AssertionError:
             caught.append(fn.__name__)
         except (ValueError, FloatingPointError, OverflowError):
+            caught.append(fn.__name__)
+    assert caught, f"no pin caught the planted mistake: {name}"
+
+
+# mistakes planted in the ragged-format oracle (stq_alloc_oracle.c)
+ALLOC_MUTANTS = [
+    ("6-bit high field position", "int hi = (row[d / 2 + j / 4] >> (2 * (j % 4))) & 0x3;",
+     "int hi = (row[d / 2 + j / 4] >> (j % 4)) & 0x3;"),
+    ("6-bit sign threshold", "return u >= 32 ? u - 64 : u;", "return u >= 31 ? u - 64 : u;"),
+    ("2-bit code not sign-extended", "return u >= 2 ? u - 4 : u;", "return u;"),
+    ("binary16 ties away from zero", "double n = oracle_rhe(ldexp(a, -qe));",
+     "double n = floor(ldexp(a, -qe) + 0.5);"),
+    ("binary16 subnormal quantum", "if (qe < -24) qe = -24;", "if (qe < -25) qe = -25;"),
+    ("pivot row keeps a row factor", "r_out[p] = 0.0f;", "r_out[p] = 1.0f;"),
+    ("q_b of the 2-bit rows", "static int qmax_of(int k) { return (1 << (kBits[k] - 1)) - 1; }",
+     "static int qmax_of(int k) { return k == 4 ? 2 : (1 << (kBits[k] - 1)) - 1; }"),
+    ("6-bit row size", "case 2: return 3 * d / 4;", "case 2: return d / 2 + d / 8;"),
+    ("segment not padded", "L->seg = (off + 15) / 16 * 16;", "L->seg = off;"),
+    ("lifetime without the square", "acc += exp(2.0 * (double)j * ell);",
+     "acc += exp((double)j * ell);"),
+    ("pivot score at 8 bits", "pv[u].score = Lw[u] * (dist[(size_t)u * NCLS + knom]",
+     "pv[u].score = Lw[u] * (dist[(size_t)u * NCLS + 1]"),
+    ("segments cheapest saving first", "if (x->slope > y->slope) return -1;\n    if (x->slope < y->slope) return 1;",
+     "if (x->slope > y->slope) return 1;\n    if (x->slope < y->slope) return -1;"),
+    ("budget counts pivots", "long budget = (long)nominal * n_int;", "long budget = (long)nominal * N;"),
+    ("FP16 distortion from fp32 rounding",
+     "double y = oracle_f16_to_double(oracle_f16_from_double(row[j]));",
+     "double y = (double)(float)row[j];"),
+]
+
+
+def _alloc_pin_cases():
+    return [
+        (apins.test_f16_matches_numpy, {}),
+        (apins.test_layout_golden_d16, {}),
+        (apins.test_two_class_layout_equals_mixed_format, {"d": 16, "n8": 8}),
+        (apins.test_round_trip_every_class, {"d": 16}),
+        (apins.test_pack_error_within_half_step, {}),
+        (apins.test_step_fixed_point_with_pivots, {"gated": False}),
+        (apins.test_step_delta_write_closed_form, {}),
+        (apins.test_step_refit_excludes_pivots_and_matches_pack, {}),
+        (apins.test_distortion_pins, {}),
+        (apins.test_lifetime_closed_form, {}),
+        (apins.test_assignment_optimal_on_convex_instances, {"seed": 0}),
+        (apins.test_assignment_optimal_on_convex_instances, {"seed": 3}),
+        (apins.test_assignment_budget_pivots_and_layout, {}),
+        (apins.test_pivot_ranking_uses_the_nominal_width, {}),
+    ]
+
+
+@pytest.mark.parametrize("name,old,new", ALLOC_MUTANTS, ids=[m[0] for m in ALLOC_MUTANTS])
+def test_alloc_pins_catch_planted_mistake(tmp_path, name, old, new):
+    src = ALLOC_SRC.read_text()
+    assert src.count(old) >= 1, f"mutation site missing: {name}"
+    msrc = tmp_path / "alloc_mutant.c"
+    msrc.write_text(src.replace(old, new))
+    lib = oracle_pkg.compile_oracle(SRC, tmp_path / "libmutant.so", alloc_src=msrc)
+    mut = oracle_pkg.Oracle(lib)
+    caught = []
+    for fn, kw in _alloc_pin_cases():
+        try:
+            fn(mut, **kw)
+        except (AssertionError, ValueError, FloatingPointError, OverflowError):
             caught.append(fn.__name__)
     assert caught, f"no pin caught the planted mistake: {name}"
