@@ -73,9 +73,16 @@ typedef enum {
     STQ_FMT_INT8ROW = 1, /* uniform symmetric rowwise-absmax INT8: n8 = d_k,
                             c = 1, identity row order (Sec. 5.1 baseline) */
     STQ_FMT_FP32 = 2,    /* unquantized fp32 state (the FP32-state baseline) */
-    STQ_FMT_REFIT = 3    /* MIXED48 codes and row factors with column factors
+    STQ_FMT_REFIT = 3,   /* MIXED48 codes and row factors with column factors
                             kept per state and refit at every step (App. C.1,
                             Table C2 step 5); see "Online column refit" */
+    STQ_FMT_ALLOC = 4,   /* ragged row classes per head: FP16 pivot rows and
+                            8-, 6-, 4-, 2-bit rows chosen by the lifetime-aware
+                            assignment (App. C.2, Table C2); fixed per-head c;
+                            see "Ragged row classes" */
+    STQ_FMT_ALLOC_REFIT = 5 /* ALLOC with per-state column factors refit over
+                            the non-pivot integer rows (App. C.1, Table C2
+                            step 5) */
 } stq_format;
 
 typedef enum { STQ_F32 = 0, STQ_BF16 = 1 } stq_dtype;
@@ -85,9 +92,14 @@ typedef enum { STQ_F32 = 0, STQ_BF16 = 1 } stq_dtype;
 #define STQ_CAL_COLS 2u     /* fold records into the per-column absmax */
 #define STQ_CAL_ROWS 4u     /* fold records into the per-row sum of squares */
 #define STQ_CAL_FINALIZE 8u /* set c and perm from the statistics */
+#define STQ_CAL_DIST 16u    /* ALLOC formats: fold records into the per-row
+                               candidate distortions (against the current c) */
 
 /* Geometry.  Supported: d_k == d_v in {16, 32, 64, 128}; 0 <= n8 <= d_k
- * (MIXED48; INT8ROW forces n8 = d_k); n_heads_v % n_heads_k == 0. */
+ * (MIXED48; INT8ROW forces n8 = d_k); n_heads_v % n_heads_k == 0.
+ * ALLOC formats: n8 = 0, nominal_bits in {2, 4, 6, 8} (the integer budget
+ * per value), 0 <= n_pivot <= n_heads_v * d_k (FP16 pivot rows per slot);
+ * every other format: nominal_bits = n_pivot = 0. */
 typedef struct {
     int32_t n_slots;
     int32_t n_heads_v;
@@ -96,6 +108,8 @@ typedef struct {
     int32_t d_v;
     int32_t n8;  /* 8-bit rows per head (same for every head) */
     int32_t fmt; /* stq_format */
+    int32_t nominal_bits;
+    int32_t n_pivot;
 } stq_desc;
 
 /* A state carved out of one caller buffer by stq_alloc_state.  Plain device
@@ -116,6 +130,12 @@ typedef struct {
     float *w2;          /* [Hv][dk]  REFIT: squared row-impact weights,
                            logical rows (1 until calibrated) */
     double *impact;     /* [Hv][dk]  REFIT calibration: accumulated row impact */
+    int32_t *layout;    /* [Hv][8]  ALLOC: class counts [0..4], segment offset
+                           [5] and segment bytes [6] of each head */
+    double *dist;       /* [Hv][dk][5]  ALLOC calibration: candidate distortions */
+    double *logret;     /* [Hv][dk]  ALLOC calibration: summed log retention */
+    double *nret;       /* [Hv]  ALLOC calibration: retention samples */
+    int64_t slot_bytes; /* ALLOC: bytes of one slot of the byte pool */
     int32_t calibrated; /* host flag: c and perm hold a calibration */
     int32_t reserved;
 } stq_state;
@@ -133,6 +153,32 @@ typedef struct {
  * stored state is (z', r', c').  w2 are squared row-impact weights
  * (stq_calibrate_impact), 1 until calibrated.  Packing a state (prefill
  * boundary) starts from the calibrated per-head c and refits the same way. */
+
+/* Ragged row classes (formats STQ_FMT_ALLOC and STQ_FMT_ALLOC_REFIT; the
+ * paper's FP16 pivots and lifetime-aware bit allocation, App. C.2 Table C1,
+ * App. C.3 Table C2, App. A.3).  Each head's physical rows are sorted into
+ * classes k = 0..4: FP16 pivot rows, then 8-, 6-, 4- and 2-bit rows
+ * (q_b = 127, 31, 7, 1), each class in ascending logical row; layout[h]
+ * holds the five counts.  pool8 is a byte pool [n_slots][slot_bytes]; head
+ * h's rows occupy bytes [layout[h][5], layout[h][5] + layout[h][6]) of a
+ * slot: class 0 rows take 2 d bytes (binary16 values, little endian), class
+ * 1 d bytes (int8), class 2 3d/4 bytes (the low four bits of column j in
+ * nibble j of the first d/2 bytes, even column in the low nibble, the top
+ * two bits in bits 2(j%4) of byte d/2 + j/4), class 3 d/2 bytes (nibbles),
+ * class 4 d/4 bytes (column j in bits 2(j%4) of byte j/4); codes are two's
+ * complement; segments are padded to 16 bytes.
+ *   slot_bytes = round16(nominal_bits (Hv d - n_pivot) d / 8
+ *                        + 2 d n_pivot + 16 Hv)
+ * holds any assignment that keeps the integer budget.  Integer rows follow
+ * the MIXED48 rules with their own q_b (r from the absmax, codes against
+ * the stored r); a pivot row stores X rounded to nearest-even binary16,
+ * saturated at +-65504, has r = 0 and no column factor, and does not enter
+ * the column refit of ALLOC_REFIT.
+ * Calibration: stq_calibrate with RESET, COLS over the records, FINALIZE
+ * (sets c only), then DIST over records (the candidate distortions against
+ * that c); stq_calibrate_retention over the gates of the calibration steps;
+ * then stq_allocate chooses pivots and widths and writes layout and perm.
+ * stq_set_alloc_layout installs a layout chosen elsewhere. */
 
 /* Bytes of device memory a state with this geometry needs (host arithmetic
  * only, no device call); 0 if the descriptor is invalid or unsupported. */
@@ -192,6 +238,45 @@ stq_status stq_calibrate_impact(stq_state *st, const void *q, const void *k,
 stq_status stq_calibrate_impact_gated(stq_state *st, const void *q, const void *k,
                                       int32_t dtype, const float *gate, const float *beta,
                                       int32_t B, uint32_t flags, stq_stream_t stream);
+
+/* Mean log retention for the lifetime weights of the ALLOC formats (App. A.3):
+ * logret[h][i] += sum_b log(retention), nret[h] += B, where the retention of
+ * row i is alpha[b][h] (scalar gate, [B][Hv] fp32) or gate[b][h][i] (row gate,
+ * [B][Hv][dk] fp32, logical rows); exactly one of alpha and gate is given when
+ * B > 0.  STQ_CAL_RESET zeroes the sums first (the only flag).
+ * Errors: STQ_E_ARG (format not ALLOC or ALLOC_REFIT, pointers, flags),
+ * STQ_E_SHAPE (B < 0), STQ_E_DEVICE. */
+stq_status stq_calibrate_retention(stq_state *st, const float *alpha, const float *gate,
+                                   int32_t B, uint32_t flags, stq_stream_t stream);
+
+/* Lifetime-aware assignment of an ALLOC state (App. C.2 "KDA calibration" and
+ * "Allocation optimizers"; App. A.3):
+ *   L_u = 1 + sum_{j=1}^{horizon-1} exp(2 j logret_u / nret),
+ *   pivots: the desc.n_pivot rows of largest L_u (d_u(nominal) - d_u(FP16))
+ *   over all heads (ties to the lower h * dk + i);
+ *   every other row starts at the smallest candidate width; on the lower
+ *   convex hull of its points (b, L_u d_u(b)) the hull steps of all rows are
+ *   taken in order of decreasing distortion saved per bit (ties: lower row,
+ *   then lower width) while sum of widths <= nominal_bits * (non-pivot rows);
+ *   a row whose next step does not fit keeps its width (the repair).
+ * candidates: bit k set for class k (1: 8, 2: 6, 3: 4, 4: 2 bits); 0 picks
+ * {8, 6, 4, 2} for nominal_bits <= 4 and {8, 6, 4} otherwise (Table C1).
+ * Writes layout and perm and marks the state calibrated; c is left as set by
+ * FINALIZE.  Synchronises the stream (reads the statistics to the host).
+ * Errors: STQ_E_ARG (format, horizon < 1, bad candidates, nominal width not
+ * a candidate, infeasible budget), STQ_E_STATE (no retention samples),
+ * STQ_E_DEVICE. */
+stq_status stq_allocate(stq_state *st, int32_t horizon, uint32_t candidates,
+                        stq_stream_t stream);
+
+/* Install a ragged layout chosen elsewhere: counts [Hv][5] (HOST memory, each
+ * head's counts >= 0 and summing to dk), c [Hv][dv] and perm [Hv][dk] (device
+ * memory, as stq_set_calibration).  Marks the state calibrated and
+ * invalidates packed contents.  Synchronises the stream.
+ * Errors: STQ_E_ARG (format not ALLOC or ALLOC_REFIT, pointers, counts),
+ * STQ_E_SPACE (the segments do not fit slot_bytes), STQ_E_DEVICE. */
+stq_status stq_set_alloc_layout(stq_state *st, const int32_t *counts, const float *c,
+                                const int32_t *perm, stq_stream_t stream);
 
 /* Install a calibration computed elsewhere: copies c [Hv][dv] (each > 0) and
  * perm [Hv][dk] (a permutation of 0..dk-1 per head) from device memory and
@@ -281,7 +366,8 @@ const char *stq_status_str(int32_t status);
 
 /* Library ABI version (bumped on any change to the declarations above):
  * 2 since the REFIT format and its state fields; 3 since the per-key-row
- * gate entry points. */
+ * gate entry points; 4 since the ALLOC formats (descriptor and state fields,
+ * retention and assignment entry points). */
 int32_t stq_abi_version(void);
 
 #ifdef __cplusplus

@@ -326,7 +326,7 @@ __global__ __launch_bounds__(D) void calib_fold_kernel(CalibArgs a, int fold, in
         for (int i = 0; i < j; ++i) before += 1 - s_sel[i];
         pos = a.n8 + before;
     }
-    a.perm[static_cast<size_t>(h) * D + pos] = j;
+    if (a.perm) a.perm[static_cast<size_t>(h) * D + pos] = j; // no perm: column factors only
 }
 
 __global__ void fill_u32_kernel(uint32_t *dst, size_t n, uint32_t value) {

@@ -5,6 +5,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <vector>
 
 #include "stq_internal.h"
 
@@ -22,25 +23,104 @@ bool supported_d(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; 
 
 struct Layout {
     size_t pool8, pool4, r, c, perm, colmax, rowscore, colpart, rowpart, s32, cs, w2, impact,
-        total;
+        layout, dist, logret, nret, total;
+    int64_t slot_bytes;
 };
 
-bool calibrated_format(int32_t fmt) { return fmt == STQ_FMT_MIXED48 || fmt == STQ_FMT_REFIT; }
+bool alloc_format(int32_t fmt) { return fmt == STQ_FMT_ALLOC || fmt == STQ_FMT_ALLOC_REFIT; }
+bool refit_format(int32_t fmt) { return fmt == STQ_FMT_REFIT || fmt == STQ_FMT_ALLOC_REFIT; }
+bool calibrated_format(int32_t fmt) {
+    return fmt == STQ_FMT_MIXED48 || fmt == STQ_FMT_REFIT || alloc_format(fmt);
+}
+
+// Row bytes of class k at head size D (FP16, 8, 6, 4, 2 bits).
+int64_t class_row_bytes(int k, int64_t D) {
+    switch (k) {
+    case 0: return 2 * D;
+    case 1: return D;
+    case 2: return 3 * D / 4;
+    case 3: return D / 2;
+    default: return D / 4;
+    }
+}
+
+int class_of_width(int bits) {
+    switch (bits) {
+    case 8: return 1;
+    case 6: return 2;
+    case 4: return 3;
+    case 2: return 4;
+    default: return -1;
+    }
+}
+
+// Bytes of one slot of an ALLOC byte pool: room for any assignment within
+// the integer budget, the pivots and the per-head padding.
+int64_t alloc_slot_bytes(const stq_desc *d) {
+    const int64_t H = d->n_heads_v, D = d->d_k, P = d->n_pivot, b = d->nominal_bits;
+    const int64_t bytes = b * (H * D - P) * D / 8 + 2 * D * P + 16 * H;
+    return (bytes + 15) / 16 * 16;
+}
+
+// Layout table rows from class counts [Hv][5]; false if a head's counts are
+// invalid or the segments do not fit slot_bytes (sets *space).
+bool build_layout(const stq_desc *d, int64_t slot_bytes, const int32_t *counts, int32_t *table,
+                  bool *space) {
+    const int H = d->n_heads_v, D = d->d_k;
+    int64_t off = 0;
+    *space = false;
+    for (int h = 0; h < H; ++h) {
+        int64_t sum = 0, seg = 0;
+        for (int k = 0; k < stq::kNumClasses; ++k) {
+            const int32_t n = counts[h * stq::kNumClasses + k];
+            if (n < 0) return false;
+            sum += n;
+            seg += n * class_row_bytes(k, D);
+        }
+        if (sum != D) return false;
+        seg = (seg + 15) / 16 * 16;
+        int32_t *row = table + static_cast<size_t>(h) * stq::kLayoutStride;
+        for (int t = 0; t < stq::kLayoutStride; ++t) row[t] = 0;
+        for (int k = 0; k < stq::kNumClasses; ++k) row[k] = counts[h * stq::kNumClasses + k];
+        row[stq::kLayoutSegOff] = static_cast<int32_t>(off);
+        row[stq::kLayoutSegBytes] = static_cast<int32_t>(seg);
+        off += seg;
+    }
+    if (off > slot_bytes) {
+        *space = true;
+        return false;
+    }
+    return true;
+}
 
 // Validates a descriptor; fills byte sizes of each region (0 = absent).
 stq_status describe(const stq_desc *d, Layout *L) {
     if (!d) return STQ_E_ARG;
-    if (d->fmt < STQ_FMT_MIXED48 || d->fmt > STQ_FMT_REFIT) return STQ_E_ARG;
+    if (d->fmt < STQ_FMT_MIXED48 || d->fmt > STQ_FMT_ALLOC_REFIT) return STQ_E_ARG;
     if (d->n_slots < 1 || d->n_heads_v < 1 || d->n_heads_k < 1) return STQ_E_SHAPE;
     if (d->n_heads_v % d->n_heads_k != 0) return STQ_E_SHAPE;
     if (d->d_k < 1 || d->d_v < 1) return STQ_E_SHAPE;
     if (d->d_k != d->d_v || !supported_d(d->d_k)) return STQ_E_UNSUPPORTED;
     if (calibrated_format(d->fmt) && (d->n8 < 0 || d->n8 > d->d_k)) return STQ_E_SHAPE;
     if (d->fmt == STQ_FMT_INT8ROW && d->n8 != d->d_k) return STQ_E_SHAPE;
+    if (alloc_format(d->fmt)) {
+        if (d->n8 != 0 || class_of_width(d->nominal_bits) < 0) return STQ_E_SHAPE;
+        if (d->n_pivot < 0 || d->n_pivot > d->n_heads_v * d->d_k) return STQ_E_SHAPE;
+    } else if (d->nominal_bits != 0 || d->n_pivot != 0) {
+        return STQ_E_SHAPE;
+    }
     const size_t S = static_cast<size_t>(d->n_slots), H = static_cast<size_t>(d->n_heads_v);
     const size_t D = static_cast<size_t>(d->d_k);
     std::memset(L, 0, sizeof(*L));
-    if (d->fmt != STQ_FMT_FP32) {
+    if (alloc_format(d->fmt)) {
+        L->slot_bytes = alloc_slot_bytes(d);
+        L->pool8 = S * static_cast<size_t>(L->slot_bytes);
+        L->r = S * H * D * sizeof(float);
+        L->layout = H * stq::kLayoutStride * sizeof(int32_t);
+        L->dist = H * D * stq::kNumClasses * sizeof(double);
+        L->logret = H * D * sizeof(double);
+        L->nret = H * sizeof(double);
+    } else if (d->fmt != STQ_FMT_FP32) {
         const size_t n8 = static_cast<size_t>(d->n8);
         L->pool8 = S * H * n8 * D;
         L->pool4 = S * H * (D - n8) * (D / 2);
@@ -56,7 +136,7 @@ stq_status describe(const stq_desc *d, Layout *L) {
         L->colpart = H * stq::kCalChunks * D * sizeof(float);
         L->rowpart = H * stq::kCalChunks * D * sizeof(double);
     }
-    if (d->fmt == STQ_FMT_REFIT) {
+    if (refit_format(d->fmt)) {
         L->cs = S * H * D * sizeof(float);
         L->w2 = H * D * sizeof(float);
         L->impact = H * D * sizeof(double);
@@ -64,7 +144,8 @@ stq_status describe(const stq_desc *d, Layout *L) {
     L->total = round_up(L->pool8) + round_up(L->pool4) + round_up(L->r) + round_up(L->c) +
                round_up(L->perm) + round_up(L->colmax) + round_up(L->rowscore) +
                round_up(L->colpart) + round_up(L->rowpart) + round_up(L->s32) +
-               round_up(L->cs) + round_up(L->w2) + round_up(L->impact);
+               round_up(L->cs) + round_up(L->w2) + round_up(L->impact) + round_up(L->layout) +
+               round_up(L->dist) + round_up(L->logret) + round_up(L->nret);
     return STQ_OK;
 }
 
@@ -84,8 +165,11 @@ stq_status check_state(const stq_state *st) {
     if (calibrated_format(st->desc.fmt) &&
         (!st->colmax || !st->rowscore || !st->cal_colpart || !st->cal_rowpart))
         return STQ_E_ARG;
-    if (st->desc.fmt == STQ_FMT_REFIT && (!st->cs || !st->w2 || !st->impact ||
-                                          !aligned(st->cs, 16) || !aligned(st->w2, 16)))
+    if (refit_format(st->desc.fmt) && (!st->cs || !st->w2 || !st->impact ||
+                                       !aligned(st->cs, 16) || !aligned(st->w2, 16)))
+        return STQ_E_ARG;
+    if (alloc_format(st->desc.fmt) &&
+        (!st->layout || !st->dist || !st->logret || !st->nret || st->slot_bytes != L.slot_bytes))
         return STQ_E_ARG;
     return STQ_OK;
 }
@@ -96,7 +180,7 @@ stq_status dev(hipError_t e) { return e == hipSuccess ? STQ_OK : STQ_E_DEVICE; }
 
 extern "C" {
 
-int32_t stq_abi_version(void) { return 3; }
+int32_t stq_abi_version(void) { return 4; }
 
 const char *stq_status_str(int32_t s) {
     switch (s) {
@@ -148,6 +232,11 @@ stq_status stq_alloc_state(const stq_desc *desc, void *devp, size_t bytes, stq_s
     st.cs = static_cast<float *>(take(L.cs));
     st.w2 = static_cast<float *>(take(L.w2));
     st.impact = static_cast<double *>(take(L.impact));
+    st.layout = static_cast<int32_t *>(take(L.layout));
+    st.dist = static_cast<double *>(take(L.dist));
+    st.logret = static_cast<double *>(take(L.logret));
+    st.nret = static_cast<double *>(take(L.nret));
+    st.slot_bytes = L.slot_bytes;
     st.calibrated = calibrated_format(desc->fmt) ? 0 : 1;
 
     const int D = desc->d_k;
@@ -166,6 +255,15 @@ stq_status stq_alloc_state(const stq_desc *desc, void *devp, size_t bytes, stq_s
     if (L.cs) run(stq::launch_fill_u32(reinterpret_cast<uint32_t *>(st.cs), L.cs / 4, kOneBits, s));
     if (L.w2) run(stq::launch_fill_u32(reinterpret_cast<uint32_t *>(st.w2), L.w2 / 4, kOneBits, s));
     if (L.impact) run(stq::launch_fill_u64(reinterpret_cast<uint64_t *>(st.impact), L.impact / 8, 0u, s));
+    if (L.layout) {
+        // every row at the nominal width, no pivots, until a layout is chosen
+        const int k = class_of_width(desc->nominal_bits);
+        const int64_t seg = (D * class_row_bytes(k, D) + 15) / 16 * 16;
+        run(stq::launch_alloc_init_layout(st.layout, desc->n_heads_v, D, k, static_cast<int>(seg), s));
+        run(stq::launch_fill_u64(reinterpret_cast<uint64_t *>(st.dist), L.dist / 8, 0u, s));
+        run(stq::launch_fill_u64(reinterpret_cast<uint64_t *>(st.logret), L.logret / 8, 0u, s));
+        run(stq::launch_fill_u64(reinterpret_cast<uint64_t *>(st.nret), L.nret / 8, 0u, s));
+    }
     if (he != hipSuccess) return STQ_E_DEVICE;
     *out = st;
     return STQ_OK;
@@ -176,9 +274,12 @@ stq_status stq_calibrate(stq_state *st, const float *records, int64_t n_rec, uin
     stq_status e = check_state(st);
     if (e != STQ_OK) return e;
     if (!calibrated_format(st->desc.fmt)) return STQ_E_ARG;
-    if (flags & ~(STQ_CAL_RESET | STQ_CAL_COLS | STQ_CAL_ROWS | STQ_CAL_FINALIZE)) return STQ_E_ARG;
+    const bool ragged = alloc_format(st->desc.fmt);
+    const uint32_t allowed = ragged ? (STQ_CAL_RESET | STQ_CAL_COLS | STQ_CAL_FINALIZE | STQ_CAL_DIST)
+                                    : (STQ_CAL_RESET | STQ_CAL_COLS | STQ_CAL_ROWS | STQ_CAL_FINALIZE);
+    if (flags & ~allowed) return STQ_E_ARG;
     if (n_rec < 0) return STQ_E_SHAPE;
-    const bool accumulate = (flags & (STQ_CAL_COLS | STQ_CAL_ROWS)) != 0;
+    const bool accumulate = (flags & (STQ_CAL_COLS | STQ_CAL_ROWS | STQ_CAL_DIST)) != 0;
     if (accumulate && n_rec > 0 && (!records || !aligned(records, 16))) return STQ_E_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int D = st->desc.d_k, H = st->desc.n_heads_v;
@@ -194,7 +295,7 @@ stq_status stq_calibrate(stq_state *st, const float *records, int64_t n_rec, uin
     a.colpart = st->cal_colpart;
     a.rowpart = st->cal_rowpart;
     a.c = st->c;
-    a.perm = st->perm;
+    a.perm = ragged ? nullptr : st->perm; // ragged: perm comes from stq_allocate
     if (flags & STQ_CAL_RESET) {
         if ((e = dev(stq::launch_fill_u32(reinterpret_cast<uint32_t *>(st->colmax),
                                           static_cast<size_t>(H) * D, 0u, s))) != STQ_OK)
@@ -202,12 +303,31 @@ stq_status stq_calibrate(stq_state *st, const float *records, int64_t n_rec, uin
         if ((e = dev(stq::launch_fill_u64(reinterpret_cast<uint64_t *>(st->rowscore),
                                           static_cast<size_t>(H) * D, 0u, s))) != STQ_OK)
             return e;
+        if (ragged) {
+            const size_t nd = static_cast<size_t>(H) * D;
+            if ((e = dev(stq::launch_fill_u64(reinterpret_cast<uint64_t *>(st->dist),
+                                              nd * stq::kNumClasses, 0u, s))) != STQ_OK ||
+                (e = dev(stq::launch_fill_u64(reinterpret_cast<uint64_t *>(st->logret), nd, 0u,
+                                              s))) != STQ_OK ||
+                (e = dev(stq::launch_fill_u64(reinterpret_cast<uint64_t *>(st->nret),
+                                              static_cast<size_t>(H), 0u, s))) != STQ_OK)
+                return e;
+        }
     }
-    if (accumulate && n_rec > 0)
+    if ((flags & (STQ_CAL_COLS | STQ_CAL_ROWS)) && n_rec > 0)
         if ((e = dev(stq::launch_calib_accumulate(D, a, s))) != STQ_OK) return e;
     if (flags & STQ_CAL_FINALIZE) {
         if ((e = dev(stq::launch_calib_finalize(D, a, s))) != STQ_OK) return e;
-        st->calibrated = 1;
+        if (!ragged) st->calibrated = 1; // ragged: stq_allocate completes it
+    }
+    if ((flags & STQ_CAL_DIST) && n_rec > 0) {
+        stq::AllocCalArgs ca{};
+        ca.records = records;
+        ca.n_rec = n_rec;
+        ca.Hv = H;
+        ca.c = st->c;
+        ca.dist = st->dist;
+        if ((e = dev(stq::launch_alloc_distortion(D, ca, s))) != STQ_OK) return e;
     }
     return STQ_OK;
 }
@@ -218,6 +338,7 @@ stq_status stq_set_calibration(stq_state *st, const float *c, const int32_t *per
     if (e != STQ_OK) return e;
     if (!calibrated_format(st->desc.fmt)) return STQ_E_ARG;
     if (!c || !perm || !aligned(c, 16) || !aligned(perm, 16)) return STQ_E_ARG;
+    if (alloc_format(st->desc.fmt)) return STQ_E_ARG; // use stq_set_alloc_layout
     hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t n = static_cast<size_t>(st->desc.n_heads_v) * st->desc.d_k * 4;
     if ((e = dev(stq::launch_copy_bytes(c, st->c, n, s))) != STQ_OK) return e;
@@ -233,7 +354,7 @@ stq_status calibrate_impact(stq_state *st, const void *q, const void *k, int32_t
                             uint32_t flags, stq_stream_t stream) {
     stq_status e = check_state(st);
     if (e != STQ_OK) return e;
-    if (st->desc.fmt != STQ_FMT_REFIT) return STQ_E_ARG;
+    if (!refit_format(st->desc.fmt)) return STQ_E_ARG;
     if (flags & ~(STQ_CAL_RESET | STQ_CAL_FINALIZE)) return STQ_E_ARG;
     if (B < 0) return STQ_E_SHAPE;
     if (dtype != STQ_F32 && dtype != STQ_BF16) return STQ_E_ARG;
@@ -292,7 +413,7 @@ stq_status batch_args(const stq_state *st, const int32_t *slots, int32_t B) {
 }
 
 stq::PackArgs pack_args(const stq_state *st, const int32_t *slots, int32_t B) {
-    stq::PackArgs a;
+    stq::PackArgs a{};
     a.pool8 = st->pool8;
     a.pool4 = st->pool4;
     a.r = st->r;
@@ -301,12 +422,14 @@ stq::PackArgs pack_args(const stq_state *st, const int32_t *slots, int32_t B) {
     a.slots = slots;
     a.S_in = nullptr;
     a.S_out = nullptr;
-    a.cs = st->desc.fmt == STQ_FMT_REFIT ? st->cs : nullptr;
-    a.w2 = st->desc.fmt == STQ_FMT_REFIT ? st->w2 : nullptr;
+    a.cs = refit_format(st->desc.fmt) ? st->cs : nullptr;
+    a.w2 = refit_format(st->desc.fmt) ? st->w2 : nullptr;
     a.B = B;
     a.Hv = st->desc.n_heads_v;
     a.n8 = st->desc.n8;
     a.n_slots = st->desc.n_slots;
+    a.layout = alloc_format(st->desc.fmt) ? st->layout : nullptr;
+    a.slot_bytes = st->slot_bytes;
     return a;
 }
 
@@ -322,6 +445,7 @@ stq_status stq_pack_state(const stq_state *st, const float *S, const int32_t *sl
     a.S_in = S;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (st->desc.fmt == STQ_FMT_FP32) return dev(stq::launch_copy_slots_fp32(st->desc.d_k, a, true, st->s32, s));
+    if (alloc_format(st->desc.fmt)) return dev(stq::launch_pack_alloc(st->desc.d_k, a, s));
     return dev(stq::launch_pack(st->desc.d_k, a, s));
 }
 
@@ -334,6 +458,7 @@ stq_status stq_dequant_state(const stq_state *st, const int32_t *slots, int32_t 
     a.S_out = S_out;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (st->desc.fmt == STQ_FMT_FP32) return dev(stq::launch_copy_slots_fp32(st->desc.d_k, a, false, st->s32, s));
+    if (alloc_format(st->desc.fmt)) return dev(stq::launch_dequant_alloc(st->desc.d_k, a, s));
     return dev(stq::launch_dequant(st->desc.d_k, a, s));
 }
 
@@ -341,7 +466,8 @@ namespace {
 
 bool same_desc(const stq_desc &x, const stq_desc &y) {
     return x.n_slots == y.n_slots && x.n_heads_v == y.n_heads_v && x.n_heads_k == y.n_heads_k &&
-           x.d_k == y.d_k && x.d_v == y.d_v && x.n8 == y.n8 && x.fmt == y.fmt;
+           x.d_k == y.d_k && x.d_v == y.d_v && x.n8 == y.n8 && x.fmt == y.fmt &&
+           x.nominal_bits == y.nominal_bits && x.n_pivot == y.n_pivot;
 }
 
 // [p, p + n) and [q, q + n) overlap without being the same range
@@ -368,14 +494,14 @@ stq_status decode(const stq_state *src, const stq_state *dst, const int32_t *slo
         !aligned(beta, 4) || !aligned(o, 4))
         return STQ_E_ARG;
     if (calibrated_format(src->desc.fmt) && !src->calibrated) return STQ_E_STATE;
-    const bool refit = src->desc.fmt == STQ_FMT_REFIT;
+    const bool refit = refit_format(src->desc.fmt);
     Layout L;
     describe(&src->desc, &L);
     if (partial_overlap(src->pool8, dst->pool8, L.pool8) || partial_overlap(src->pool4, dst->pool4, L.pool4) ||
         partial_overlap(src->r, dst->r, L.r) || partial_overlap(src->s32, dst->s32, L.s32) ||
         partial_overlap(src->cs, dst->cs, L.cs))
         return STQ_E_ARG;
-    stq::DecodeArgs a;
+    stq::DecodeArgs a{};
     a.pool8 = src->pool8;
     a.pool4 = src->pool4;
     a.r = src->r;
@@ -402,9 +528,12 @@ stq_status decode(const stq_state *src, const stq_state *dst, const int32_t *slo
     a.Hk = src->desc.n_heads_k;
     a.n8 = src->desc.n8;
     a.n_slots = src->desc.n_slots;
+    a.layout = alloc_format(src->desc.fmt) ? src->layout : nullptr;
+    a.slot_bytes = src->slot_bytes;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const bool bf16 = dtype == STQ_BF16;
     if (src->desc.fmt == STQ_FMT_FP32) return dev(stq::launch_decode_fp32(src->desc.d_k, bf16, a, s));
+    if (alloc_format(src->desc.fmt)) return dev(stq::launch_decode_alloc(src->desc.d_k, bf16, a, s));
     return dev(stq::launch_decode_mixed(src->desc.d_k, bf16, a, s));
 }
 
@@ -431,6 +560,101 @@ stq_status stq_decode_step_gated(const stq_state *src, const stq_state *dst, con
                                  stq_stream_t stream) {
     if (!src || !dst || !gate) return STQ_E_ARG;
     return decode(src, dst, slots, B, q, k, v, dtype, nullptr, gate, beta, o, stream);
+}
+
+stq_status stq_calibrate_retention(stq_state *st, const float *alpha, const float *gate,
+                                   int32_t B, uint32_t flags, stq_stream_t stream) {
+    stq_status e = check_state(st);
+    if (e != STQ_OK) return e;
+    if (!alloc_format(st->desc.fmt)) return STQ_E_ARG;
+    if (flags & ~STQ_CAL_RESET) return STQ_E_ARG;
+    if (B < 0) return STQ_E_SHAPE;
+    if (B > 0) {
+        if ((alpha == nullptr) == (gate == nullptr)) return STQ_E_ARG;
+        if (!aligned(alpha ? alpha : gate, 4)) return STQ_E_ARG;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int D = st->desc.d_k, H = st->desc.n_heads_v;
+    if (flags & STQ_CAL_RESET) {
+        if ((e = dev(stq::launch_fill_u64(reinterpret_cast<uint64_t *>(st->logret),
+                                          static_cast<size_t>(H) * D, 0u, s))) != STQ_OK ||
+            (e = dev(stq::launch_fill_u64(reinterpret_cast<uint64_t *>(st->nret),
+                                          static_cast<size_t>(H), 0u, s))) != STQ_OK)
+            return e;
+    }
+    if (B == 0) return STQ_OK;
+    stq::AllocCalArgs a{};
+    a.Hv = H;
+    a.alpha = alpha;
+    a.gate = gate;
+    a.B = B;
+    a.logret = st->logret;
+    a.nret = st->nret;
+    return dev(stq::launch_alloc_retention(D, a, s));
+}
+
+stq_status stq_allocate(stq_state *st, int32_t horizon, uint32_t candidates,
+                        stq_stream_t stream) {
+    stq_status e = check_state(st);
+    if (e != STQ_OK) return e;
+    if (!alloc_format(st->desc.fmt) || horizon < 1) return STQ_E_ARG;
+    const int nominal = st->desc.nominal_bits;
+    uint32_t mask = candidates;
+    if (mask == 0) mask = nominal <= 4 ? 0x1Eu : 0x0Eu; // {8,6,4,2} or {8,6,4}
+    if (mask & ~0x1Eu) return STQ_E_ARG;
+    if (!(mask & (1u << class_of_width(nominal)))) return STQ_E_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int D = st->desc.d_k, H = st->desc.n_heads_v;
+    const size_t nd = static_cast<size_t>(H) * D;
+    std::vector<double> dist(nd * stq::kNumClasses), logret(nd), nret(H);
+    if (hipMemcpyAsync(dist.data(), st->dist, dist.size() * sizeof(double), hipMemcpyDeviceToHost,
+                       s) != hipSuccess ||
+        hipMemcpyAsync(logret.data(), st->logret, nd * sizeof(double), hipMemcpyDeviceToHost, s) !=
+            hipSuccess ||
+        hipMemcpyAsync(nret.data(), st->nret, H * sizeof(double), hipMemcpyDeviceToHost, s) !=
+            hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return STQ_E_DEVICE;
+    if (!(nret[0] > 0.0)) return STQ_E_STATE;
+    std::vector<int32_t> counts(static_cast<size_t>(H) * stq::kNumClasses), perm(nd);
+    if (!stq::assign_rows(H, D, dist.data(), logret.data(), nret[0], horizon, mask, nominal,
+                          st->desc.n_pivot, counts.data(), perm.data()))
+        return STQ_E_ARG;
+    std::vector<int32_t> table(static_cast<size_t>(H) * stq::kLayoutStride);
+    bool space = false;
+    if (!build_layout(&st->desc, st->slot_bytes, counts.data(), table.data(), &space))
+        return space ? STQ_E_SPACE : STQ_E_ARG;
+    if (hipMemcpyAsync(st->layout, table.data(), table.size() * sizeof(int32_t),
+                       hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipMemcpyAsync(st->perm, perm.data(), perm.size() * sizeof(int32_t), hipMemcpyHostToDevice,
+                       s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return STQ_E_DEVICE;
+    st->calibrated = 1;
+    return STQ_OK;
+}
+
+stq_status stq_set_alloc_layout(stq_state *st, const int32_t *counts, const float *c,
+                                const int32_t *perm, stq_stream_t stream) {
+    stq_status e = check_state(st);
+    if (e != STQ_OK) return e;
+    if (!alloc_format(st->desc.fmt)) return STQ_E_ARG;
+    if (!counts || !c || !perm || !aligned(c, 16) || !aligned(perm, 16)) return STQ_E_ARG;
+    const int D = st->desc.d_k, H = st->desc.n_heads_v;
+    std::vector<int32_t> table(static_cast<size_t>(H) * stq::kLayoutStride);
+    bool space = false;
+    if (!build_layout(&st->desc, st->slot_bytes, counts, table.data(), &space))
+        return space ? STQ_E_SPACE : STQ_E_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t n = static_cast<size_t>(H) * D * 4;
+    if ((e = dev(stq::launch_copy_bytes(c, st->c, n, s))) != STQ_OK) return e;
+    if ((e = dev(stq::launch_copy_bytes(perm, st->perm, n, s))) != STQ_OK) return e;
+    if (hipMemcpyAsync(st->layout, table.data(), table.size() * sizeof(int32_t),
+                       hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return STQ_E_DEVICE;
+    st->calibrated = 1;
+    return STQ_OK;
 }
 
 stq_status stq_stream_copy(const void *src, void *dst, size_t bytes, stq_stream_t stream) {

@@ -32,6 +32,10 @@ struct DecodeArgs {
     float *o;             // [B][Hv][D]
     int32_t B, Hv, Hk, n8, n_slots;
     const float *gate;    // [B][Hv][D] per-key-row gate, logical rows, or null
+    // ragged row classes (ALLOC formats): pool8 / pool8_out are the byte
+    // pools [n_slots][slot_bytes]; layout [Hv][kLayoutStride]
+    const int32_t *layout;
+    int64_t slot_bytes;
 };
 
 // Pack / dequant of B slots.
@@ -48,6 +52,31 @@ struct PackArgs {
                        // (pack writes them, dequant reads them); else null
     const float *w2;   // REFIT: [Hv][D] squared row-impact weights
     int32_t B, Hv, n8, n_slots;
+    const int32_t *layout; // ALLOC formats: [Hv][kLayoutStride]; pool8 is the byte pool
+    int64_t slot_bytes;
+};
+
+// Ragged row classes (ALLOC formats).  Class k = 0..4: FP16 pivot rows and
+// 8-, 6-, 4-, 2-bit rows, stored per head in that physical order.  Layout
+// table per head: counts of the five classes, then the head's segment offset
+// within a slot and the segment size in bytes (a multiple of 16).
+constexpr int kNumClasses = 5;
+constexpr int kLayoutStride = 8;
+constexpr int kLayoutSegOff = 5;
+constexpr int kLayoutSegBytes = 6;
+
+// Offline calibration of the ALLOC formats.
+struct AllocCalArgs {
+    const float *records; // [n_rec][Hv][D][D] fp32 states, logical rows
+    int64_t n_rec;
+    int32_t Hv;
+    const float *c;       // [Hv][D] column factors the candidates are taken against
+    double *dist;         // [Hv][D][kNumClasses] accumulated candidate distortions
+    const float *alpha;   // retention: [B][Hv] scalar gate, or
+    const float *gate;    //            [B][Hv][D] row gate
+    int32_t B;
+    double *logret;       // [Hv][D] summed log retention
+    double *nret;         // [Hv] number of retention samples
 };
 
 // Row-impact calibration of the refit format.
@@ -71,7 +100,7 @@ struct CalibArgs {
     float *colpart;      // [Hv][chunks][D]
     double *rowpart;     // [Hv][chunks][D]
     float *c;            // [Hv][D]
-    int32_t *perm;       // [Hv][D]
+    int32_t *perm;       // [Hv][D], or null: finalize sets the column factors only
 };
 
 constexpr int kCalChunks = 64;
@@ -90,9 +119,24 @@ hipError_t launch_calib_accumulate(int D, const CalibArgs &a, hipStream_t s);
 hipError_t launch_calib_finalize(int D, const CalibArgs &a, hipStream_t s);
 hipError_t launch_impact_accumulate(int D, bool bf16, const ImpactArgs &a, hipStream_t s);
 hipError_t launch_impact_finalize(int D, const ImpactArgs &a, hipStream_t s);
+hipError_t launch_decode_alloc(int D, bool bf16, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_pack_alloc(int D, const PackArgs &a, hipStream_t s);
+hipError_t launch_dequant_alloc(int D, const PackArgs &a, hipStream_t s);
+hipError_t launch_alloc_distortion(int D, const AllocCalArgs &a, hipStream_t s);
+hipError_t launch_alloc_retention(int D, const AllocCalArgs &a, hipStream_t s);
+hipError_t launch_alloc_init_layout(int32_t *layout, int Hv, int D, int k, int seg_bytes,
+                                    hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *dst, size_t n, uint32_t value, hipStream_t s);
 hipError_t launch_fill_u64(uint64_t *dst, size_t n, uint64_t value, hipStream_t s);
 hipError_t launch_iota_rows(int32_t *perm, int rows, int D, hipStream_t s);
 hipError_t launch_copy_bytes(const void *src, void *dst, size_t bytes, hipStream_t s);
+
+// Host side of the lifetime-aware assignment (alloc_host.cpp).  Inputs on the
+// host: dist [Hv][D][5], logret [Hv][D], n (retention samples).  Outputs:
+// counts [Hv][5] and perm [Hv][D].  Returns false for an infeasible budget or
+// a nominal width outside the candidates.
+bool assign_rows(int Hv, int D, const double *dist, const double *logret, double n,
+                 int horizon, unsigned cand_mask, int nominal, int n_pivot, int32_t *counts,
+                 int32_t *perm);
 
 } // namespace stq

@@ -20,9 +20,12 @@ STQ_OK = 0
 STATUS_NAMES = {0: "STQ_OK", 1: "STQ_E_ARG", 2: "STQ_E_SHAPE", 3: "STQ_E_UNSUPPORTED",
                 4: "STQ_E_SPACE", 5: "STQ_E_STATE", 6: "STQ_E_DEVICE"}
 
-FMT_MIXED48, FMT_INT8ROW, FMT_FP32, FMT_REFIT = 0, 1, 2, 3
+FMT_MIXED48, FMT_INT8ROW, FMT_FP32, FMT_REFIT, FMT_ALLOC, FMT_ALLOC_REFIT = 0, 1, 2, 3, 4, 5
 F32, BF16 = 0, 1
-CAL_RESET, CAL_COLS, CAL_ROWS, CAL_FINALIZE = 1, 2, 4, 8
+CAL_RESET, CAL_COLS, CAL_ROWS, CAL_FINALIZE, CAL_DIST = 1, 2, 4, 8, 16
+# ragged row classes (ALLOC formats): FP16 pivots, 8, 6, 4, 2 bits
+CLASS_BITS = (16, 8, 6, 4, 2)
+LAYOUT_STRIDE = 8
 CAL_CHUNKS = 64
 
 
@@ -35,7 +38,8 @@ class StqError(RuntimeError):
 class Desc(ctypes.Structure):
     _fields_ = [("n_slots", ctypes.c_int32), ("n_heads_v", ctypes.c_int32),
                 ("n_heads_k", ctypes.c_int32), ("d_k", ctypes.c_int32),
-                ("d_v", ctypes.c_int32), ("n8", ctypes.c_int32), ("fmt", ctypes.c_int32)]
+                ("d_v", ctypes.c_int32), ("n8", ctypes.c_int32), ("fmt", ctypes.c_int32),
+                ("nominal_bits", ctypes.c_int32), ("n_pivot", ctypes.c_int32)]
 
 
 class CState(ctypes.Structure):
@@ -44,7 +48,9 @@ class CState(ctypes.Structure):
                 ("colmax", ctypes.c_void_p), ("rowscore", ctypes.c_void_p),
                 ("cal_colpart", ctypes.c_void_p), ("cal_rowpart", ctypes.c_void_p),
                 ("s32", ctypes.c_void_p), ("cs", ctypes.c_void_p), ("w2", ctypes.c_void_p),
-                ("impact", ctypes.c_void_p), ("calibrated", ctypes.c_int32),
+                ("impact", ctypes.c_void_p), ("layout", ctypes.c_void_p),
+                ("dist", ctypes.c_void_p), ("logret", ctypes.c_void_p), ("nret", ctypes.c_void_p),
+                ("slot_bytes", ctypes.c_int64), ("calibrated", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
 
 
@@ -52,7 +58,8 @@ _LIB = None
 EXPORTS = ("stq_state_bytes", "stq_alloc_state", "stq_calibrate", "stq_calibrate_impact",
            "stq_calibrate_impact_gated", "stq_set_calibration", "stq_pack_state",
            "stq_decode_step", "stq_decode_step_into", "stq_decode_step_gated",
-           "stq_dequant_state", "stq_stream_copy", "stq_status_str", "stq_abi_version")
+           "stq_dequant_state", "stq_stream_copy", "stq_status_str", "stq_abi_version",
+           "stq_calibrate_retention", "stq_allocate", "stq_set_alloc_layout")
 
 
 def _lib():
@@ -77,6 +84,9 @@ def _lib():
         lib.stq_decode_step_into.argtypes = [ctypes.POINTER(CState), ctypes.POINTER(CState), P,
                                              I32, P, P, P, I32, P, P, P, P]
         lib.stq_decode_step_gated.argtypes = lib.stq_decode_step_into.argtypes
+        lib.stq_calibrate_retention.argtypes = [ctypes.POINTER(CState), P, P, I32, U32, P]
+        lib.stq_allocate.argtypes = [ctypes.POINTER(CState), I32, U32, P]
+        lib.stq_set_alloc_layout.argtypes = [ctypes.POINTER(CState), P, P, P, P]
         lib.stq_dequant_state.argtypes = [ctypes.POINTER(CState), P, I32, P, P]
         lib.stq_stream_copy.argtypes = [P, P, SZ, P]
         lib.stq_status_str.argtypes = [I32]
@@ -85,7 +95,8 @@ def _lib():
         for name in ("stq_alloc_state", "stq_calibrate", "stq_calibrate_impact",
                      "stq_calibrate_impact_gated", "stq_set_calibration",
                      "stq_pack_state", "stq_decode_step", "stq_decode_step_into",
-                     "stq_decode_step_gated", "stq_dequant_state", "stq_stream_copy"):
+                     "stq_decode_step_gated", "stq_dequant_state", "stq_stream_copy",
+                     "stq_calibrate_retention", "stq_allocate", "stq_set_alloc_layout"):
             getattr(lib, name).restype = I32
         _LIB = lib
     return _LIB
@@ -128,8 +139,8 @@ def _in_dtype(q, k, v) -> int:
     return dt
 
 
-def state_bytes(n_slots, n_heads_v, n_heads_k, d, n8, fmt) -> int:
-    d_ = Desc(n_slots, n_heads_v, n_heads_k, d, d, n8, fmt)
+def state_bytes(n_slots, n_heads_v, n_heads_k, d, n8, fmt, nominal_bits=0, n_pivot=0) -> int:
+    d_ = Desc(n_slots, n_heads_v, n_heads_k, d, d, n8, fmt, nominal_bits, n_pivot)
     return int(_lib().stq_state_bytes(ctypes.byref(d_)))
 
 
@@ -141,6 +152,8 @@ class Geometry:
     d: int
     n8: int
     fmt: int = FMT_MIXED48
+    nominal_bits: int = 0  # ALLOC formats: integer budget per value
+    n_pivot: int = 0       # ALLOC formats: FP16 pivot rows per slot
 
 
 class State:
@@ -148,7 +161,8 @@ class State:
 
     def __init__(self, geo: Geometry, device="cuda", stream=None):
         self.geo = geo
-        self.desc = Desc(geo.n_slots, geo.n_heads_v, geo.n_heads_k, geo.d, geo.d, geo.n8, geo.fmt)
+        self.desc = Desc(geo.n_slots, geo.n_heads_v, geo.n_heads_k, geo.d, geo.d, geo.n8, geo.fmt,
+                         geo.nominal_bits, geo.n_pivot)
         nbytes = int(_lib().stq_state_bytes(ctypes.byref(self.desc)))
         if nbytes == 0:
             raise StqError(2, "stq_state_bytes (invalid or unsupported geometry)")
@@ -224,6 +238,59 @@ class State:
     def impact(self):
         g = self.geo
         return self._view("impact", torch.float64, (g.n_heads_v, g.d))
+
+    # -- ragged row classes (ALLOC formats) --
+    @property
+    def pool(self):
+        """The byte pool [n_slots][slot_bytes] of an ALLOC state."""
+        g = self.geo
+        return self._view("pool8", torch.uint8, (g.n_slots, int(self.c_state.slot_bytes)))
+
+    @property
+    def layout(self):
+        g = self.geo
+        return self._view("layout", torch.int32, (g.n_heads_v, LAYOUT_STRIDE))
+
+    @property
+    def dist(self):
+        g = self.geo
+        return self._view("dist", torch.float64, (g.n_heads_v, g.d, 5))
+
+    @property
+    def logret(self):
+        g = self.geo
+        return self._view("logret", torch.float64, (g.n_heads_v, g.d))
+
+    @property
+    def nret(self):
+        g = self.geo
+        return self._view("nret", torch.float64, (g.n_heads_v,))
+
+    @property
+    def slot_bytes(self) -> int:
+        return int(self.c_state.slot_bytes)
+
+    def calibrate_retention(self, alpha=None, gate=None, flags: int = 0, stream=None):
+        """Fold one step's gates (alpha [B][Hv] or gate [B][Hv][d]) into the
+        summed log retention (stq_calibrate_retention)."""
+        src = gate if gate is not None else alpha
+        B = 0 if src is None else int(src.shape[0])
+        _check(_lib().stq_calibrate_retention(ctypes.byref(self.c_state), _dev_ptr(alpha, "alpha"),
+                                              _dev_ptr(gate, "gate"), B, flags, _stream(stream)),
+               "stq_calibrate_retention")
+
+    def allocate(self, horizon: int, candidates: int = 0, stream=None):
+        """Pivots and row widths from the calibration statistics (stq_allocate)."""
+        _check(_lib().stq_allocate(ctypes.byref(self.c_state), int(horizon), int(candidates),
+                                   _stream(stream)), "stq_allocate")
+
+    def set_alloc_layout(self, counts, c: torch.Tensor, perm: torch.Tensor, stream=None):
+        """Install class counts [Hv][5] (host array), c and perm (device)."""
+        import numpy as np
+        cnt = np.ascontiguousarray(counts, dtype=np.int32)
+        _check(_lib().stq_set_alloc_layout(ctypes.byref(self.c_state), cnt.ctypes.data,
+                                           _dev_ptr(c, "c"), _dev_ptr(perm, "perm"),
+                                           _stream(stream)), "stq_set_alloc_layout")
 
     @property
     def calibrated(self) -> bool:

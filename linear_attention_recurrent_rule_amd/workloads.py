@@ -244,3 +244,73 @@ def unpack_codes(ps_pool8: np.ndarray, ps_pool4: np.ndarray) -> np.ndarray:
     z4[..., 0::2] = lo
     z4[..., 1::2] = hi
     return np.concatenate([ps_pool8, z4], axis=-2)
+
+
+RAGGED_ROW_BYTES = (lambda d: 2 * d, lambda d: d, lambda d: 3 * d // 4, lambda d: d // 2,
+                    lambda d: d // 4)
+
+
+def ragged_segments(counts: np.ndarray, d: int) -> np.ndarray:
+    """Byte offset of each head's segment in a slot of the ragged byte pool
+    (segments padded to 16 bytes, heads in order)."""
+    off, out = 0, []
+    for h in range(counts.shape[0]):
+        out.append(off)
+        seg = sum(int(counts[h, k]) * RAGGED_ROW_BYTES[k](d) for k in range(5))
+        off += (seg + 15) // 16 * 16
+    return np.array(out, np.int64)
+
+
+def unpack_ragged(pool: np.ndarray, counts: np.ndarray, d: int):
+    """Read a ragged byte pool [B][slot_bytes] back into (codes, half_bits,
+    cls): codes int32 [B][Hv][d][d] of the integer rows (physical order, 0
+    on pivot rows), half_bits uint16 [B][Hv][d][d] of the pivot rows (0
+    elsewhere) and the class of every physical row [Hv][d] (layout read-out
+    for test statistics; not part of any arithmetic)."""
+    B = pool.shape[0]
+    hv = counts.shape[0]
+    seg = ragged_segments(counts, d)
+    codes = np.zeros((B, hv, d, d), np.int32)
+    halfs = np.zeros((B, hv, d, d), np.uint16)
+    cls = np.zeros((hv, d), np.int32)
+    j = np.arange(d)
+    for h in range(hv):
+        off = int(seg[h])
+        p = 0
+        for k in range(5):
+            rb = RAGGED_ROW_BYTES[k](d)
+            for _ in range(int(counts[h, k])):
+                row = pool[:, off:off + rb]
+                cls[h, p] = k
+                if k == 0:
+                    halfs[:, h, p] = row.view(np.uint16) if row.flags["C_CONTIGUOUS"] else \
+                        np.ascontiguousarray(row).view(np.uint16)
+                elif k == 1:
+                    codes[:, h, p] = row.view(np.int8)
+                else:
+                    if k == 2:
+                        lo = (row[:, j // 2] >> (4 * (j % 2))) & 0xF
+                        hi = (row[:, d // 2 + j // 4] >> (2 * (j % 4))) & 0x3
+                        u = (lo | (hi << 4)).astype(np.int32)
+                        codes[:, h, p] = np.where(u >= 32, u - 64, u)
+                    elif k == 3:
+                        u = ((row[:, j // 2] >> (4 * (j % 2))) & 0xF).astype(np.int32)
+                        codes[:, h, p] = np.where(u >= 8, u - 16, u)
+                    else:
+                        u = ((row[:, j // 4] >> (2 * (j % 4))) & 0x3).astype(np.int32)
+                        codes[:, h, p] = np.where(u >= 2, u - 4, u)
+                off += rb
+                p += 1
+    return codes, halfs, cls
+
+
+def random_ragged_counts(hv: int, d: int, *, seed: int, pivots: int = 1) -> np.ndarray:
+    """Random class counts [Hv][5] (FP16, 8, 6, 4, 2 bits) summing to d, with
+    `pivots` FP16 rows per head and every integer class present when d allows."""
+    g = rng_for(seed, _TAG_PACKED, 5)
+    counts = np.zeros((hv, 5), np.int32)
+    for h in range(hv):
+        rest = d - pivots
+        cut = np.sort(g.integers(1, rest, size=3)) if rest > 4 else np.array([rest] * 3)
+        counts[h] = [pivots, cut[0], cut[1] - cut[0], cut[2] - cut[1], rest - cut[2]]
+    return counts

@@ -9,6 +9,7 @@ import ctypes
 import re
 from pathlib import Path
 
+import numpy as np
 import pytest
 
 ROOT = Path(__file__).resolve().parents[1]
@@ -32,15 +33,20 @@ def test_library_exports_every_declared_symbol():
     assert "stq_decode_step" in names and len(names) >= 8
     for n in names:
         assert hasattr(lib, n), f"libstq.so does not export {n}"
-    assert lib.stq_abi_version() == 3
+    assert lib.stq_abi_version() == 4
 
 
-def _desc(n_slots=4, hv=4, hk=2, d=64, n8=32, fmt=stq.FMT_MIXED48, dv=None):
-    return stq.Desc(n_slots, hv, hk, d, d if dv is None else dv, n8, fmt)
+def _desc(n_slots=4, hv=4, hk=2, d=64, n8=32, fmt=stq.FMT_MIXED48, dv=None, nominal=0, piv=0):
+    return stq.Desc(n_slots, hv, hk, d, d if dv is None else dv, n8, fmt, nominal, piv)
 
 
 def _bytes(**kw):
     return stq.lib().stq_state_bytes(ctypes.byref(_desc(**kw)))
+
+
+def _alloc_slot_bytes(hv, d, nominal, piv):
+    b = nominal * (hv * d - piv) * d // 8 + 2 * d * piv + 16 * hv
+    return (b + 15) // 16 * 16
 
 
 def _r(n):
@@ -253,3 +259,87 @@ def test_gated_rejections():
     assert cg(st, -1, stq.CAL_RESET) == E_SHAPE
     assert cg(st, 2, stq.CAL_COLS) == E_ARG
     assert cg(_fake_state(calibrated=1), 0, stq.CAL_RESET) == E_ARG
+
+
+def test_alloc_layout_arithmetic_and_rejections():
+    S, H, D = 64, 32, 128
+    for fmt in (stq.FMT_ALLOC, stq.FMT_ALLOC_REFIT):
+        for nominal, piv in ((6, 26), (4, 0), (2, 100), (8, H * D)):
+            slot = _alloc_slot_bytes(H, D, nominal, piv)
+            expect = (_r(S * slot) + _r(S * H * D * 4) + _r(H * D * 4) * 2
+                      + _r(H * D * 4) + _r(H * D * 8) + _r(H * 64 * D * 4) + _r(H * 64 * D * 8)
+                      + _r(H * 8 * 4) + _r(H * D * 5 * 8) + _r(H * D * 8) + _r(H * 8))
+            if fmt == stq.FMT_ALLOC_REFIT:
+                expect += _r(S * H * D * 4) + _r(H * D * 4) + _r(H * D * 8)
+            got = _bytes(n_slots=S, hv=H, hk=16, d=D, n8=0, fmt=fmt, nominal=nominal, piv=piv)
+            assert got == expect, (fmt, nominal, piv)
+    # the 6-bit budget with 0.625 % pivots: 12,288 B of codes per head plus
+    # 256 B per pivot row (vs 96 B at 6 bits) and the padding allowance
+    assert _alloc_slot_bytes(H, D, 6, 26) == 6 * (H * D - 26) * D // 8 + 2 * D * 26 + 16 * H
+    for kw in (dict(n8=8), dict(nominal=5), dict(nominal=0), dict(piv=-1),
+               dict(piv=4 * 64 + 1)):
+        base = dict(n_slots=4, hv=4, hk=2, d=64, n8=0, fmt=stq.FMT_ALLOC, nominal=6, piv=0)
+        base.update(kw)
+        assert _bytes(**base) == 0, kw
+    # other formats must leave the two fields at zero
+    assert _bytes(n8=32, nominal=6) == 0
+    assert _bytes(n8=32, piv=1) == 0
+
+
+def _fake_alloc_state(fmt=stq.FMT_ALLOC, calibrated=1, d=64, hv=4, nominal=6, piv=3):
+    st = stq.CState()
+    st.desc = _desc(fmt=fmt, n8=0, d=d, hv=hv, nominal=nominal, piv=piv)
+    for i, f in enumerate(("pool8", "r", "c", "perm", "colmax", "rowscore", "cal_colpart",
+                           "cal_rowpart", "cs", "w2", "impact", "layout", "dist", "logret",
+                           "nret")):
+        setattr(st, f, FAKE + 0x1000000 * (i + 1))
+    st.slot_bytes = _alloc_slot_bytes(hv, d, nominal, piv)
+    st.calibrated = calibrated
+    return st
+
+
+def test_alloc_rejections():
+    lib = stq.lib()
+    st = _fake_alloc_state()
+    assert _decode(_fake_alloc_state(calibrated=0)) == E_STATE
+    bad = _fake_alloc_state()
+    bad.slot_bytes += 16
+    assert _decode(bad) == E_ARG  # slot_bytes must match the descriptor
+    bad = _fake_alloc_state()
+    bad.layout = None
+    assert _decode(bad) == E_ARG
+    # calibration flags: DIST only for ALLOC, ROWS not for ALLOC
+    assert lib.stq_calibrate(ctypes.byref(st), FAKE, 1, stq.CAL_ROWS, None) == E_ARG
+    assert lib.stq_calibrate(ctypes.byref(_fake_state(calibrated=1)), FAKE, 1, stq.CAL_DIST,
+                             None) == E_ARG
+    assert lib.stq_calibrate(ctypes.byref(st), None, 2, stq.CAL_DIST, None) == E_ARG
+    assert lib.stq_set_calibration(ctypes.byref(st), FAKE, FAKE, None) == E_ARG
+    # retention
+    ret = lambda s_, a, g, B, f=0: lib.stq_calibrate_retention(  # noqa: E731
+        ctypes.byref(s_), a, g, B, f, None)
+    assert ret(st, FAKE, FAKE, 2) == E_ARG          # both gates
+    assert ret(st, None, None, 2) == E_ARG          # neither
+    assert ret(st, FAKE + 2, None, 2) == E_ARG      # misaligned
+    assert ret(st, FAKE, None, -1) == E_SHAPE
+    assert ret(st, FAKE, None, 2, stq.CAL_COLS) == E_ARG
+    assert ret(_fake_state(calibrated=1), FAKE, None, 2) == E_ARG
+    # assignment arguments
+    assert lib.stq_allocate(ctypes.byref(st), 0, 0, None) == E_ARG       # horizon
+    assert lib.stq_allocate(ctypes.byref(st), 64, 0x21, None) == E_ARG   # unknown class bit
+    assert lib.stq_allocate(ctypes.byref(st), 64, 0x12, None) == E_ARG   # 6 bits not a candidate
+    assert lib.stq_allocate(ctypes.byref(_fake_state(calibrated=1)), 64, 0, None) == E_ARG
+    # installing a layout: counts on the host
+    good = np.tile(np.array([0, 8, 24, 24, 8], np.int32), (4, 1))
+    ok_counts = good.ctypes.data
+    assert lib.stq_set_alloc_layout(ctypes.byref(st), None, FAKE, FAKE, None) == E_ARG
+    assert lib.stq_set_alloc_layout(ctypes.byref(st), ok_counts, FAKE + 4, FAKE, None) == E_ARG
+    short = good.copy()
+    short[1, 4] -= 1                                  # head 1 sums to 63
+    assert lib.stq_set_alloc_layout(ctypes.byref(st), short.ctypes.data, FAKE, FAKE,
+                                    None) == E_ARG
+    neg = good.copy()
+    neg[0, 1], neg[0, 2] = -1, 25
+    assert lib.stq_set_alloc_layout(ctypes.byref(st), neg.ctypes.data, FAKE, FAKE, None) == E_ARG
+    fat = np.tile(np.array([64, 0, 0, 0, 0], np.int32), (4, 1))  # all pivots: too big
+    assert lib.stq_set_alloc_layout(ctypes.byref(st), fat.ctypes.data, FAKE, FAKE,
+                                    None) == E_SPACE
