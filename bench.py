@@ -58,6 +58,8 @@ def parse():
                         "step t reads pool t and writes pool t+1 (stq_decode_step_into)")
     p.add_argument("--window", type=int, default=16, help="distinct input steps cycled")
     p.add_argument("--no-variants", action="store_true", help="skip the comparison formats")
+    p.add_argument("--variants", default=None,
+                   help="comma-separated subset of the comparison variants to run")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only-decode", action="store_true",
                    help="time the main workload only (for profiler runs)")
@@ -72,6 +74,9 @@ def parse():
                         "step, row-impact weights from the calibration steps)")
     p.add_argument("--drift-steps", type=int, default=None, help="T for --drift (default: the "
                    "workload's)")
+    p.add_argument("--alloc", action="store_true",
+                   help="--drift with the ragged format: FP16 pivot rows and 8/6/4/2-bit rows "
+                        "chosen by the lifetime-aware assignment (with --refit: the refit variant)")
     p.add_argument("--gate", action="store_true",
                    help="--drift with a per-key-row gate of the KDA form in place of alpha, "
                         "d_i = sigmoid(N(2.5, 1.5)) per (sequence, value head, key row, step)")
@@ -114,6 +119,75 @@ def measure_copy(torch, stq, nbytes: int = 1 << 30, iters: int = 10) -> float:
     e_ev.record()
     torch.cuda.synchronize()
     return 2 * nbytes * iters / (s_ev.elapsed_time(e_ev) / 1e3) / 1e9
+
+
+def alloc_pivots(hv: int, d: int) -> int:
+    """FP16 pivot rows per slot: the paper's KDA share, 512 of 81,920 key rows
+    (App. C.2 Table C1), of this layer's Hv * d rows."""
+    return int(round(hv * d * 512 / 81920))
+
+
+def alloc_nominal(w) -> int:
+    """Nominal integer width of the ragged format for a workload: 6 bits for
+    the 6-bit mix (half the rows 8-bit), 4 bits below it (Table C1 budgets)."""
+    return 6 if 2 * w.n8 >= w.d else 4
+
+
+def calibrate_alloc(torch, stq, S0, step_inputs, *, B, hv, hk, d, steps, nominal, n_pivot,
+                    horizon=2048, gated=False, refit=False):
+    """Offline calibration of the ragged format on unquantized FP32-state steps
+    from S0: pass 1 folds the column maxima and the log retention (and the row
+    impact for the refit format), FINALIZE sets c; pass 2 replays the same
+    steps and folds the candidate distortions against that c; then the
+    lifetime-aware assignment.  step_inputs(t) gives (q, k, v, alpha or gate,
+    beta).  Returns (counts [Hv][5] numpy, c, perm, w2 or None)."""
+    fmt = stq.FMT_ALLOC_REFIT if refit else stq.FMT_ALLOC
+    cal = stq.State(stq.Geometry(1, hv, hk, d, 0, fmt, nominal_bits=nominal, n_pivot=n_pivot))
+    fp = stq.State(stq.Geometry(B, hv, hk, d, 0, stq.FMT_FP32))
+    cal.calibrate(None, stq.CAL_RESET)
+    cal.calibrate_retention(flags=stq.CAL_RESET)
+    if refit:
+        cal.calibrate_impact(None, None, None, None, stq.CAL_RESET)
+    for pass_ in (0, 1):
+        fp.pack(S0)
+        for t in range(steps):
+            q, k, v, g, b = step_inputs(t)
+            if gated:
+                fp.decode_step_gated(q, k, v, g, b)
+            else:
+                fp.decode_step(q, k, v, g, b)
+            if pass_ == 0:
+                cal.calibrate(fp.s32, stq.CAL_COLS)
+                if gated:
+                    cal.calibrate_retention(gate=g)
+                else:
+                    cal.calibrate_retention(alpha=g)
+                if refit and gated:
+                    cal.calibrate_impact(q, k, None, b, 0, gate=g)
+                elif refit:
+                    cal.calibrate_impact(q, k, g, b, 0)
+            else:
+                cal.calibrate(fp.s32, stq.CAL_DIST)
+        if pass_ == 0:
+            cal.calibrate(None, stq.CAL_FINALIZE)
+    cal.allocate(horizon)
+    if refit:
+        cal.calibrate_impact(None, None, None, None, stq.CAL_FINALIZE)
+    counts = cal.layout[:, :5].cpu().numpy().copy()
+    out = (counts, cal.c.clone(), cal.perm.clone(), cal.w2.clone() if refit else None)
+    del fp, cal
+    torch.cuda.synchronize()
+    return out
+
+
+def alloc_unit_bytes(counts, d: int) -> float:
+    """Average bytes per (slot, head) of a ragged layout: the used segment
+    bytes plus the fp32 row factors."""
+    import numpy as np
+    rb = np.array([2 * d, d, 3 * d // 4, d // 2, d // 4])
+    seg = (counts * rb).sum(axis=1)
+    seg = (seg + 15) // 16 * 16
+    return float(seg.mean() + 4 * d)
 
 
 def main():
@@ -171,12 +245,26 @@ def main():
     log(f"[bench] calibrated in {time.time() - t0:.1f}s")
 
     window = [to_dev_inputs(wl.workload_inputs(w, t)) for t in range(args.window)]
+
+    def alloc_cal_inputs(t, gated_):
+        q, k, v, a, b = to_dev_inputs(wl.workload_inputs(w, t, calibration=True))
+        if gated_:
+            a = dev(wl.draw_gate(B, hv, d, seed=w.calib_seed, step=t))
+        return q, k, v, a, b
     o = torch.empty((B, hv, d), dtype=torch.float32, device="cuda")
 
-    def make_pools(fmt: int, n8: int, n: int):
+    alloc_cal = {}  # gated -> (counts, c, perm, w2) of the ragged format
+
+    def make_pools(fmt: int, n8: int, n: int, gated: bool = False):
         pools = []
         for _ in range(n):
-            st = stq.State(stq.Geometry(B, hv, hk, d, n8, fmt))
+            if fmt in (stq.FMT_ALLOC, stq.FMT_ALLOC_REFIT):
+                counts, ca, pa, _ = alloc_cal[gated]
+                st = stq.State(stq.Geometry(B, hv, hk, d, 0, fmt, nominal_bits=alloc_nominal(w),
+                                            n_pivot=alloc_pivots(hv, d)))
+                st.set_alloc_layout(counts, ca, pa)
+            else:
+                st = stq.State(stq.Geometry(B, hv, hk, d, n8, fmt))
             if fmt in (stq.FMT_MIXED48, stq.FMT_REFIT):
                 st.set_calibration(c, perm)
             st.pack(S0)
@@ -217,13 +305,17 @@ def main():
     def measure(fmt_name: str, fmt: int, n8: int, npools: int, steps: int, warmup: int,
                 into: bool = False, gated: bool = False):
         nonlocal gates
-        pools = make_pools(fmt, n8, npools)
+        pools = make_pools(fmt, n8, npools, gated)
         if gated:  # per-key-row gates of the KDA form, one per window step
             gates = [dev(wl.draw_gate(B, hv, d, seed=w.seed, step=t))
                      for t in range(len(window))]
         total_ms, mean_ms = time_decode(pools, steps, warmup, into)
         gates = None
         nbytes = algorithmic_bytes(fmt_name, B, hv, hk, d, n8, in_el, gated)
+        if fmt in (stq.FMT_ALLOC, stq.FMT_ALLOC_REFIT):
+            unit = alloc_unit_bytes(alloc_cal[gated][0], d)
+            nbytes = int(2 * unit * B * hv) + algorithmic_bytes("fp32", B, hv, hk, d, 0, in_el,
+                                                                 gated) - 2 * 4 * d * d * B * hv
         res = dict(updates_per_s=B * hv * steps / (total_ms / 1e3), ms_per_step=total_ms / steps,
                    kernel_ms_mean=mean_ms,
                    algorithmic_bytes_per_launch=nbytes,
@@ -244,23 +336,48 @@ def main():
     variants = {}
     copy_gbps = None
     if not args.only_decode and not args.no_variants:
+        chosen = None if args.variants is None else set(args.variants.split(","))
+        want = lambda name: chosen is None or name in chosen  # noqa: E731
         other = "in_place" if into else "double_buffered"
-        variants[other] = measure("mixed", stq.FMT_MIXED48, w.n8, args.pools, args.steps,
-                                  args.warmup, not into)
-        if not into:
+        if want(other):
+            variants[other] = measure("mixed", stq.FMT_MIXED48, w.n8, args.pools, args.steps,
+                                      args.warmup, not into)
+        if not into and want("single_pool_as_stated"):
             variants["single_pool_as_stated"] = measure("mixed", stq.FMT_MIXED48, w.n8, 1,
                                                         args.steps, args.warmup)
-        if w.n8 != 16:
+        if w.n8 != 16 and want("mix_4p5bit_n8_16"):
             variants["mix_4p5bit_n8_16"] = measure("mixed", stq.FMT_MIXED48, 16, args.pools,
                                                    args.steps, args.warmup)
-        variants["int8row"] = measure("int8row", stq.FMT_INT8ROW, d, args.pools, args.steps,
-                                      args.warmup)
-        if d == 128 and w.n8 % 16 == 0:
+        if want("int8row"):
+            variants["int8row"] = measure("int8row", stq.FMT_INT8ROW, d, args.pools, args.steps,
+                                          args.warmup)
+        if d == 128 and w.n8 % 16 == 0 and want("refit_column_factors"):
             variants["refit_column_factors"] = measure("refit", stq.FMT_REFIT, w.n8, args.pools,
                                                        args.steps, args.warmup)
-        variants["row_gate_kda"] = measure("mixed", stq.FMT_MIXED48, w.n8, args.pools, args.steps,
-                                           args.warmup, gated=True)
-        variants["fp32_state"] = measure("fp32", stq.FMT_FP32, 0, 2, args.steps, args.warmup)
+        if want("row_gate_kda"):
+            variants["row_gate_kda"] = measure("mixed", stq.FMT_MIXED48, w.n8, args.pools,
+                                               args.steps, args.warmup, gated=True)
+        # ragged rows (FP16 pivots + 8/6/4/2 bits from the lifetime-aware
+        # assignment), scalar gate and KDA row gate, each with its own calibration
+        for gated_ in (False, True):
+            name = "alloc_pivots_kda_gate" if gated_ else "alloc_pivots"
+            if not want(name):
+                continue
+            t1 = time.time()
+            alloc_cal[gated_] = calibrate_alloc(
+                torch, stq, S0, lambda t: alloc_cal_inputs(t, gated_), B=B, hv=hv, hk=hk, d=d,
+                steps=w.calib_steps, nominal=alloc_nominal(w), n_pivot=alloc_pivots(hv, d),
+                gated=gated_)
+            cnt = alloc_cal[gated_][0]
+            res = measure("mixed", stq.FMT_ALLOC, w.n8, args.pools, args.steps, args.warmup,
+                          gated=gated_)
+            res["rows_by_width"] = {str(b): int(cnt[:, k].sum())
+                                    for k, b in enumerate((16, 8, 6, 4, 2))}
+            res["bits_per_value"] = 8 * alloc_unit_bytes(cnt, d) / (d * d)
+            res["calibration_s"] = time.time() - t1
+            variants[name] = res
+        if want("fp32_state"):
+            variants["fp32_state"] = measure("fp32", stq.FMT_FP32, 0, 2, args.steps, args.warmup)
         for k_, v_ in variants.items():
             log(f"[bench] {k_}: {v_['updates_per_s'] / 1e6:.1f} M updates/s, "
                 f"{v_['hbm_gbps']:.0f} GB/s")
@@ -420,6 +537,7 @@ def run_drift(args, np, torch, stq, wl, w) -> dict:
 
     t0 = time.time()
     quant, ref = [], []
+    alloc_counts = []
     for layer in range(layers):
         S0 = dev(wl.initial_state(w, layer=layer)) if host else device_initial_state(torch, w, layer)
         fp = stq.State(stq.Geometry(w.B, w.hv, w.hk, w.d, 0, stq.FMT_FP32))
@@ -427,6 +545,19 @@ def run_drift(args, np, torch, stq, wl, w) -> dict:
         n8 = w.n8
         if w.calib_seed is None:  # all rows 8-bit, c = 1 (uniform rowwise INT8)
             qs = stq.State(stq.Geometry(w.B, w.hv, w.hk, w.d, w.d, stq.FMT_INT8ROW))
+        elif args.alloc:
+            counts, ca, pa, w2a = calibrate_alloc(
+                torch, stq, S0, lambda t: inputs(layer, t, calibration=True), B=w.B, hv=w.hv,
+                hk=w.hk, d=w.d, steps=w.calib_steps, nominal=alloc_nominal(w),
+                n_pivot=alloc_pivots(w.hv, w.d), gated=args.gate, refit=args.refit)
+            fmt = stq.FMT_ALLOC_REFIT if args.refit else stq.FMT_ALLOC
+            qs = stq.State(stq.Geometry(w.B, w.hv, w.hk, w.d, 0, fmt,
+                                        nominal_bits=alloc_nominal(w),
+                                        n_pivot=alloc_pivots(w.hv, w.d)))
+            qs.set_alloc_layout(counts, ca, pa)
+            if args.refit:
+                qs.w2.copy_(w2a)
+            alloc_counts.append(counts)
         else:
             fmt = stq.FMT_REFIT if args.refit else stq.FMT_MIXED48
             cal = stq.State(stq.Geometry(1, w.hv, w.hk, w.d, n8, fmt))
@@ -499,7 +630,15 @@ def run_drift(args, np, torch, stq, wl, w) -> dict:
     return {"drift": {"workload": w.name, "layers": layers, "steps": T,
                       "inputs": "host generator" if host else "device generator",
                       "state": ("int8row" if w.calib_seed is None
-                                else "packed, refit column factors" if args.refit else "packed"),
+                                else ("ragged rows (FP16 pivots, 8/6/4/2 bits)" if args.alloc
+                                      else "packed") + (", refit column factors" if args.refit
+                                                        else "")),
+                      "rows_by_width": ({str(b): int(sum(cn[:, k].sum() for cn in alloc_counts))
+                                         for k, b in enumerate((16, 8, 6, 4, 2))}
+                                        if alloc_counts else None),
+                      "bits_per_value": (8 * float(np.mean([alloc_unit_bytes(cn, w.d)
+                                                            for cn in alloc_counts])) / w.d ** 2
+                                         if alloc_counts else None),
                       "n8": w.n8 if w.calib_seed is not None else w.d,
                       "gate": "per key row (KDA form)" if args.gate else "scalar",
                       "checkpoints": points,

@@ -28,6 +28,7 @@ namespace {
 
 constexpr float kRowFloor = 1.17549435082228750797e-38f; // 2^-126
 constexpr float kHalfMax = 65504.0f;
+constexpr float kRoundMagic = 12582912.0f; // 1.5 * 2^23
 
 template <typename T> struct In;
 template <> struct In<float> {
@@ -57,6 +58,10 @@ __device__ __forceinline__ float qmax_of(int k) {
     return k == 1 ? 127.0f : (k == 2 ? 31.0f : (k == 3 ? 7.0f : 1.0f));
 }
 
+__device__ __forceinline__ float qinv_of(int k) {
+    return k == 1 ? (1.0f / 127.0f) : (k == 2 ? (1.0f / 31.0f) : (k == 3 ? (1.0f / 7.0f) : 1.0f));
+}
+
 // Where physical row p of a head lives: its class and byte offset within the
 // head's segment, from the five class counts.
 struct RowPlace {
@@ -81,6 +86,37 @@ __device__ __forceinline__ RowPlace place_row(const int32_t *lay, int p) {
         boff += n * rb[k];
     }
     return rp;
+}
+
+// Class boundaries of one head, computed once per unit: first physical row
+// (s1..s4) and first byte (b1..b4) of classes 1..4 (class 0 starts at 0).
+struct HeadLayout {
+    int s1, s2, s3, s4;
+    int b1, b2, b3, b4;
+};
+
+template <int D>
+__device__ __forceinline__ HeadLayout head_layout(const int32_t *lay) {
+    const int n0 = lay[0], n1 = lay[1], n2 = lay[2], n3 = lay[3];
+    HeadLayout L;
+    L.s1 = n0;
+    L.s2 = L.s1 + n1;
+    L.s3 = L.s2 + n2;
+    L.s4 = L.s3 + n3;
+    L.b1 = n0 * (2 * D);
+    L.b2 = L.b1 + n1 * D;
+    L.b3 = L.b2 + n2 * (3 * D / 4);
+    L.b4 = L.b3 + n3 * (D / 2);
+    return L;
+}
+
+template <int D>
+__device__ __forceinline__ RowPlace place_in(const HeadLayout &L, int p) {
+    if (p < L.s1) return RowPlace{0, p * (2 * D)};
+    if (p < L.s2) return RowPlace{1, L.b1 + (p - L.s1) * D};
+    if (p < L.s3) return RowPlace{2, L.b2 + (p - L.s2) * (3 * D / 4)};
+    if (p < L.s4) return RowPlace{3, L.b3 + (p - L.s3) * (D / 2)};
+    return RowPlace{4, L.b4 + (p - L.s4) * (D / 4)};
 }
 
 // The 8 raw code words of this lane's chunk of one row (layout above).
@@ -231,6 +267,7 @@ __global__ __launch_bounds__(256) void decode_alloc_kernel(DecodeArgs a) {
     float *rw = a.r_out + ubase * D;
 
     // Table C2 step 1: fetch this lane's row chunks and row factors.
+    const HeadLayout hl = head_layout<D>(lay);
     Chunk ch[8];
     int cls[8];
     int roff[8];
@@ -238,7 +275,7 @@ __global__ __launch_bounds__(256) void decode_alloc_kernel(DecodeArgs a) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
         const int p = g + C8 * m;
-        const RowPlace pl = place_row<D>(lay, p);
+        const RowPlace pl = place_in<D>(hl, p);
         cls[m] = pl.cls;
         roff[m] = pl.off;
         rrow[m] = 0.0f;
@@ -270,9 +307,12 @@ __global__ __launch_bounds__(256) void decode_alloc_kernel(DecodeArgs a) {
     }
     __syncthreads();
 
-    float cj[8];
+    float cj[8], cinv[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) cj[e] = s_c[ul][8 * c + e];
+    for (int e = 0; e < 8; ++e) {
+        cj[e] = s_c[ul][8 * c + e];
+        cinv[e] = __builtin_amdgcn_rcpf(cj[e]);
+    }
 
     // Decode the chunks to the column-normalised domain and accumulate this
     // lane's share of u~ = (D S / c)^T k and w~ = (D S / c)^T q.
@@ -290,7 +330,7 @@ __global__ __launch_bounds__(256) void decode_alloc_kernel(DecodeArgs a) {
         float scale;
         if (cls[m] == 0) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) z[m][e] = half_bits_to_float(ch[m].w[e >> 1] >> (16 * (e & 1))) / cj[e];
+            for (int e = 0; e < 8; ++e) z[m][e] = half_bits_to_float(ch[m].w[e >> 1] >> (16 * (e & 1))) * cinv[e];
             scale = 1.0f;
         } else {
 #pragma unroll
@@ -375,14 +415,17 @@ __global__ __launch_bounds__(256) void decode_alloc_kernel(DecodeArgs a) {
             }
             continue;
         }
-        const float qb = qmax_of(cls[m]);
-        const float rn = fmaxf(mx / qb, kRowFloor);
+        // row factor from the row max times fl32(1/q_b); codes by one FMA that
+        // adds 1.5 * 2^23 (round half to even into the low mantissa bits)
+        const int qbi = static_cast<int>(qmax_of(cls[m]));
+        const float rn = fmaxf(mx * qinv_of(cls[m]), kRowFloor);
+        const float mul = __builtin_amdgcn_rcpf(rn);
         int zq[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            float y = rintf(x[e] / rn);
-            y = fminf(fmaxf(y, -qb), qb);
-            zq[e] = static_cast<int>(y);
+            const int zi = __float_as_int(__builtin_fmaf(x[e], mul, kRoundMagic)) -
+                           __float_as_int(kRoundMagic);
+            zq[e] = min(max(zi, -qbi), qbi);
         }
         if (REFIT) {
             // sum_i w2 r' z' X = c sum_i (w2 r') z' x, sum_i w2 r'^2 z'^2
