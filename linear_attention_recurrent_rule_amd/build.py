@@ -20,7 +20,8 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIB = PKG / "libstq.so"
-SOURCES = ["decode.hip", "decode128.hip", "aux_kernels.hip", "alloc_kernels.hip", "alloc_host.cpp",
+SOURCES = ["decode.hip", "decode128.hip", "aux_kernels.hip", "alloc_kernels.hip", "alloc128.hip",
+           "alloc_host.cpp",
            "stq_api.cpp"]
 
 ARCH = os.environ.get("STQ_OFFLOAD_ARCH", "gfx950")

@@ -730,6 +730,7 @@ template <int D> static unsigned alloc_unit_grid(long units) {
 }
 
 hipError_t launch_decode_alloc(int D, bool bf16, const DecodeArgs &a, hipStream_t s) {
+    if (D == 128) return launch_decode_alloc128(bf16, a, s);
     const long units = static_cast<long>(a.B) * a.Hv;
     const bool refit = a.cs != nullptr;
     if (bf16 && refit) {

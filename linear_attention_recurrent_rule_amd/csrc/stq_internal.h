@@ -120,6 +120,8 @@ hipError_t launch_calib_finalize(int D, const CalibArgs &a, hipStream_t s);
 hipError_t launch_impact_accumulate(int D, bool bf16, const ImpactArgs &a, hipStream_t s);
 hipError_t launch_impact_finalize(int D, const ImpactArgs &a, hipStream_t s);
 hipError_t launch_decode_alloc(int D, bool bf16, const DecodeArgs &a, hipStream_t s);
+// 128 x 128 heads: matrix-core column sums, per-slot class branches.
+hipError_t launch_decode_alloc128(bool bf16, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_pack_alloc(int D, const PackArgs &a, hipStream_t s);
 hipError_t launch_dequant_alloc(int D, const PackArgs &a, hipStream_t s);
 hipError_t launch_alloc_distortion(int D, const AllocCalArgs &a, hipStream_t s);
