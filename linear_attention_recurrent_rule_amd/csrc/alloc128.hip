@@ -386,6 +386,11 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
     float *rw = a.r_out + ub * D;
 
     const unsigned tab = slot_table(L, wv, t);
+    // ---- perm and r before the codes: the gathers of k and q depend on perm,
+    // and loads complete in the order they are issued (every lane loads, so
+    // no branch holds the results back)
+    int praw = a.perm[h * D + (t & (D - 1))];
+    float rpv = rr[t & (D - 1)];
 
     // ---- Table C2 step 1: issue the loads of this lane's row chunks
     uint32_t ld[8][4]; // per slot: A.x, A.y, B.x, B.y
@@ -407,15 +412,16 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
 
     // ---- per-row and per-column factors, once per unit
     if (t < D) {
+        asm volatile("" : "+v"(praw), "+v"(rpv));
         const int p = t;
         const int k = class_of(L, p);
-        const int i = a.perm[h * D + p] & (D - 1);
+        const int i = praw & (D - 1);
         const unsigned kb = static_cast<unsigned>((b * a.Hk + hk) * D);
         const float kp = In<TIn>::get(a.k, kb + i);
         const float qp = In<TIn>::get(a.q, kb + i);
         // integer rows: r / W (codes are widened as W z); pivot rows: 1
         const float winv = k == 1 ? 1.0f : (k == 2 ? 0.25f : (k == 3 ? 0.0625f : 0.015625f));
-        float scale = k == 0 ? 1.0f : rr[p] * winv;
+        float scale = k == 0 ? 1.0f : rpv * winv;
         if (GATED) scale *= a.gate[static_cast<size_t>(unit) * D + i];
         {
             uint16_t(&cf)[kCoefRows][8] = sh.coef[(p & 15) >> 2][p & 3];
@@ -446,6 +452,9 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
         const float kq = wave_sum(kp * qp);
         if ((t & 63) == 0) sh.kq[t >> 6] = kq;
     } else {
+        // (a use on this side too, so the compiler keeps the two loads ahead
+        // of the code loads instead of sinking them into the branch above)
+        asm volatile("" ::"v"(praw), "v"(rpv));
         const int j = t - D;
         sh.v[j] = In<TIn>::get(a.v, static_cast<unsigned>((b * Hv + h) * D + j));
         sh.c[j] = REFIT ? a.cs[ub * D + j] : a.c[h * D + j];
@@ -653,7 +662,11 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
             }
         }
     }
-    __syncthreads();
+    // the multipliers of a row group are written and read by the 16 lanes of
+    // that group, inside one wave: a wave-level fence suffices
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- Table C2 steps 5-6: codes against the stored factors, pack, write back
     float mulv[8];

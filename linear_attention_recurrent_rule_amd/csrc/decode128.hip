@@ -324,7 +324,11 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
             }
         }
     }
-    __syncthreads();
+    // the multipliers of a row group are written and read by the 16 lanes of
+    // that group, inside one wave: a wave-level fence suffices
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- Table C2 step 6: codes against the stored factors, pack, write back
     float mulv[8];
@@ -446,17 +450,23 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
     L.rw = a.r_out + ub * D;
     L.cw = REFIT ? a.cs_out + ub * D : nullptr;
 
+    // ---- perm and r before the codes: the gathers of k and q depend on perm,
+    // and loads complete in the order they are issued (every lane loads, so
+    // no branch holds the results back)
+    int praw = a.perm[h * D + (t & (D - 1))];
+    float rpv = L.rr[t & (D - 1)];
     // ---- Table C2 step 1: issue the loads of this lane's packed rows
     uint32_t w0[8], w1[8];
     load_codes<N8>(L, w0, w1);
     // ---- per-row and per-column factors, once per unit
     if (t < D) {
+        asm volatile("" : "+v"(praw), "+v"(rpv));
         const int p = t;
-        const int i = a.perm[h * D + p] & (D - 1);
+        const int i = praw & (D - 1);
         const unsigned kb = static_cast<unsigned>((b * a.Hk + hk) * D);
         const float kp = In<TIn>::get(a.k, kb + i);
         const float qp = In<TIn>::get(a.q, kb + i);
-        const float rp = L.rr[p];
+        const float rp = rpv;
         // 4-bit codes are widened as 16 z; a row gate scales the whole row
         float scale = p < N8 ? rp : rp * 0.0625f;
         if (GATED) scale *= a.gate[static_cast<size_t>(unit) * D + i];
@@ -484,6 +494,9 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
         const float kq = wave_sum(kp * qp);
         if ((t & 63) == 0) sh.kq[t >> 6] = kq;
     } else {
+        // (a use on this side too, so the compiler keeps the two loads ahead
+        // of the code loads instead of sinking them into the branch above)
+        asm volatile("" ::"v"(praw), "v"(rpv));
         const int j = t - D;
         sh.v[j] = In<TIn>::get(a.v, static_cast<unsigned>((b * Hv + h) * D + j));
         sh.c[j] = REFIT ? a.cs[ub * D + j] : a.c[h * D + j];
