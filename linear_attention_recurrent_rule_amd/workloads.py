@@ -314,3 +314,69 @@ def random_ragged_counts(hv: int, d: int, *, seed: int, pivots: int = 1) -> np.n
         cut = np.sort(g.integers(1, rest, size=3)) if rest > 4 else np.array([rest] * 3)
         counts[h] = [pivots, cut[0], cut[1] - cut[0], cut[2] - cut[1], rest - cut[2]]
     return counts
+
+
+def calibration_shaped_counts(hv: int, d: int, *, seed: int, two_bit_heads: int = 0) -> np.ndarray:
+    """Class counts [Hv][5] shaped like an assignment at a 6-bit budget: 0-3
+    FP16 rows, about a fifth of the rows at 8 and at 4 bits, the rest 6-bit;
+    the first `two_bit_heads` heads also get a few 2-bit rows.  Boundaries
+    fall anywhere, so row groups straddle classes as they do after a real
+    assignment."""
+    g = rng_for(seed, _TAG_PACKED, 6)
+    counts = np.zeros((hv, 5), np.int32)
+    for h in range(hv):
+        piv = int(g.integers(0, 4))
+        n8 = int(g.integers(d // 8, d // 4 + 1))
+        n4 = int(g.integers(d // 8, d // 4 + 1))
+        n2 = int(g.integers(1, d // 8 + 1)) if h < two_bit_heads else 0
+        counts[h] = [piv, n8, d - piv - n8 - n4 - n2, n4, n2]
+    return counts
+
+
+def random_ragged_state(B: int, counts: np.ndarray, d: int, slot_bytes: int, *, seed: int,
+                        r_log10_range: tuple[float, float] = (-2.0, 0.5)):
+    """A valid ragged packed state drawn directly (layout of the ragged
+    formats: per head, FP16 rows, then 8-, 6-, 4-, 2-bit rows, segments
+    padded to 16 bytes): integer codes uniform on each width's symmetric
+    range, FP16 rows N(0, 1) rounded to binary16, log-uniform row factors
+    (0 on FP16 rows).  Returns (pool uint8 [B][slot_bytes], r f32 [B][Hv][d])."""
+    g = rng_for(seed, _TAG_PACKED, 7)
+    hv = counts.shape[0]
+    pool = np.zeros((B, slot_bytes), np.uint8)
+    r = (10.0 ** g.uniform(*r_log10_range, size=(B, hv, d))).astype(np.float32)
+    seg = ragged_segments(counts, d)
+    assert seg[-1] + sum(int(counts[-1, k]) * RAGGED_ROW_BYTES[k](d) for k in range(5)) \
+        <= slot_bytes
+    qmax = (0, 127, 31, 7, 1)
+    for h in range(hv):
+        off = int(seg[h])
+        p = 0
+        for k in range(5):
+            n = int(counts[h, k])
+            if n == 0:
+                continue
+            rb = RAGGED_ROW_BYTES[k](d)
+            if k == 0:
+                vals = g.standard_normal((B, n, d)).astype(np.float16)
+                rows = vals.view(np.uint8).reshape(B, n, 2 * d)
+                r[:, h, p:p + n] = 0.0
+            else:
+                z = g.integers(-qmax[k], qmax[k] + 1, size=(B, n, d), dtype=np.int16)
+                u = (z & ((1 << (8 if k == 1 else (6, 4, 2)[k - 2])) - 1)).astype(np.uint8)
+                if k == 1:
+                    rows = u
+                elif k == 3:
+                    rows = (u[..., 0::2] & 0xF) | ((u[..., 1::2] & 0xF) << 4)
+                else:
+                    f = (u >> 4) & 0x3 if k == 2 else u & 0x3  # the 2-bit fields
+                    fields = (f[..., 0::4] | (f[..., 1::4] << 2) | (f[..., 2::4] << 4)
+                              | (f[..., 3::4] << 6)).astype(np.uint8)
+                    if k == 2:
+                        nib = (u[..., 0::2] & 0xF) | ((u[..., 1::2] & 0xF) << 4)
+                        rows = np.concatenate([nib, fields], axis=-1)
+                    else:
+                        rows = fields
+            pool[:, off:off + n * rb] = rows.reshape(B, n * rb)
+            off += n * rb
+            p += n
+    return pool, r

@@ -58,7 +58,12 @@ def _load(st, pool, r, cs=None):
     torch.cuda.synchronize()
 
 
-def _compare(gpu_pool, gpu_r, ref_pool, ref_r, counts, d, label, *, o=None, ref_o=None):
+def _compare(gpu_pool, gpu_r, ref_pool, ref_r, counts, d, label, *, o=None, ref_o=None,
+             pivot_err=None):
+    """pivot_err (optional, [B][Hv][d][d] in physical row order): an absolute
+    allowance added to the one-ulp bar of each pivot value, for values formed
+    by cancellation, where the fp32 evaluation error of the terms exceeds
+    half an ulp of the binary16 result."""
     zg, hg, cls = wl.unpack_ragged(gpu_pool, counts, d)
     zr, hr, _ = wl.unpack_ragged(ref_pool, counts, d)
     ints = np.broadcast_to(cls[None, :, :, None] != 0, zg.shape)
@@ -75,6 +80,8 @@ def _compare(gpu_pool, gpu_r, ref_pool, ref_r, counts, d, label, *, o=None, ref_
     va = hg[hpiv].view(np.float16).astype(np.float64)
     vb = hr[hpiv].view(np.float16).astype(np.float64)
     step = np.spacing(np.maximum(np.abs(va), np.abs(vb)).astype(np.float16)).astype(np.float64)
+    if pivot_err is not None:
+        step = step + pivot_err[hpiv]
     hd = np.abs(va - vb)
     assert hd.size == 0 or np.all(hd <= step), f"{label}: pivot value off by more than 1 ulp"
     stats = dict(code_match=match, max_r_rel=float(rel.max()) if rel.size else 0.0,

@@ -1,0 +1,95 @@
+"""Full-size decode steps of the ragged row-class format (FP16 pivot rows and
+8-, 6-, 4-, 2-bit rows; STEPQuant paper App. C.2 Table C1, App. C.3 Table C2)
+at the benchmark's shape: B = 1024 sequences, 32 value heads over 16 key
+heads, d = 128, bf16 inputs, one launch over the whole batch.  The layout is
+shaped like an assignment at a 6-bit budget (0-3 pivot rows per head, class
+boundaries anywhere, a few heads with 2-bit rows).  The oracle checks sampled
+sequences (all heads of each); properties that hold at any size are checked
+on every unit.  Bars as in test_gpu_alloc, except that a pivot value may also
+differ from the oracle's by the fp32 evaluation error of its two terms: the
+GPU forms X = c_j s_i (P_i h_ij / c_j + e_j) in fp32, so where d_i h_ij and
+beta k_i c_j e_j nearly cancel, the result carries an absolute error of a few
+fp32 ulps of the terms, which can exceed half a binary16 ulp of the small
+result.  The allowance is 2^-20 (|d_i h_ij| + |X_ij - d_i h_ij|), 16 fp32
+roundings of the larger term, with X the oracle's double value."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from linear_attention_recurrent_rule_amd import workloads as wl
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+from linear_attention_recurrent_rule_amd import stq  # noqa: E402
+from tests import gpu_util as gu  # noqa: E402
+from tests.test_gpu_alloc import _compare  # noqa: E402
+
+QMAX = np.array([0, 127, 31, 7, 1])
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_alloc_fullsize_step_sampled_parity_and_properties(oracle_mod, gated):
+    w = wl.WORKLOADS["highconc_6bit"]
+    B, hv, hk, d = w.B, w.hv, w.hk, w.d
+    print(f"[case] ragged full size B={B} hv={hv} hk={hk} d={d} gated={gated}", flush=True)
+    counts = wl.calibration_shaped_counts(hv, d, seed=w.seed + 600, two_bit_heads=4)
+    g = wl.rng_for(w.seed, 601)
+    perm = np.stack([g.permutation(d) for _ in range(hv)]).astype(np.int32)
+    c = g.lognormal(0.0, 0.7, size=(hv, d)).astype(np.float32)
+    st = stq.State(stq.Geometry(B, hv, hk, d, 0, stq.FMT_ALLOC, nominal_bits=8,
+                                n_pivot=int(counts[:, 0].sum())))
+    st.set_alloc_layout(counts, gu.dev(c), gu.dev(perm))
+    pool, r = wl.random_ragged_state(B, counts, d, st.slot_bytes, seed=w.seed + 602)
+    st.pool.copy_(gu.dev(pool))
+    st.r.copy_(gu.dev(r))
+    x = wl.workload_inputs(w, 0)
+    q, k, v, a, b = gu.inputs_to_device(x)
+    gate = wl.draw_gate(B, hv, d, seed=w.seed + 603, step=0) if gated else None
+    torch.cuda.synchronize()
+    print("[case] launching the full-size step", flush=True)
+    if gated:
+        o = st.decode_step_gated(q, k, v, gu.dev(gate), b)
+    else:
+        o = st.decode_step(q, k, v, a, b)
+    torch.cuda.synchronize()
+    gp, gr, go = st.pool.cpu().numpy(), st.r.cpu().numpy(), o.cpu().numpy()
+
+    # properties on every unit
+    print("[case] properties on all units", flush=True)
+    assert np.all(np.isfinite(go))
+    z, hbits, cls = wl.unpack_ragged(gp, counts, d)
+    qb = QMAX[cls]  # [Hv][d]
+    zmax = np.abs(z).max(axis=-1)  # [B][Hv][d]
+    ints = np.broadcast_to(cls[None] != 0, zmax.shape)
+    assert np.all(zmax <= qb[None]), "code outside its width's symmetric range"
+    floor = gr == np.float32(2.0 ** -126)
+    assert np.all(((zmax == qb[None]) | floor)[ints]), "integer row not spanning its range"
+    assert np.all(gr[~ints] == 0.0), "pivot row with a row factor"
+    piv = np.broadcast_to(cls[None, :, :, None] == 0, hbits.shape)
+    assert np.all(np.isfinite(hbits[piv].view(np.float16)))
+    del z, hbits
+
+    # oracle on sampled sequences, all heads each
+    bs = np.unique(np.concatenate([[0, B - 1], g.choice(B, 6, replace=False)]))
+    print(f"[case] oracle on sequences {bs.tolist()}", flush=True)
+    kw = dict(gate=gate[bs]) if gated else {}
+    ref = oracle_mod.alloc_step(pool[bs], r[bs], counts, perm, x.q[bs], x.k[bs], x.v[bs],
+                                None if gated else x.alpha[bs], x.beta[bs], c=c, nthreads=16,
+                                want_X=True, **kw)
+    # terms of each pivot value: the gated old value d_i h_ij and the rest
+    _, h_old, _ = wl.unpack_ragged(pool[bs], counts, d)
+    Xp = np.take_along_axis(ref["X"], perm[None, :, :, None], axis=2)  # physical rows
+    if gated:
+        dp = np.take_along_axis(gate[bs].astype(np.float64), perm[None], axis=2)[..., None]
+    else:
+        dp = x.alpha[bs].astype(np.float64)[:, :, None, None]
+    t1 = dp * h_old.view(np.float16).astype(np.float64)
+    pivot_err = 2.0 ** -20 * (np.abs(t1) + np.abs(Xp - t1))
+    stats = _compare(gp[bs], gr[bs], ref["pool"], ref["r"], counts, d, "ragged full size",
+                     o=go[bs], ref_o=ref["o"], pivot_err=pivot_err)
+    print(stats)
