@@ -90,6 +90,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 // MFMA operand A for the column sums: per wave w and lane group gl, seven
 // 8-entry bf16 rows: r k (hi, mid, lo), r q (hi, mid, lo) of the lane group's
@@ -144,7 +145,10 @@ struct Lane {
     float *cw;         // refit column factors written (REFIT format)
 };
 
-// Fetch this lane's packed rows (Table C2 step 1).
+// Fetch this lane's packed rows (Table C2 step 1).  The packed state is read
+// once and written once per step and nothing reuses it within the step, so
+// its loads and stores carry the non-temporal hint (measured 5 % faster than
+// cached accesses at B = 1024).
 template <int N8>
 __device__ __forceinline__ void load_codes(const Lane &L, uint32_t (&w0)[8], uint32_t (&w1)[8]) {
     constexpr int M8 = N8 / 16;
@@ -152,11 +156,13 @@ __device__ __forceinline__ void load_codes(const Lane &L, uint32_t (&w0)[8], uin
     for (int m = 0; m < 8; ++m) {
         const unsigned p = static_cast<unsigned>(L.g + 16 * m);
         if (m < M8) {
-            const uint2 v2 = *reinterpret_cast<const uint2 *>(L.p8 + (p * D + 8 * L.c));
-            w0[m] = v2.x;
-            w1[m] = v2.y;
+            const u32x2 v2 =
+                __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(L.p8 + (p * D + 8 * L.c)));
+            w0[m] = v2[0];
+            w1[m] = v2[1];
         } else {
-            w0[m] = *reinterpret_cast<const uint32_t *>(L.p4 + ((p - N8) * (D / 2) + 4 * L.c));
+            w0[m] = __builtin_nontemporal_load(
+                reinterpret_cast<const uint32_t *>(L.p4 + ((p - N8) * (D / 2) + 4 * L.c)));
             w1[m] = 0u;
         }
     }
@@ -370,7 +376,8 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
             const uint32_t a23 = __builtin_amdgcn_perm(bt[3], bt[2], 0x04000C0Cu);
             const uint32_t a45 = __builtin_amdgcn_perm(bt[5], bt[4], 0x0C0C0400u);
             const uint32_t a67 = __builtin_amdgcn_perm(bt[7], bt[6], 0x04000C0Cu);
-            *reinterpret_cast<uint2 *>(L.q8 + (p * D + 8 * c)) = make_uint2(a01 | a23, a45 | a67);
+            __builtin_nontemporal_store(u32x2{a01 | a23, a45 | a67},
+                                        reinterpret_cast<u32x2 *>(L.q8 + (p * D + 8 * c)));
         } else {
             // even columns -> low nibbles, odd columns -> high nibbles
             const uint32_t ev02 = __builtin_amdgcn_perm(bt[2], bt[0], 0x0C0C0400u);
@@ -380,7 +387,8 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
             const uint32_t evn = ev02 | ev46;
             const uint32_t odd = (od13 | od57) << 4;
             const uint32_t word = (evn & 0x0F0F0F0Fu) | (odd & 0xF0F0F0F0u);
-            *reinterpret_cast<uint32_t *>(L.q4 + ((p - N8) * (D / 2) + 4 * c)) = word;
+            __builtin_nontemporal_store(word,
+                                        reinterpret_cast<uint32_t *>(L.q4 + ((p - N8) * (D / 2) + 4 * c)));
         }
     }
     if (REFIT) {
