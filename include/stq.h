@@ -356,8 +356,9 @@ stq_status stq_dequant_state(const stq_state *st, const int32_t *slots, int32_t 
                              float *S_out, stq_stream_t stream);
 
 /* Streaming copy of `bytes` (a multiple of 16, both pointers 16-byte aligned)
- * from src to dst: the plain copy kernel used to measure the practical HBM
- * ceiling and to scale hardware byte counters.
+ * from src to dst with non-temporal loads and stores: the plain copy kernel
+ * used to measure the practical HBM ceiling and to scale hardware byte
+ * counters.
  * Errors: STQ_E_ARG, STQ_E_DEVICE. */
 stq_status stq_stream_copy(const void *src, void *dst, size_t bytes, stq_stream_t stream);
 

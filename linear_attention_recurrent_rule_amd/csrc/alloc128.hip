@@ -41,8 +41,6 @@ constexpr float kMulMax = 1.70141183460469231732e38f;    // 2^127
 constexpr float kFormTiny = 5.42101086242752217004e-20f; // 2^-64
 constexpr float kHalfMax = 65504.0f;
 
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
 template <typename T> struct In;
 template <> struct In<float> {
     static __device__ __forceinline__ float get(const void *p, unsigned i) {
@@ -242,8 +240,7 @@ __device__ __forceinline__ void store_codes(uint8_t *base, unsigned off, int c,
         const uint32_t a23 = __builtin_amdgcn_perm(bt[3], bt[2], 0x04000C0Cu);
         const uint32_t a45 = __builtin_amdgcn_perm(bt[5], bt[4], 0x0C0C0400u);
         const uint32_t a67 = __builtin_amdgcn_perm(bt[7], bt[6], 0x04000C0Cu);
-        __builtin_nontemporal_store(u32x2{a01 | a23, a45 | a67},
-                                    reinterpret_cast<u32x2 *>(base + (off + 8u * c)));
+        *reinterpret_cast<uint2 *>(base + (off + 8u * c)) = make_uint2(a01 | a23, a45 | a67);
     } else {
         // bytes of the even columns 0, 2, 4, 6 and of the odd columns
         const uint32_t evn = __builtin_amdgcn_perm(bt[2], bt[0], 0x0C0C0400u) |
@@ -252,18 +249,18 @@ __device__ __forceinline__ void store_codes(uint8_t *base, unsigned off, int c,
                              __builtin_amdgcn_perm(bt[7], bt[5], 0x04000C0Cu);
         if constexpr (K == 2 || K == 3) {
             const uint32_t word = (evn & 0x0F0F0F0Fu) | ((odd << 4) & 0xF0F0F0F0u);
-            __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(base + (off + 4u * c)));
+            *reinterpret_cast<uint32_t *>(base + (off + 4u * c)) = word;
         }
         if constexpr (K == 2) {
             // bits 4..5 of each code: column e in bits 2e of a 16-bit field
             const uint32_t n = ((evn >> 4) & 0x03030303u) | ((odd >> 2) & 0x0C0C0C0Cu);
-            __builtin_nontemporal_store(static_cast<uint16_t>(bytes_to_nibbles(n)),
-                                        reinterpret_cast<uint16_t *>(base + (off + D / 2 + 2u * c)));
+            *reinterpret_cast<uint16_t *>(base + (off + D / 2 + 2u * c)) =
+                static_cast<uint16_t>(bytes_to_nibbles(n));
         }
         if constexpr (K == 4) {
             const uint32_t n = (evn & 0x03030303u) | ((odd << 2) & 0x0C0C0C0Cu);
-            __builtin_nontemporal_store(static_cast<uint16_t>(bytes_to_nibbles(n)),
-                                        reinterpret_cast<uint16_t *>(base + (off + 2u * c)));
+            *reinterpret_cast<uint16_t *>(base + (off + 2u * c)) =
+                static_cast<uint16_t>(bytes_to_nibbles(n));
         }
     }
 }
@@ -405,13 +402,12 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
             chunk_offsets<K>(static_cast<unsigned>(slot_base<K>(L, m) + g * Cls<K>::row), c, offA,
                              offB);
         });
-        // the packed state is streamed: non-temporal loads and stores
-        const u32x2 A = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(seg_in + offA));
-        const u32x2 Bw = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(seg_in + offB));
-        ld[m][0] = A[0];
-        ld[m][1] = A[1];
-        ld[m][2] = Bw[0];
-        ld[m][3] = Bw[1];
+        const uint2 A = *reinterpret_cast<const uint2 *>(seg_in + offA);
+        const uint2 Bw = *reinterpret_cast<const uint2 *>(seg_in + offB);
+        ld[m][0] = A.x;
+        ld[m][1] = A.y;
+        ld[m][2] = Bw.x;
+        ld[m][3] = Bw.y;
     }
 
     // ---- per-row and per-column factors, once per unit
@@ -710,8 +706,7 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
                     const float *y = &z[m][4 * hf];
                     const uint32_t lo = half_bits(cq.x * (sc * y[0])) | (half_bits(cq.y * (sc * y[1])) << 16);
                     const uint32_t hi = half_bits(cq.z * (sc * y[2])) | (half_bits(cq.w * (sc * y[3])) << 16);
-                    __builtin_nontemporal_store(
-                        u32x2{lo, hi}, reinterpret_cast<u32x2 *>(base + (off + 16u * cs_ + 8u * hf)));
+                    *reinterpret_cast<uint2 *>(base + (off + 16u * cs_ + 8u * hf)) = make_uint2(lo, hi);
                 }
             } else {
                 uint32_t bt[8];

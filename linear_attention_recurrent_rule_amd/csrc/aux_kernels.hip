@@ -350,10 +350,13 @@ __global__ void iota_rows_kernel(int32_t *perm, int rows, int D) {
 
 // Streaming copy: one 16-byte word per lane, one 4 KiB tile per workgroup
 // (the fastest of the plain copy shapes measured on gfx950).
-__global__ __launch_bounds__(256) void copy_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
-                                                   size_t n) {
+// A streaming copy with non-temporal loads and stores (the faster of the two
+// on this part: about 6.4 TB/s against 6.0 TB/s for cached accesses).
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void copy_kernel(const u32x4v *__restrict__ src,
+                                                   u32x4v *__restrict__ dst, size_t n) {
     const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (i < n) dst[i] = src[i];
+    if (i < n) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 // Row impact (Sec. 4.1; App. C.1 with the scalar gate): one workgroup per
@@ -517,7 +520,7 @@ hipError_t launch_copy_bytes(const void *src, void *dst, size_t bytes, hipStream
     const size_t blocks = (n + 255) / 256;
     if (blocks > 0x7fffffffu) return hipErrorInvalidValue;
     hipLaunchKernelGGL(copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                       static_cast<const uint4 *>(src), static_cast<uint4 *>(dst), n);
+                       static_cast<const u32x4v *>(src), static_cast<u32x4v *>(dst), n);
     return hipGetLastError();
 }
 
