@@ -228,20 +228,25 @@ def main():
     S0 = dev(wl.initial_state(w))
     log(f"[bench] S0 generated ({S0.numel() * 4 / 2**30:.2f} GiB) in {time.time() - t0:.1f}s")
 
-    # offline calibration: 32 unquantized steps on the calibration stream
-    fp_cal = stq.State(stq.Geometry(B, hv, hk, d, 0, stq.FMT_FP32))
-    fp_cal.pack(S0)
-    cal = stq.State(stq.Geometry(1, hv, hk, d, w.n8, stq.FMT_MIXED48))
-    cal.calibrate(None, stq.CAL_RESET)
-    for t in range(w.calib_steps):
-        q, k, v, a, b = to_dev_inputs(wl.workload_inputs(w, t, calibration=True))
-        fp_cal.decode_step(q, k, v, a, b)
-        last = t == w.calib_steps - 1
-        cal.calibrate(fp_cal.s32, stq.CAL_COLS | (stq.CAL_ROWS if last else 0))
-    cal.calibrate(None, stq.CAL_FINALIZE)
-    c, perm = cal.c.clone(), cal.perm.clone()
-    del fp_cal
-    torch.cuda.synchronize()
+    if w.calib_seed is None:
+        # no calibration stream (the tiny workload): c = 1, rows in order
+        c = torch.ones((hv, d), dtype=torch.float32, device="cuda")
+        perm = torch.arange(d, dtype=torch.int32, device="cuda").repeat(hv, 1).contiguous()
+    else:
+        # offline calibration: 32 unquantized steps on the calibration stream
+        fp_cal = stq.State(stq.Geometry(B, hv, hk, d, 0, stq.FMT_FP32))
+        fp_cal.pack(S0)
+        cal = stq.State(stq.Geometry(1, hv, hk, d, w.n8, stq.FMT_MIXED48))
+        cal.calibrate(None, stq.CAL_RESET)
+        for t in range(w.calib_steps):
+            q, k, v, a, b = to_dev_inputs(wl.workload_inputs(w, t, calibration=True))
+            fp_cal.decode_step(q, k, v, a, b)
+            last = t == w.calib_steps - 1
+            cal.calibrate(fp_cal.s32, stq.CAL_COLS | (stq.CAL_ROWS if last else 0))
+        cal.calibrate(None, stq.CAL_FINALIZE)
+        c, perm = cal.c.clone(), cal.perm.clone()
+        del fp_cal
+        torch.cuda.synchronize()
     log(f"[bench] calibrated in {time.time() - t0:.1f}s")
 
     window = [to_dev_inputs(wl.workload_inputs(w, t)) for t in range(args.window)]
