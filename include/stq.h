@@ -304,7 +304,9 @@ stq_status stq_pack_state(const stq_state *st, const float *S, const int32_t *sl
  *   z'_ij = clip(rhe(X_ij / c_j / r'_i), -q_b, q_b)
  * REFIT format: c is the state's own cs, refit after the codes are taken.
  * q, k, v are fp32 or bf16 (`dtype`); alpha, beta and o are fp32.
- * Preconditions: slots distinct within a call (not checked on the device);
+ * Preconditions: slots distinct within a call (not checked on the device;
+ * with STQ_CHECK_SLOTS set in the environment the host copies the slot list,
+ * synchronising the stream, and returns STQ_E_ARG for a repeated slot);
  * a slot outside [0, n_slots) is skipped and its o is filled with NaN.
  * Errors: STQ_E_ARG (null/misaligned pointer, bad dtype), STQ_E_SHAPE (B < 1
  * or B > n_slots), STQ_E_STATE (MIXED48 or REFIT not calibrated),

@@ -4,6 +4,7 @@
 #include "stq.h"
 
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -412,6 +413,26 @@ stq_status batch_args(const stq_state *st, const int32_t *slots, int32_t B) {
     return STQ_OK;
 }
 
+// Debug check of the slot precondition, enabled by setting STQ_CHECK_SLOTS in
+// the environment: the slot list is copied to the host (which synchronises
+// the stream) and a slot in range that appears twice is rejected.
+stq_status check_slots_distinct(const int32_t *slots, int32_t B, int32_t n_slots,
+                                hipStream_t stream) {
+    if (!slots || std::getenv("STQ_CHECK_SLOTS") == nullptr) return STQ_OK;
+    std::vector<int32_t> h(static_cast<size_t>(B));
+    if (hipMemcpyAsync(h.data(), slots, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
+                       stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return STQ_E_DEVICE;
+    std::vector<char> seen(static_cast<size_t>(n_slots), 0);
+    for (int32_t s : h) {
+        if (s < 0 || s >= n_slots) continue; // skipped by the kernels
+        if (seen[static_cast<size_t>(s)]) return STQ_E_ARG;
+        seen[static_cast<size_t>(s)] = 1;
+    }
+    return STQ_OK;
+}
+
 stq::PackArgs pack_args(const stq_state *st, const int32_t *slots, int32_t B) {
     stq::PackArgs a{};
     a.pool8 = st->pool8;
@@ -441,6 +462,8 @@ stq_status stq_pack_state(const stq_state *st, const float *S, const int32_t *sl
     if (e != STQ_OK) return e;
     if (!S || !aligned(S, 16)) return STQ_E_ARG;
     if (calibrated_format(st->desc.fmt) && !st->calibrated) return STQ_E_STATE;
+    if ((e = check_slots_distinct(slots, B, st->desc.n_slots, static_cast<hipStream_t>(stream))) != STQ_OK)
+        return e;
     stq::PackArgs a = pack_args(st, slots, B);
     a.S_in = S;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -494,6 +517,9 @@ stq_status decode(const stq_state *src, const stq_state *dst, const int32_t *slo
         !aligned(beta, 4) || !aligned(o, 4))
         return STQ_E_ARG;
     if (calibrated_format(src->desc.fmt) && !src->calibrated) return STQ_E_STATE;
+    if ((e = check_slots_distinct(slots, B, src->desc.n_slots, static_cast<hipStream_t>(stream))) !=
+        STQ_OK)
+        return e;
     const bool refit = refit_format(src->desc.fmt);
     Layout L;
     describe(&src->desc, &L);

@@ -147,6 +147,31 @@ def test_out_of_range_slot_is_skipped(oracle_mod, d, n8, hv, hk):
     gu.compare_step(dict(pool8=p8[[1]], pool4=p4[[1]], r=r[[1]], o=o[[0]]), ref, n8=n8, d=d)
 
 
+def test_repeated_slot_rejected_with_debug_check(monkeypatch):
+    """With STQ_CHECK_SLOTS set, a repeated slot is rejected on the host before
+    anything is queued (decode and pack); without it the call is accepted (the
+    precondition is the caller's).  Slots out of range stay allowed."""
+    d, n8, hv, hk, n_slots = 64, 32, 2, 1, 4
+    ps = wl.random_packed_state(n_slots, hv, d, n8, seed=43)
+    st = gu.make_state(n_slots, hv, hk, d, n8)
+    gu.load_packed(st, ps)
+    x = wl.draw_inputs(2, hk, hv, d, dtype="f32", seed=43, step=0)
+    q, k, v, a, b = gu.inputs_to_device(x)
+    dup = gu.dev(np.array([2, 2], np.int32))
+    monkeypatch.setenv("STQ_CHECK_SLOTS", "1")
+    with pytest.raises(stq.StqError, match="STQ_E_ARG"):
+        st.decode_step(q, k, v, a, b, slots=dup)
+    S = gu.dev(np.zeros((2, hv, d, d), np.float32))
+    with pytest.raises(stq.StqError, match="STQ_E_ARG"):
+        st.pack(S, slots=dup)
+    st.decode_step(q, k, v, a, b, slots=gu.dev(np.array([3, 17], np.int32)))  # 17: skipped
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(st.pool8[2].cpu().numpy(), ps.pool8[2])  # nothing ran on 2
+    monkeypatch.delenv("STQ_CHECK_SLOTS")
+    st.decode_step(q, k, v, a, b, slots=gu.dev(np.array([0, 1], np.int32)))
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("name,steps", [("tiny", 64), ("small_mixed", 48)])
 def test_trajectory_per_step_parity(oracle_mod, name, steps):
     """Along the oracle's own trajectory of a workload (S0 packed by the
