@@ -95,6 +95,24 @@ def _compare(gpu_pool, gpu_r, ref_pool, ref_r, counts, d, label, *, o=None, ref_
     return stats
 
 
+def pivot_allowance(pool, counts, perm, X, d, *, alpha=None, gate=None):
+    """Per pivot value [B][Hv][d][d] (physical rows): the fp32 evaluation error
+    of its two terms, 2^-20 (|d_i h_ij| + |X_ij - d_i h_ij|), with h the
+    binary16 values of the input pool, d_i the gate (alpha for the scalar
+    gate) and X the oracle's double state (logical rows).  Where the gated old
+    value and the delta write nearly cancel, the GPU's fp32 result carries an
+    error of a few ulps of the terms, which can exceed half a binary16 ulp of
+    the small result."""
+    _, h_old, _ = wl.unpack_ragged(pool, counts, d)
+    Xp = np.take_along_axis(X, perm[None, :, :, None], axis=2)  # physical rows
+    if gate is not None:
+        dp = np.take_along_axis(gate.astype(np.float64), perm[None], axis=2)[..., None]
+    else:
+        dp = alpha.astype(np.float64)[:, :, None, None]
+    t1 = dp * h_old.view(np.float16).astype(np.float64)
+    return 2.0 ** -20 * (np.abs(t1) + np.abs(Xp - t1))
+
+
 @pytest.mark.parametrize("d", [16, 32, 64, 128])
 def test_alloc_pack_dequant_parity(oracle_mod, d):
     B, hv, hk = 3, 4, 2

@@ -27,7 +27,7 @@ if not torch.cuda.is_available():  # pragma: no cover
 
 from linear_attention_recurrent_rule_amd import stq  # noqa: E402
 from tests import gpu_util as gu  # noqa: E402
-from tests.test_gpu_alloc import _compare  # noqa: E402
+from tests.test_gpu_alloc import _compare, pivot_allowance  # noqa: E402
 
 QMAX = np.array([0, 127, 31, 7, 1])
 
@@ -81,15 +81,9 @@ def test_alloc_fullsize_step_sampled_parity_and_properties(oracle_mod, gated):
     ref = oracle_mod.alloc_step(pool[bs], r[bs], counts, perm, x.q[bs], x.k[bs], x.v[bs],
                                 None if gated else x.alpha[bs], x.beta[bs], c=c, nthreads=16,
                                 want_X=True, **kw)
-    # terms of each pivot value: the gated old value d_i h_ij and the rest
-    _, h_old, _ = wl.unpack_ragged(pool[bs], counts, d)
-    Xp = np.take_along_axis(ref["X"], perm[None, :, :, None], axis=2)  # physical rows
-    if gated:
-        dp = np.take_along_axis(gate[bs].astype(np.float64), perm[None], axis=2)[..., None]
-    else:
-        dp = x.alpha[bs].astype(np.float64)[:, :, None, None]
-    t1 = dp * h_old.view(np.float16).astype(np.float64)
-    pivot_err = 2.0 ** -20 * (np.abs(t1) + np.abs(Xp - t1))
+    pivot_err = pivot_allowance(pool[bs], counts, perm, ref["X"], d,
+                                alpha=None if gated else x.alpha[bs],
+                                gate=gate[bs] if gated else None)
     stats = _compare(gp[bs], gr[bs], ref["pool"], ref["r"], counts, d, "ragged full size",
                      o=go[bs], ref_o=ref["o"], pivot_err=pivot_err)
     print(stats)
