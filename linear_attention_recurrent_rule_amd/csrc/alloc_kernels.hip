@@ -12,9 +12,10 @@
 // parts), 4-bit (D/2), 2-bit (D/4, column j in bits 2(j%4) of byte j/4).
 // Codes are two's complement; pivot rows have r = 0 and no column factor.
 //
-// The decode kernel uses the lane decomposition of decode_mixed_kernel (lane
-// (g, c) owns columns 8c..8c+7 of rows g + (D/8) m) and the column-normalised
-// arithmetic x = X / c.  A pivot row enters that arithmetic as z_ij = h_ij /
+// The generic decode kernel here serves d = 16, 32, 64 (128 x 128 heads have
+// their own kernel in alloc128.hip).  It uses the lane decomposition of
+// decode_mixed_kernel (lane (g, c) owns columns 8c..8c+7 of rows g + (D/8) m)
+// and the column-normalised arithmetic x = X / c.  A pivot row enters that arithmetic as z_ij = h_ij /
 // c_j with a row factor of 1, so every row class shares the column sums, the
 // update and the readout; only loads, the row factor and the stores differ
 // per class.  Rows of one head are sorted by class, so a wave diverges only
@@ -729,22 +730,32 @@ template <int D> static unsigned alloc_unit_grid(long units) {
     return static_cast<unsigned>((units + Geo<D>::UPW - 1) / Geo<D>::UPW);
 }
 
+// The generic decode serves d = 16, 32, 64; 128 x 128 heads go to the
+// matrix-core kernel of alloc128.hip.
+#define STQ_ALLOC_DISPATCH_SMALL(D, CALL)                   \
+    switch (D) {                                            \
+    case 16: { constexpr int DD = 16; CALL; } break;        \
+    case 32: { constexpr int DD = 32; CALL; } break;        \
+    case 64: { constexpr int DD = 64; CALL; } break;        \
+    default: return hipErrorInvalidValue;                   \
+    }
+
 hipError_t launch_decode_alloc(int D, bool bf16, const DecodeArgs &a, hipStream_t s) {
     if (D == 128) return launch_decode_alloc128(bf16, a, s);
     const long units = static_cast<long>(a.B) * a.Hv;
     const bool refit = a.cs != nullptr;
     if (bf16 && refit) {
-        STQ_ALLOC_DISPATCH(D, hipLaunchKernelGGL((decode_alloc_kernel<DD, uint16_t, true>),
-                                                 dim3(alloc_unit_grid<DD>(units)), dim3(256), 0, s, a));
+        STQ_ALLOC_DISPATCH_SMALL(D, hipLaunchKernelGGL((decode_alloc_kernel<DD, uint16_t, true>),
+                                                       dim3(alloc_unit_grid<DD>(units)), dim3(256), 0, s, a));
     } else if (bf16) {
-        STQ_ALLOC_DISPATCH(D, hipLaunchKernelGGL((decode_alloc_kernel<DD, uint16_t, false>),
-                                                 dim3(alloc_unit_grid<DD>(units)), dim3(256), 0, s, a));
+        STQ_ALLOC_DISPATCH_SMALL(D, hipLaunchKernelGGL((decode_alloc_kernel<DD, uint16_t, false>),
+                                                       dim3(alloc_unit_grid<DD>(units)), dim3(256), 0, s, a));
     } else if (refit) {
-        STQ_ALLOC_DISPATCH(D, hipLaunchKernelGGL((decode_alloc_kernel<DD, float, true>),
-                                                 dim3(alloc_unit_grid<DD>(units)), dim3(256), 0, s, a));
+        STQ_ALLOC_DISPATCH_SMALL(D, hipLaunchKernelGGL((decode_alloc_kernel<DD, float, true>),
+                                                       dim3(alloc_unit_grid<DD>(units)), dim3(256), 0, s, a));
     } else {
-        STQ_ALLOC_DISPATCH(D, hipLaunchKernelGGL((decode_alloc_kernel<DD, float, false>),
-                                                 dim3(alloc_unit_grid<DD>(units)), dim3(256), 0, s, a));
+        STQ_ALLOC_DISPATCH_SMALL(D, hipLaunchKernelGGL((decode_alloc_kernel<DD, float, false>),
+                                                       dim3(alloc_unit_grid<DD>(units)), dim3(256), 0, s, a));
     }
     return hipGetLastError();
 }
