@@ -453,7 +453,17 @@ def main():
                    sample=f"{n_steps} successive full decode steps of the workload ({B * hv} "
                           f"units each, d={d}, n8={w.n8}) from a seeded random packed state, "
                           f"{dt:.1f}s wall on {threads} threads")
-        log(f"[bench] oracle: {cpu['value']:.0f} updates/s on {threads} threads")
+        # the same oracle on one thread, over the first 64 sequences of one step
+        nb = min(B, 64)
+        x = wl.workload_inputs(w, 0)
+        t1 = time.perf_counter()
+        oracle.step(p8[:nb], p4[:nb], r[:nb], ps.c, ps.perm, x.q[:nb], x.k[:nb], x.v[:nb],
+                    x.alpha[:nb], x.beta[:nb], n8=w.n8, nthreads=1)
+        dt1 = time.perf_counter() - t1
+        cpu["single_thread"] = dict(value=nb * hv / dt1, unit="state-updates/s", cores=1,
+                                    sample=f"one decode step of {nb * hv} units, {dt1:.2f}s")
+        log(f"[bench] oracle: {cpu['value']:.0f} updates/s on {threads} threads, "
+            f"{cpu['single_thread']['value']:.0f} on one")
 
     # -------------------------------------------------------- roofline etc --
     traffic = None
