@@ -31,6 +31,8 @@
 //    shift and one bit-field insert per 8 codes.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "stq_internal.h"
 
 namespace stq {
@@ -132,8 +134,15 @@ __device__ __forceinline__ unsigned udiv(unsigned n, unsigned d, unsigned m) {
     return q;
 }
 
+// N8 = kRuntimeN8 selects the instance whose 4/8-bit split is read at run
+// time (any n8): slot m of wave w holds rows 16 m + 4 w .. 16 m + 4 w + 3, so
+// a slot is all 8-bit, all 4-bit, or (at most one per wave) straddles n8;
+// the first two take a scalar branch, the last a per-lane one.
+constexpr int kRuntimeN8 = -1;
+
 struct Lane {
     int t, c, g;
+    int n8, wv;        // the split (runtime instance) and the wave, wave-uniform
     unsigned unit;
     float alpha, beta;
     const int8_t *p8;  // packed rows read ...
@@ -149,8 +158,39 @@ struct Lane {
 // once and written once per step and nothing reuses it within the step, so
 // its loads and stores carry the non-temporal hint (measured 5 % faster than
 // cached accesses at B = 1024).
+// Class of slot m for this wave in the runtime instance: 1 all 8-bit, 0 all
+// 4-bit, -1 straddling n8 (wave-uniform).
+__device__ __forceinline__ int slot_class(const Lane &L, int m) {
+    const int p0 = 16 * m + 4 * L.wv;
+    return p0 + 3 < L.n8 ? 1 : (p0 >= L.n8 ? 0 : -1);
+}
+
 template <int N8>
 __device__ __forceinline__ void load_codes(const Lane &L, uint32_t (&w0)[8], uint32_t (&w1)[8]) {
+    if constexpr (N8 == kRuntimeN8) {
+        // one 8-byte load per slot whatever its width (4-bit rows: the aligned
+        // 8 bytes holding the lane's 4), so no register is written by
+        // different loads on different paths; only the address depends on it
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int p = L.g + 16 * m;
+            const int k = slot_class(L, m);
+            const uint8_t *addr;
+            if (k == 1) {
+                addr = reinterpret_cast<const uint8_t *>(L.p8) + (16 * m * D) +
+                       static_cast<unsigned>(L.g * D + 8 * L.c);
+            } else if (k == 0) {
+                addr = L.p4 + ((16 * m - L.n8) * (D / 2)) +
+                       static_cast<unsigned>(L.g * (D / 2) + ((4 * L.c) & ~7));
+            } else {
+                addr = p < L.n8 ? reinterpret_cast<const uint8_t *>(L.p8) + (p * D + 8 * L.c)
+                                : L.p4 + ((p - L.n8) * (D / 2) + ((4 * L.c) & ~7));
+            }
+            const u32x2 v2 = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(addr));
+            w0[m] = v2[0];
+            w1[m] = v2[1];
+        }
+    } else {
     constexpr int M8 = N8 / 16;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
@@ -166,13 +206,14 @@ __device__ __forceinline__ void load_codes(const Lane &L, uint32_t (&w0)[8], uin
             w1[m] = 0u;
         }
     }
+    }
 }
 
 // Everything after the staging barrier.
 template <int N8, bool REFIT>
 __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const Lane &L,
                                             const uint32_t (&w0)[8], const uint32_t (&w1)[8]) {
-    constexpr int M8 = N8 / 16;
+    constexpr int M8 = N8 < 0 ? 0 : N8 / 16;
     const int t = L.t, c = L.c, g = L.g;
 
     // ---- widen the codes; column sums u~ = S~^T (r k), w~ = S~^T (r q) on the
@@ -185,11 +226,25 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
     float z[8][8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-        if (m < M8) {
+        bool is8 = m < M8;
+        if constexpr (N8 == kRuntimeN8) {
+            const int k = slot_class(L, m);
+            is8 = k == 1 || (k == -1 && g + 16 * m < L.n8);
+        }
+        if (is8) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 z[m][e] = sbyte(w0[m], e);
                 z[m][4 + e] = sbyte(w1[m], e);
+            }
+        } else if constexpr (N8 == kRuntimeN8) {
+            const uint32_t w4 = (c & 1) ? w1[m] : w0[m];     // the lane's 4 bytes
+            const uint32_t hi = w4 & 0xF0F0F0F0u;
+            const uint32_t lo = (w4 << 4) & 0xF0F0F0F0u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                z[m][2 * e] = sbyte(lo, e);
+                z[m][2 * e + 1] = sbyte(hi, e);
             }
         } else {
             const uint32_t hi = w0[m] & 0xF0F0F0F0u;         // odd columns, x16
@@ -315,7 +370,8 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
         const int p = g + 16 * mm;
         const float sc = sh.row[p].y;
         const float mrow = fabsf(sc) * rmax;
-        const float qinv = (mm < M8) ? (1.0f / 127.0f) : (1.0f / 7.0f);
+        const bool row8 = N8 == kRuntimeN8 ? p < L.n8 : mm < M8;
+        const float qinv = row8 ? (1.0f / 127.0f) : (1.0f / 7.0f);
         const float rn = fmaxf(mrow * qinv, kRowFloor);
         const float inv = __builtin_amdgcn_rcpf(rn);
         float mul = sc * inv;
@@ -357,38 +413,87 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
             rbv[e] = sh.rb[g][e];
         }
     }
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const unsigned p = static_cast<unsigned>(g + 16 * m);
-        uint32_t bt[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) bt[e] = __float_as_uint(__builtin_fmaf(z[m][e], mulv[m], kRoundMagic));
-        if (REFIT) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float zq = __uint_as_float(bt[e]) - kRoundMagic; // the code, exactly
-                num[e] = __builtin_fmaf(rav[m] * zq, z[m][e], num[e]);
-                den[e] = __builtin_fmaf(rbv[m] * zq, zq, den[e]);
-            }
+    if constexpr (N8 == kRuntimeN8) {
+        const int n8 = L.n8;
+    #pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const unsigned p = static_cast<unsigned>(g + 16 * m);
+            // codes, refit sums and the packed store of slot m; the whole body sits
+            // inside the width branch (in the runtime instance this keeps the
+            // codes of one slot live at a time)
+            auto emit = [&](auto W8) __attribute__((always_inline)) {
+                constexpr bool IS8 = decltype(W8)::value;
+                uint32_t bt[8];
+    #pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    bt[e] = __float_as_uint(__builtin_fmaf(z[m][e], mulv[m], kRoundMagic));
+                if (REFIT) {
+    #pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float zq = __uint_as_float(bt[e]) - kRoundMagic; // the code, exactly
+                        num[e] = __builtin_fmaf(rav[m] * zq, z[m][e], num[e]);
+                        den[e] = __builtin_fmaf(rbv[m] * zq, zq, den[e]);
+                    }
+                }
+                if constexpr (IS8) {
+                    const uint32_t a01 = __builtin_amdgcn_perm(bt[1], bt[0], 0x0C0C0400u);
+                    const uint32_t a23 = __builtin_amdgcn_perm(bt[3], bt[2], 0x04000C0Cu);
+                    const uint32_t a45 = __builtin_amdgcn_perm(bt[5], bt[4], 0x0C0C0400u);
+                    const uint32_t a67 = __builtin_amdgcn_perm(bt[7], bt[6], 0x04000C0Cu);
+                    __builtin_nontemporal_store(u32x2{a01 | a23, a45 | a67},
+                                                reinterpret_cast<u32x2 *>(L.q8 + (p * D + 8 * c)));
+                } else {
+                    // even columns -> low nibbles, odd columns -> high nibbles
+                    const uint32_t ev02 = __builtin_amdgcn_perm(bt[2], bt[0], 0x0C0C0400u);
+                    const uint32_t ev46 = __builtin_amdgcn_perm(bt[6], bt[4], 0x04000C0Cu);
+                    const uint32_t od13 = __builtin_amdgcn_perm(bt[3], bt[1], 0x0C0C0400u);
+                    const uint32_t od57 = __builtin_amdgcn_perm(bt[7], bt[5], 0x04000C0Cu);
+                    const uint32_t evn = ev02 | ev46;
+                    const uint32_t odd = (od13 | od57) << 4;
+                    const uint32_t word = (evn & 0x0F0F0F0Fu) | (odd & 0xF0F0F0F0u);
+                    __builtin_nontemporal_store(
+                        word,
+                        reinterpret_cast<uint32_t *>(L.q4 + ((static_cast<int>(p) - n8) * (D / 2) + 4 * c)));
+                }
+            };
+            const int k = slot_class(L, m);
+            if (k == 1 || (k == -1 && static_cast<int>(p) < n8)) emit(std::true_type{});
+            else emit(std::false_type{});
         }
-        if (m < M8) {
-            const uint32_t a01 = __builtin_amdgcn_perm(bt[1], bt[0], 0x0C0C0400u);
-            const uint32_t a23 = __builtin_amdgcn_perm(bt[3], bt[2], 0x04000C0Cu);
-            const uint32_t a45 = __builtin_amdgcn_perm(bt[5], bt[4], 0x0C0C0400u);
-            const uint32_t a67 = __builtin_amdgcn_perm(bt[7], bt[6], 0x04000C0Cu);
-            __builtin_nontemporal_store(u32x2{a01 | a23, a45 | a67},
-                                        reinterpret_cast<u32x2 *>(L.q8 + (p * D + 8 * c)));
-        } else {
-            // even columns -> low nibbles, odd columns -> high nibbles
-            const uint32_t ev02 = __builtin_amdgcn_perm(bt[2], bt[0], 0x0C0C0400u);
-            const uint32_t ev46 = __builtin_amdgcn_perm(bt[6], bt[4], 0x04000C0Cu);
-            const uint32_t od13 = __builtin_amdgcn_perm(bt[3], bt[1], 0x0C0C0400u);
-            const uint32_t od57 = __builtin_amdgcn_perm(bt[7], bt[5], 0x04000C0Cu);
-            const uint32_t evn = ev02 | ev46;
-            const uint32_t odd = (od13 | od57) << 4;
-            const uint32_t word = (evn & 0x0F0F0F0Fu) | (odd & 0xF0F0F0F0u);
-            __builtin_nontemporal_store(word,
-                                        reinterpret_cast<uint32_t *>(L.q4 + ((p - N8) * (D / 2) + 4 * c)));
+    } else {
+    #pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const unsigned p = static_cast<unsigned>(g + 16 * m);
+            uint32_t bt[8];
+    #pragma unroll
+            for (int e = 0; e < 8; ++e) bt[e] = __float_as_uint(__builtin_fmaf(z[m][e], mulv[m], kRoundMagic));
+            if (REFIT) {
+    #pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float zq = __uint_as_float(bt[e]) - kRoundMagic; // the code, exactly
+                    num[e] = __builtin_fmaf(rav[m] * zq, z[m][e], num[e]);
+                    den[e] = __builtin_fmaf(rbv[m] * zq, zq, den[e]);
+                }
+            }
+            if (m < M8) {
+                const uint32_t a01 = __builtin_amdgcn_perm(bt[1], bt[0], 0x0C0C0400u);
+                const uint32_t a23 = __builtin_amdgcn_perm(bt[3], bt[2], 0x04000C0Cu);
+                const uint32_t a45 = __builtin_amdgcn_perm(bt[5], bt[4], 0x0C0C0400u);
+                const uint32_t a67 = __builtin_amdgcn_perm(bt[7], bt[6], 0x04000C0Cu);
+                __builtin_nontemporal_store(u32x2{a01 | a23, a45 | a67},
+                                            reinterpret_cast<u32x2 *>(L.q8 + (p * D + 8 * c)));
+            } else {
+                // even columns -> low nibbles, odd columns -> high nibbles
+                const uint32_t ev02 = __builtin_amdgcn_perm(bt[2], bt[0], 0x0C0C0400u);
+                const uint32_t ev46 = __builtin_amdgcn_perm(bt[6], bt[4], 0x04000C0Cu);
+                const uint32_t od13 = __builtin_amdgcn_perm(bt[3], bt[1], 0x0C0C0400u);
+                const uint32_t od57 = __builtin_amdgcn_perm(bt[7], bt[5], 0x04000C0Cu);
+                const uint32_t evn = ev02 | ev46;
+                const uint32_t odd = (od13 | od57) << 4;
+                const uint32_t word = (evn & 0x0F0F0F0Fu) | (odd & 0xF0F0F0F0u);
+                __builtin_nontemporal_store(word,
+                                            reinterpret_cast<uint32_t *>(L.q4 + ((p - N8) * (D / 2) + 4 * c)));
+            }
         }
     }
     if (REFIT) {
@@ -421,7 +526,8 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
 template <int N8, typename TIn, bool REFIT, bool GATED>
 __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_remap, unsigned hv_m,
                                                         unsigned g_m) {
-    static_assert(N8 % 16 == 0 && N8 >= 0 && N8 <= D, "n8 must be a multiple of 16");
+    static_assert(N8 == kRuntimeN8 || (N8 % 16 == 0 && N8 >= 0 && N8 <= D),
+                  "n8 must be a multiple of 16 (or read at run time)");
     __shared__ Smem sh;
 
     Lane L;
@@ -450,11 +556,15 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
     L.alpha = GATED ? 1.0f : a.alpha[unit];
     L.beta = a.beta[unit];
     const size_t ub = static_cast<size_t>(slot) * Hv + h;
-    L.p8 = a.pool8 + ub * (N8 * D);
-    L.p4 = a.pool4 + ub * ((D - N8) * (D / 2));
+    const int n8 = N8 == kRuntimeN8 ? a.n8 : N8;
+    L.n8 = n8;
+    L.wv = 0;
+    if constexpr (N8 == kRuntimeN8) L.wv = __builtin_amdgcn_readfirstlane(t >> 6);
+    L.p8 = a.pool8 + ub * (n8 * D);
+    L.p4 = a.pool4 + ub * ((D - n8) * (D / 2));
     L.rr = a.r + ub * D;
-    L.q8 = a.pool8_out + ub * (N8 * D);
-    L.q4 = a.pool4_out + ub * ((D - N8) * (D / 2));
+    L.q8 = a.pool8_out + ub * (n8 * D);
+    L.q4 = a.pool4_out + ub * ((D - n8) * (D / 2));
     L.rw = a.r_out + ub * D;
     L.cw = REFIT ? a.cs_out + ub * D : nullptr;
 
@@ -476,7 +586,7 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
         const float qp = In<TIn>::get(a.q, kb + i);
         const float rp = rpv;
         // 4-bit codes are widened as 16 z; a row gate scales the whole row
-        float scale = p < N8 ? rp : rp * 0.0625f;
+        float scale = p < n8 ? rp : rp * 0.0625f;
         if (GATED) scale *= a.gate[static_cast<size_t>(unit) * D + i];
         {
             // row p = 4 w + gl + 16 m of wave w, lane group gl, slot m
@@ -553,7 +663,7 @@ hipError_t launch_n8(bool bf16, const DecodeArgs &a, hipStream_t s) {
 
 } // namespace
 
-bool decode128_supported(int n8) { return n8 >= 0 && n8 <= D && n8 % 16 == 0; }
+bool decode128_supported(int n8) { return n8 >= 0 && n8 <= D; }
 
 hipError_t launch_decode128(int n8, bool bf16, const DecodeArgs &a, hipStream_t s) {
     switch (n8) {
@@ -566,7 +676,7 @@ hipError_t launch_decode128(int n8, bool bf16, const DecodeArgs &a, hipStream_t 
     case 96: return launch_n8<96>(bf16, a, s);
     case 112: return launch_n8<112>(bf16, a, s);
     case 128: return launch_n8<128>(bf16, a, s);
-    default: return hipErrorInvalidValue;
+    default: return launch_n8<kRuntimeN8>(bf16, a, s);
     }
 }
 

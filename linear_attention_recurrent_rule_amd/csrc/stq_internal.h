@@ -107,7 +107,8 @@ constexpr int kCalChunks = 64;
 
 // Launchers (return hipSuccess or the launch error).  D in {16, 32, 64, 128}.
 hipError_t launch_decode_mixed(int D, bool bf16, const DecodeArgs &a, hipStream_t s);
-// 128 x 128 heads with n8 a multiple of 16 (compile-time row split).
+// 128 x 128 heads: a compile-time row split for n8 a multiple of 16, the
+// split read at run time otherwise.
 bool decode128_supported(int n8);
 hipError_t launch_decode128(int n8, bool bf16, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_fp32(int D, bool bf16, const DecodeArgs &a, hipStream_t s);

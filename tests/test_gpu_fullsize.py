@@ -18,9 +18,16 @@ if not torch.cuda.is_available():  # pragma: no cover
 from tests import gpu_util as gu  # noqa: E402
 
 
-@pytest.mark.parametrize("name", ["highconc_6bit", "highconc_4p5bit"])
-def test_fullsize_step_sampled_parity_and_properties(oracle_mod, name):
+@pytest.mark.parametrize("name,n8", [("highconc_6bit", None), ("highconc_4p5bit", None),
+                                     ("highconc_6bit", 40)])
+def test_fullsize_step_sampled_parity_and_properties(oracle_mod, name, n8):
+    """n8 = 40 takes the kernel instance that reads the 4/8-bit split at run
+    time."""
+    import dataclasses
+
     w = wl.WORKLOADS[name]
+    if n8 is not None:
+        w = dataclasses.replace(w, n8=n8)
     print(f"[case] {name}: B={w.B} hv={w.hv} hk={w.hk} d={w.d} n8={w.n8}", flush=True)
     ps = wl.random_packed_state(w.B, w.hv, w.d, w.n8, seed=w.seed + 500)
     x = wl.workload_inputs(w, 0)

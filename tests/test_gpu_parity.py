@@ -49,7 +49,10 @@ def _one_step(oracle_mod, B, hv, hk, d, n8, *, dtype, seed, nthreads=8, c_one=Fa
     (128, 16, 5, 32, 16),  # 4.5-bit mix
     (128, 128, 2, 4, 2),   # all 8-bit
     (128, 0, 2, 4, 2),     # all 4-bit
-    (128, 37, 3, 2, 1),    # ragged split
+    (128, 37, 3, 2, 1),    # ragged split (read at run time; one slot straddles it)
+    (128, 3, 4, 8, 4),     # runtime split straddling the first slot
+    (128, 124, 2, 4, 2),   # runtime split on a 4-row boundary (no straddle)
+    (128, 125, 3, 32, 16), # runtime split straddling the last slot
 ])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_step_parity_random_state(oracle_mod, d, n8, B, hv, hk, dtype):
