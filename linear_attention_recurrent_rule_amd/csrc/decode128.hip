@@ -1,5 +1,6 @@
-// Decode step specialised for 128 x 128 heads and a compile-time 4/8-bit row
-// split (n8 a multiple of 16): the serving shapes.  Same arithmetic contract as
+// Decode step specialised for 128 x 128 heads: the serving shapes, with a
+// compile-time 4/8-bit row split (n8 a multiple of 16) or, in one more
+// instance, the split read at run time (any n8).  Same arithmetic contract as
 // decode.hip (STEPQuant paper, Sec. 2.1 Eq. (1) with D_t = a I or, in the KDA
 // form, D_t = diag(d) over the key rows; Sec. 2.2 quantizer; Sec. 4.3
 // representation; App. C.3 Table C2 step order), arranged to keep the vector
@@ -13,7 +14,11 @@
 //  * one workgroup of 256 lanes per (slot, head); lane (g, c), g = lane / 16,
 //    c = lane % 16, owns columns 8c..8c+7 of physical rows g + 16 m, m = 0..7;
 //    with n8 a multiple of 16, row m of every lane is 8-bit iff m < n8 / 16,
-//    so the row width is a compile-time property of m and no lane diverges;
+//    so the row width is a compile-time property of m and no lane diverges
+//    (the runtime-split instance branches per slot on a wave-uniform test);
+//  * the packed state is streamed with non-temporal loads and stores, and
+//    perm and r are loaded before the codes (loads complete in issue order
+//    and the k and q gathers depend on perm);
 //  * per-row factors are formed once per row by the staging lanes and read
 //    from LDS: r k and r q (with 1/16 folded in for 4-bit rows, whose codes are
 //    widened as 16 z), and the update in the form
@@ -25,7 +30,8 @@
 //    the lane picks e or a zero vector per row by its LDS address;
 //  * the row absmax over the 16 lanes of a row is a DPP reduce-scatter that
 //    leaves row c / 2 in lane c, so each lane derives one row factor and its
-//    reciprocal, and the 8 multipliers are exchanged through LDS;
+//    reciprocal, and the 8 multipliers are exchanged through LDS inside the
+//    wave (a wave-level fence, no workgroup barrier);
 //  * codes: one FMA adds 1.5 * 2^23 (round-half-even to an integer in the low
 //    mantissa bits), then bytes are gathered with v_perm and nibbles with one
 //    shift and one bit-field insert per 8 codes.
