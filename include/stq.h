@@ -86,6 +86,10 @@ typedef enum {
 } stq_format;
 
 typedef enum { STQ_F32 = 0, STQ_BF16 = 1 } stq_dtype;
+/* OR'd into the dtype argument of the decode steps: the readout o is written
+ * in bf16 (rounded to nearest even from the fp32 readout; NaN for a skipped
+ * slot) instead of fp32 -- the form the layer's next product consumes. */
+#define STQ_OUT_BF16 0x100
 
 /* Calibration flags (stq_calibrate), combinable. */
 #define STQ_CAL_RESET 1u    /* zero the accumulated statistics first */
@@ -303,7 +307,8 @@ stq_status stq_pack_state(const stq_state *st, const float *S, const int32_t *sl
  *   r'_i = max(fl32(max_j |X_ij / c_j| / q_b), 2^-126);
  *   z'_ij = clip(rhe(X_ij / c_j / r'_i), -q_b, q_b)
  * REFIT format: c is the state's own cs, refit after the codes are taken.
- * q, k, v are fp32 or bf16 (`dtype`); alpha, beta and o are fp32.
+ * q, k, v are fp32 or bf16 (`dtype`); alpha and beta are fp32; o is fp32, or
+ * bf16 with STQ_OUT_BF16 in `dtype`.
  * Preconditions: slots distinct within a call (not checked on the device;
  * with STQ_CHECK_SLOTS set in the environment the host copies the slot list,
  * synchronising the stream, and returns STQ_E_ARG for a repeated slot);
@@ -313,7 +318,7 @@ stq_status stq_pack_state(const stq_state *st, const float *S, const int32_t *sl
  * STQ_E_DEVICE. */
 stq_status stq_decode_step(const stq_state *st, const int32_t *slots, int32_t B,
                            const void *q, const void *k, const void *v, int32_t dtype,
-                           const float *alpha, const float *beta, float *o,
+                           const float *alpha, const float *beta, void *o,
                            stq_stream_t stream);
 
 /* The same decode step, reading slots[b] of `src` and writing the updated
@@ -331,7 +336,7 @@ stq_status stq_decode_step(const stq_state *st, const int32_t *slots, int32_t B,
 stq_status stq_decode_step_into(const stq_state *src, const stq_state *dst,
                                 const int32_t *slots, int32_t B, const void *q,
                                 const void *k, const void *v, int32_t dtype,
-                                const float *alpha, const float *beta, float *o,
+                                const float *alpha, const float *beta, void *o,
                                 stq_stream_t stream);
 
 /* The decode step with a per-key-row gate (Sec. 2.1 Eq. (1) with
@@ -347,7 +352,7 @@ stq_status stq_decode_step_into(const stq_state *src, const stq_state *dst,
 stq_status stq_decode_step_gated(const stq_state *src, const stq_state *dst,
                                  const int32_t *slots, int32_t B, const void *q,
                                  const void *k, const void *v, int32_t dtype,
-                                 const float *gate, const float *beta, float *o,
+                                 const float *gate, const float *beta, void *o,
                                  stq_stream_t stream);
 
 /* Reconstruct S_ij = r_i c_j z_ij (Sec. 4.3) of slots[b] into fp32
@@ -370,7 +375,7 @@ const char *stq_status_str(int32_t status);
 /* Library ABI version (bumped on any change to the declarations above):
  * 2 since the REFIT format and its state fields; 3 since the per-key-row
  * gate entry points; 4 since the ALLOC formats (descriptor and state fields,
- * retention and assignment entry points). */
+ * retention and assignment entry points); 5 since STQ_OUT_BF16 (o is void *). */
 int32_t stq_abi_version(void);
 
 #ifdef __cplusplus

@@ -376,9 +376,9 @@ __global__ __launch_bounds__(256) void decode_alloc_kernel(DecodeArgs a) {
         s_e[ul][j] = e;
         const float ov = cc * __builtin_fmaf(alpha, w, (beta * kq) * e);
         if (live)
-            a.o[static_cast<size_t>(unit) * D + j] = ov;
+            store_o(a, static_cast<size_t>(unit) * D + j, ov);
         else if (active)
-            a.o[static_cast<size_t>(unit) * D + j] = __int_as_float(0x7fc00000);
+            store_o(a, static_cast<size_t>(unit) * D + j, __int_as_float(0x7fc00000));
     }
     __syncthreads();
 

@@ -324,8 +324,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
     // ---- Table C2 step 3: readout of the updated state, before requantizing
     if (t >= D) {
         const float kq = sh.kq[0] + sh.kq[1];
-        a.o[static_cast<size_t>(L.unit) * D + jcol] =
-            sh.c[jcol] * __builtin_fmaf(L.alpha, wsum, (L.beta * kq) * sh.ez[ezi]);
+        store_o(a, static_cast<size_t>(L.unit) * D + jcol, sh.c[jcol] * __builtin_fmaf(L.alpha, wsum, (L.beta * kq) * sh.ez[ezi]));
     }
 
     // ---- Table C2 steps 2 and 4: updated entries and row absmax
@@ -556,7 +555,7 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
     const int hk = static_cast<int>(udiv(static_cast<unsigned>(h), static_cast<unsigned>(Hv / a.Hk), g_m));
     const int slot = a.slots ? a.slots[b] : b;
     if (slot < 0 || slot >= a.n_slots) { // whole workgroup leaves together
-        if (t < D) a.o[static_cast<size_t>(unit) * D + t] = __int_as_float(0x7fc00000);
+        if (t < D) store_o(a, static_cast<size_t>(unit) * D + t, __int_as_float(0x7fc00000));
         return;
     }
     L.alpha = GATED ? 1.0f : a.alpha[unit];

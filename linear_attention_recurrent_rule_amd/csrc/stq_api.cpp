@@ -181,7 +181,7 @@ stq_status dev(hipError_t e) { return e == hipSuccess ? STQ_OK : STQ_E_DEVICE; }
 
 extern "C" {
 
-int32_t stq_abi_version(void) { return 4; }
+int32_t stq_abi_version(void) { return 5; }
 
 const char *stq_status_str(int32_t s) {
     switch (s) {
@@ -504,17 +504,19 @@ bool partial_overlap(const void *p, const void *q, size_t n) {
 // is non-null.
 stq_status decode(const stq_state *src, const stq_state *dst, const int32_t *slots, int32_t B,
                   const void *q, const void *k, const void *v, int32_t dtype, const float *alpha,
-                  const float *gate, const float *beta, float *o, stq_stream_t stream) {
+                  const float *gate, const float *beta, void *o, stq_stream_t stream) {
     stq_status e = batch_args(src, slots, B);
     if (e != STQ_OK) return e;
     if ((e = check_state(dst)) != STQ_OK) return e;
     if (!same_desc(src->desc, dst->desc)) return STQ_E_SHAPE;
+    const bool o_bf16 = (dtype & STQ_OUT_BF16) != 0;
+    dtype &= ~STQ_OUT_BF16;
     if (dtype != STQ_F32 && dtype != STQ_BF16) return STQ_E_ARG;
     const size_t el = dtype == STQ_F32 ? 4 : 2;
     const float *g_or_a = gate ? gate : alpha;
     if (!q || !k || !v || !g_or_a || !beta || !o) return STQ_E_ARG;
     if (!aligned(q, el) || !aligned(k, el) || !aligned(v, el) || !aligned(g_or_a, 4) ||
-        !aligned(beta, 4) || !aligned(o, 4))
+        !aligned(beta, 4) || !aligned(o, o_bf16 ? 2 : 4))
         return STQ_E_ARG;
     if (calibrated_format(src->desc.fmt) && !src->calibrated) return STQ_E_STATE;
     if ((e = check_slots_distinct(slots, B, src->desc.n_slots, static_cast<hipStream_t>(stream))) !=
@@ -548,7 +550,8 @@ stq_status decode(const stq_state *src, const stq_state *dst, const int32_t *slo
     a.alpha = gate ? nullptr : alpha;
     a.gate = gate;
     a.beta = beta;
-    a.o = o;
+    a.o = static_cast<float *>(o);
+    a.o_bf16 = o_bf16 ? 1 : 0;
     a.B = B;
     a.Hv = src->desc.n_heads_v;
     a.Hk = src->desc.n_heads_k;
@@ -567,14 +570,14 @@ stq_status decode(const stq_state *src, const stq_state *dst, const int32_t *slo
 
 stq_status stq_decode_step(const stq_state *st, const int32_t *slots, int32_t B, const void *q,
                            const void *k, const void *v, int32_t dtype, const float *alpha,
-                           const float *beta, float *o, stq_stream_t stream) {
+                           const float *beta, void *o, stq_stream_t stream) {
     if (!alpha) return STQ_E_ARG;
     return decode(st, st, slots, B, q, k, v, dtype, alpha, nullptr, beta, o, stream);
 }
 
 stq_status stq_decode_step_into(const stq_state *src, const stq_state *dst, const int32_t *slots,
                                 int32_t B, const void *q, const void *k, const void *v,
-                                int32_t dtype, const float *alpha, const float *beta, float *o,
+                                int32_t dtype, const float *alpha, const float *beta, void *o,
                                 stq_stream_t stream) {
     if (!src || !dst || !alpha) return STQ_E_ARG;
     return decode(src, dst, slots, B, q, k, v, dtype, alpha, nullptr, beta, o, stream);
@@ -582,7 +585,7 @@ stq_status stq_decode_step_into(const stq_state *src, const stq_state *dst, cons
 
 stq_status stq_decode_step_gated(const stq_state *src, const stq_state *dst, const int32_t *slots,
                                  int32_t B, const void *q, const void *k, const void *v,
-                                 int32_t dtype, const float *gate, const float *beta, float *o,
+                                 int32_t dtype, const float *gate, const float *beta, void *o,
                                  stq_stream_t stream) {
     if (!src || !dst || !gate) return STQ_E_ARG;
     return decode(src, dst, slots, B, q, k, v, dtype, nullptr, gate, beta, o, stream);

@@ -29,14 +29,26 @@ struct DecodeArgs {
     const void *v;        // [B][Hv][D]
     const float *alpha;   // [B][Hv] scalar gate (null when gate is given)
     const float *beta;    // [B][Hv]
-    float *o;             // [B][Hv][D]
+    float *o;             // [B][Hv][D] fp32, or bf16 when o_bf16
     int32_t B, Hv, Hk, n8, n_slots;
     const float *gate;    // [B][Hv][D] per-key-row gate, logical rows, or null
+    int32_t o_bf16;       // readout written as bf16 (RNE) instead of fp32
     // ragged row classes (ALLOC formats): pool8 / pool8_out are the byte
     // pools [n_slots][slot_bytes]; layout [Hv][kLayoutStride]
     const int32_t *layout;
     int64_t slot_bytes;
 };
+
+// Store readout element idx in the requested precision (wave-uniform choice).
+__device__ __forceinline__ void store_o(const DecodeArgs &a, size_t idx, float v) {
+    if (a.o_bf16) {
+        const uint32_t u = __builtin_bit_cast(uint32_t, v);
+        const uint32_t h = (v != v) ? 0x7FC0u : ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+        reinterpret_cast<uint16_t *>(a.o)[idx] = static_cast<uint16_t>(h);
+    } else {
+        a.o[idx] = v;
+    }
+}
 
 // Pack / dequant of B slots.
 struct PackArgs {

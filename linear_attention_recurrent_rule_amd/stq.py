@@ -22,6 +22,7 @@ STATUS_NAMES = {0: "STQ_OK", 1: "STQ_E_ARG", 2: "STQ_E_SHAPE", 3: "STQ_E_UNSUPPO
 
 FMT_MIXED48, FMT_INT8ROW, FMT_FP32, FMT_REFIT, FMT_ALLOC, FMT_ALLOC_REFIT = 0, 1, 2, 3, 4, 5
 F32, BF16 = 0, 1
+OUT_BF16 = 0x100  # readout written in bf16 (STQ_OUT_BF16)
 CAL_RESET, CAL_COLS, CAL_ROWS, CAL_FINALIZE, CAL_DIST = 1, 2, 4, 8, 16
 # ragged row classes (ALLOC formats): FP16 pivots, 8, 6, 4, 2 bits
 CLASS_BITS = (16, 8, 6, 4, 2)
@@ -334,19 +335,23 @@ class State:
                                      _dev_ptr(slots, "slots"), B, _stream(stream)),
                "stq_pack_state")
 
-    def decode_step(self, q, k, v, alpha, beta, o=None, slots=None, stream=None):
-        if q.dtype == torch.float32:
-            dt = F32
-        elif q.dtype == torch.bfloat16:
-            dt = BF16
-        else:
-            raise ValueError("q, k, v must be float32 or bfloat16")
-        if k.dtype != q.dtype or v.dtype != q.dtype:
-            raise ValueError("q, k, v must share one dtype")
-        B = int(q.shape[0])
+    def _readout(self, q, k, v, o, o_dtype):
+        """The readout buffer (allocated when o is None, in o_dtype: fp32 by
+        default) and the dtype argument: the input dtype, with STQ_OUT_BF16
+        when o is bf16."""
+        dt = _in_dtype(q, k, v)
         if o is None:
-            o = torch.empty((B, self.geo.n_heads_v, self.geo.d), dtype=torch.float32,
-                            device=q.device)
+            o = torch.empty((int(q.shape[0]), self.geo.n_heads_v, self.geo.d),
+                            dtype=o_dtype or torch.float32, device=q.device)
+        if o.dtype == torch.bfloat16:
+            dt |= OUT_BF16
+        elif o.dtype != torch.float32:
+            raise ValueError("o must be float32 or bfloat16")
+        return o, dt
+
+    def decode_step(self, q, k, v, alpha, beta, o=None, slots=None, stream=None, o_dtype=None):
+        B = int(q.shape[0])
+        o, dt = self._readout(q, k, v, o, o_dtype)
         _check(_lib().stq_decode_step(ctypes.byref(self.c_state), _dev_ptr(slots, "slots"), B,
                                       _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), dt,
                                       _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
@@ -354,20 +359,10 @@ class State:
         return o
 
     def decode_step_into(self, dst: "State", q, k, v, alpha, beta, o=None, slots=None,
-                         stream=None):
+                         stream=None, o_dtype=None):
         """Decode reading this state and writing the updated one into `dst`."""
-        if q.dtype == torch.float32:
-            dt = F32
-        elif q.dtype == torch.bfloat16:
-            dt = BF16
-        else:
-            raise ValueError("q, k, v must be float32 or bfloat16")
-        if k.dtype != q.dtype or v.dtype != q.dtype:
-            raise ValueError("q, k, v must share one dtype")
         B = int(q.shape[0])
-        if o is None:
-            o = torch.empty((B, self.geo.n_heads_v, self.geo.d), dtype=torch.float32,
-                            device=q.device)
+        o, dt = self._readout(q, k, v, o, o_dtype)
         _check(_lib().stq_decode_step_into(ctypes.byref(self.c_state), ctypes.byref(dst.c_state),
                                            _dev_ptr(slots, "slots"), B, _dev_ptr(q, "q"),
                                            _dev_ptr(k, "k"), _dev_ptr(v, "v"), dt,
@@ -377,14 +372,11 @@ class State:
         return o
 
     def decode_step_gated(self, q, k, v, gate, beta, o=None, slots=None, stream=None,
-                          dst: "State | None" = None):
+                          dst: "State | None" = None, o_dtype=None):
         """Decode with a per-key-row gate [B][Hv][d] (logical rows, fp32),
         in place or, with dst, into another state (stq_decode_step_gated)."""
-        dt = _in_dtype(q, k, v)
         B = int(q.shape[0])
-        if o is None:
-            o = torch.empty((B, self.geo.n_heads_v, self.geo.d), dtype=torch.float32,
-                            device=q.device)
+        o, dt = self._readout(q, k, v, o, o_dtype)
         target = self if dst is None else dst
         _check(_lib().stq_decode_step_gated(ctypes.byref(self.c_state),
                                             ctypes.byref(target.c_state),

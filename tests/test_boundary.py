@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert "stq_decode_step" in names and len(names) >= 8
     for n in names:
         assert hasattr(lib, n), f"libstq.so does not export {n}"
-    assert lib.stq_abi_version() == 4
+    assert lib.stq_abi_version() == 5
 
 
 def _desc(n_slots=4, hv=4, hk=2, d=64, n8=32, fmt=stq.FMT_MIXED48, dv=None, nominal=0, piv=0):
@@ -127,6 +127,12 @@ def test_decode_rejections():
     assert _decode(st, ptrs=[FAKE, FAKE, None, FAKE, FAKE, FAKE]) == E_ARG
     assert _decode(st, ptrs=[FAKE + 1, FAKE, FAKE, FAKE, FAKE, FAKE], dtype=1) == E_ARG
     assert _decode(st, slots=FAKE + 2) == E_ARG
+    # bf16 readout: the flag combines with an input dtype only; o needs 2-byte
+    # alignment with it and 4-byte alignment without it
+    assert _decode(st, dtype=stq.OUT_BF16 | 2) == E_ARG
+    assert _decode(st, dtype=stq.OUT_BF16 | 0x200) == E_ARG
+    assert _decode(st, ptrs=[FAKE] * 5 + [FAKE + 1], dtype=stq.OUT_BF16) == E_ARG
+    assert _decode(st, ptrs=[FAKE] * 5 + [FAKE + 2]) == E_ARG
     bad = _fake_state(calibrated=1)
     bad.pool8 = None
     assert _decode(bad) == E_ARG
@@ -221,6 +227,7 @@ def test_refit_layout_and_rejections():
     assert ci(st, 2, stq.CAL_COLS) == E_ARG
     assert ci(st, 2, 0, q=None) == E_ARG
     assert ci(st, 2, 0, dtype=5) == E_ARG
+    assert ci(st, 2, 0, dtype=stq.OUT_BF16) == E_ARG  # no readout here
     assert ci(st, 2, 0, q=FAKE + 2) == E_ARG
     mixed_st = _fake_state(calibrated=1)
     assert ci(mixed_st, 0, stq.CAL_RESET) == E_ARG
