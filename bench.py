@@ -112,13 +112,13 @@ def unit_state_bytes(fmt: str, d: int, n8: int) -> int:
 
 
 def algorithmic_bytes(fmt: str, B: int, hv: int, hk: int, d: int, n8: int, in_el: int,
-                      gated: bool = False) -> int:
+                      gated: bool = False, out_el: int = 4) -> int:
     """Bytes one decode launch must move: read + write of every state, q and k
     once per key head, v, alpha (or the fp32 row gate), beta once per value
-    head, o written once."""
+    head, o written once (out_el bytes per element)."""
     state = 2 * unit_state_bytes(fmt, d, n8) * B * hv
     gate = 4 * d if gated else 4
-    vecs = B * hk * 2 * d * in_el + B * hv * (d * in_el + gate + 4 + 4 * d)
+    vecs = B * hk * 2 * d * in_el + B * hv * (d * in_el + gate + 4 + out_el * d)
     return state + vecs
 
 
@@ -274,7 +274,8 @@ def main():
         if gated_:
             a = dev(wl.draw_gate(B, hv, d, seed=w.calib_seed, step=t))
         return q, k, v, a, b
-    o = torch.empty((B, hv, d), dtype=torch.float32, device="cuda")
+    o_f32 = torch.empty((B, hv, d), dtype=torch.float32, device="cuda")
+    o = o_f32
 
     alloc_cal = {}  # gated -> (counts, c, perm, w2) of the ragged format
 
@@ -361,15 +362,17 @@ def main():
         return total_ms, total_ms / steps
 
     def measure(fmt_name: str, fmt: int, n8: int, npools: int, steps: int, warmup: int,
-                into: bool = False, gated: bool = False):
-        nonlocal gates
+                into: bool = False, gated: bool = False, out_bf16: bool = False):
+        nonlocal gates, o
+        o = torch.empty((B, hv, d), dtype=torch.bfloat16, device="cuda") if out_bf16 else o_f32
         pools = make_pools(fmt, n8, npools, gated)
         if gated:  # per-key-row gates of the KDA form, one per window step
             gates = [dev(wl.draw_gate(B, hv, d, seed=w.seed, step=t))
                      for t in range(len(window))]
         total_ms, mean_ms = time_decode(pools, steps, warmup, into)
         gates = None
-        nbytes = algorithmic_bytes(fmt_name, B, hv, hk, d, n8, in_el, gated)
+        o = o_f32
+        nbytes = algorithmic_bytes(fmt_name, B, hv, hk, d, n8, in_el, gated, 2 if out_bf16 else 4)
         if fmt in (stq.FMT_ALLOC, stq.FMT_ALLOC_REFIT):
             unit = alloc_unit_bytes(alloc_cal[gated][0], d)
             nbytes = int(2 * unit * B * hv) + algorithmic_bytes("fp32", B, hv, hk, d, 0, in_el,
@@ -412,6 +415,9 @@ def main():
         if d == 128 and w.n8 % 16 == 0 and want("refit_column_factors"):
             variants["refit_column_factors"] = measure("refit", stq.FMT_REFIT, w.n8, args.pools,
                                                        args.steps, args.warmup)
+        if want("bf16_readout"):
+            variants["bf16_readout"] = measure("mixed", stq.FMT_MIXED48, w.n8, args.pools,
+                                               args.steps, args.warmup, out_bf16=True)
         if want("row_gate_kda"):
             variants["row_gate_kda"] = measure("mixed", stq.FMT_MIXED48, w.n8, args.pools,
                                                args.steps, args.warmup, gated=True)

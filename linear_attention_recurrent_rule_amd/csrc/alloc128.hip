@@ -12,6 +12,10 @@
 //    class, so those four rows almost always share one class: the wave then
 //    branches on a scalar class and runs the code of that class; only a slot
 //    that straddles a class boundary takes a per-lane branch;
+//  * the per-unit vectors (perm, r, k, q, v, c, gate) are loaded before the
+//    codes at addresses that depend on no other load: k and q are read in
+//    logical order, two entries per lane, and brought into physical row order
+//    by lane permutes instead of a gather through perm;
 //  * integer codes are widened so that every class fits a signed byte: 8-bit
 //    codes as z, 6-bit as 4 z, 4-bit as 16 z, 2-bit as 64 z (the row
 //    coefficients carry the inverse power of two);
@@ -41,16 +45,20 @@ constexpr float kMulMax = 1.70141183460469231732e38f;    // 2^127
 constexpr float kFormTiny = 5.42101086242752217004e-20f; // 2^-64
 constexpr float kHalfMax = 65504.0f;
 
+// Input elements as raw bits (a load whose result is only moved does not
+// wait for it) and their fp32 value.
 template <typename T> struct In;
 template <> struct In<float> {
-    static __device__ __forceinline__ float get(const void *p, unsigned i) {
-        return static_cast<const float *>(p)[i];
+    static __device__ __forceinline__ uint32_t raw(const void *p, unsigned i) {
+        return static_cast<const uint32_t *>(p)[i];
     }
+    static __device__ __forceinline__ float cvt(uint32_t bits) { return __uint_as_float(bits); }
 };
 template <> struct In<uint16_t> {
-    static __device__ __forceinline__ float get(const void *p, unsigned i) {
-        return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(p)[i]) << 16);
+    static __device__ __forceinline__ uint32_t raw(const void *p, unsigned i) {
+        return static_cast<const uint16_t *>(p)[i];
     }
+    static __device__ __forceinline__ float cvt(uint32_t bits) { return __uint_as_float(bits << 16); }
 };
 
 // Bytes per row of each class (pivot, 8, 6, 4, 2 bits).
@@ -386,11 +394,39 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
     float *rw = a.r_out + ub * D;
 
     const unsigned tab = slot_table(L, wv, t);
-    // ---- perm and r before the codes: the gathers of k and q depend on perm,
-    // and loads complete in the order they are issued (every lane loads, so
-    // no branch holds the results back)
-    int praw = a.perm[h * D + (t & (D - 1))];
-    float rpv = rr[t & (D - 1)];
+    // ---- the per-unit vectors, loaded at logical indices so that no load
+    // waits for another one (the gathers through perm are lane permutes
+    // below); they are issued before the codes, because loads complete in
+    // the order they are issued.  Waves 0 and 1 (lanes below D) each load
+    // all 128 entries of k and q (two per lane), the others v and c.
+    const int tl = t & (D - 1);
+    const int l64 = t & 63;
+    const bool lowhalf = wv < 2;
+    const unsigned kb = static_cast<unsigned>((b * a.Hk + hk) * D);
+    const int praw = a.perm[h * D + tl];
+    const float rpv = rr[tl];
+    // raw bits only: widening here would make the branch wait for the loads
+    uint32_t x0, x1, x2 = 0u, x3 = 0u, g0 = 0u, g1 = 0u, u0 = 0u, u1 = 0u;
+    if (lowhalf) {
+        x0 = In<TIn>::raw(a.k, kb + l64);
+        x1 = In<TIn>::raw(a.k, kb + 64 + l64);
+        x2 = In<TIn>::raw(a.q, kb + l64);
+        x3 = In<TIn>::raw(a.q, kb + 64 + l64);
+        if (GATED) {
+            const uint32_t *gp = reinterpret_cast<const uint32_t *>(a.gate) + static_cast<size_t>(unit) * D;
+            g0 = gp[l64];
+            g1 = gp[64 + l64];
+        }
+        if (REFIT) {
+            const uint32_t *wp = reinterpret_cast<const uint32_t *>(a.w2) + h * D;
+            u0 = wp[l64];
+            u1 = wp[64 + l64];
+        }
+    } else {
+        x0 = In<TIn>::raw(a.v, static_cast<unsigned>((b * Hv + h) * D + tl));
+        x1 = REFIT ? reinterpret_cast<const uint32_t *>(a.cs)[ub * D + tl]
+                   : reinterpret_cast<const uint32_t *>(a.c)[h * D + tl];
+    }
 
     // ---- Table C2 step 1: issue the loads of this lane's row chunks
     uint32_t ld[8][4]; // per slot: A.x, A.y, B.x, B.y
@@ -411,18 +447,23 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
     }
 
     // ---- per-row and per-column factors, once per unit
-    if (t < D) {
-        asm volatile("" : "+v"(praw), "+v"(rpv));
+    if (lowhalf) {
         const int p = t;
         const int k = class_of(L, p);
         const int i = praw & (D - 1);
-        const unsigned kb = static_cast<unsigned>((b * a.Hk + hk) * D);
-        const float kp = In<TIn>::get(a.k, kb + i);
-        const float qp = In<TIn>::get(a.q, kb + i);
+        const int src = (i & 63) << 2;
+        const bool up = (i & 64) != 0;
+        auto pick = [&](uint32_t lo, uint32_t hi) {
+            const uint32_t a0 = __builtin_amdgcn_ds_bpermute(src, static_cast<int>(lo));
+            const uint32_t a1 = __builtin_amdgcn_ds_bpermute(src, static_cast<int>(hi));
+            return up ? a1 : a0;
+        };
+        const float kp = In<TIn>::cvt(pick(x0, x1));
+        const float qp = In<TIn>::cvt(pick(x2, x3));
         // integer rows: r / W (codes are widened as W z); pivot rows: 1
         const float winv = k == 1 ? 1.0f : (k == 2 ? 0.25f : (k == 3 ? 0.0625f : 0.015625f));
         float scale = k == 0 ? 1.0f : rpv * winv;
-        if (GATED) scale *= a.gate[static_cast<size_t>(unit) * D + i];
+        if (GATED) scale *= __uint_as_float(pick(g0, g1));
         {
             uint16_t(&cf)[kCoefRows][8] = sh.coef[(p & 15) >> 2][p & 3];
             const int mm = p >> 4;
@@ -443,7 +484,8 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
         const float ar = alpha * scale;
         const float bk = beta * kp;
         const bool scaled = fabsf(bk) > fabsf(ar) * kFormTiny;
-        const float w2 = (REFIT && k != 0) ? a.w2[h * D + i] : 0.0f;
+        const float w2v = REFIT ? __uint_as_float(pick(u0, u1)) : 0.0f;
+        const float w2 = k != 0 ? w2v : 0.0f;
         sh.row[p] = make_float4(scaled ? ar * __builtin_amdgcn_rcpf(bk) : ar, scaled ? bk : 1.0f, w2,
                                 __int_as_float(scaled ? 0 : D));
         sh.qinv[p] = k == 0 ? 0.0f
@@ -455,9 +497,9 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
         // (a use on this side too, so the compiler keeps the two loads ahead
         // of the code loads instead of sinking them into the branch above)
         asm volatile("" ::"v"(praw), "v"(rpv));
-        const int j = t - D;
-        sh.v[j] = In<TIn>::get(a.v, static_cast<unsigned>((b * Hv + h) * D + j));
-        sh.c[j] = REFIT ? a.cs[ub * D + j] : a.c[h * D + j];
+        const int j = tl;
+        sh.v[j] = In<TIn>::cvt(x0);
+        sh.c[j] = __uint_as_float(x1);
         sh.ez[D + j] = 0.0f;
         if (j < 16)
             *reinterpret_cast<uint4 *>(&sh.coef[j >> 2][j & 3][kCoefRows - 1][0]) =

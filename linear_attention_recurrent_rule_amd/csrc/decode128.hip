@@ -16,9 +16,12 @@
 //    with n8 a multiple of 16, row m of every lane is 8-bit iff m < n8 / 16,
 //    so the row width is a compile-time property of m and no lane diverges
 //    (the runtime-split instance branches per slot on a wave-uniform test);
-//  * the packed state is streamed with non-temporal loads and stores, and
-//    perm and r are loaded before the codes (loads complete in issue order
-//    and the k and q gathers depend on perm);
+//  * the packed state is streamed with non-temporal loads and stores; the
+//    per-unit vectors (perm, r, k, q, v, c, gate) are loaded before the codes
+//    (loads complete in issue order) at addresses that depend on no other
+//    load: k and q are read in logical order, two entries per lane, and
+//    brought into physical row order by lane permutes instead of a gather
+//    through perm;
 //  * per-row factors are formed once per row by the staging lanes and read
 //    from LDS: r k and r q (with 1/16 folded in for 4-bit rows, whose codes are
 //    widened as 16 z), and the update in the form
@@ -55,11 +58,21 @@ template <> struct In<float> {
     static __device__ __forceinline__ float get(const void *p, unsigned i) {
         return static_cast<const float *>(p)[i];
     }
+    static __device__ __forceinline__ uint32_t raw(const void *p, unsigned i) {
+        return static_cast<const uint32_t *>(p)[i];
+    }
+    static __device__ __forceinline__ float cvt(uint32_t bits) { return __uint_as_float(bits); }
 };
 template <> struct In<uint16_t> {
     static __device__ __forceinline__ float get(const void *p, unsigned i) {
         return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(p)[i]) << 16);
     }
+    // the element's bits, widened later (a load whose result is only moved
+    // does not wait for it)
+    static __device__ __forceinline__ uint32_t raw(const void *p, unsigned i) {
+        return static_cast<const uint16_t *>(p)[i];
+    }
+    static __device__ __forceinline__ float cvt(uint32_t bits) { return __uint_as_float(bits << 16); }
 };
 
 __device__ __forceinline__ float sbyte(uint32_t w, int k) {
@@ -573,26 +586,59 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
     L.rw = a.r_out + ub * D;
     L.cw = REFIT ? a.cs_out + ub * D : nullptr;
 
-    // ---- perm and r before the codes: the gathers of k and q depend on perm,
-    // and loads complete in the order they are issued (every lane loads, so
-    // no branch holds the results back)
-    int praw = a.perm[h * D + (t & (D - 1))];
-    float rpv = L.rr[t & (D - 1)];
+    // ---- the per-unit vectors, loaded at logical indices so that no load
+    // waits for another one (the gathers through perm are lane permutes
+    // below); they are issued before the codes, because loads complete in
+    // the order they are issued.  Waves 0 and 1 (lanes below D) each load
+    // all 128 entries of k and q (two per lane), the others v and c.
+    const int tl = t & (D - 1);
+    const int l64 = t & 63;
+    const bool lowhalf = __builtin_amdgcn_readfirstlane(t) < D; // wave-uniform
+    const unsigned kb = static_cast<unsigned>((b * a.Hk + hk) * D);
+    const int praw = a.perm[h * D + tl];
+    const float rpv = L.rr[tl];
+    // raw bits only: widening here would make the branch wait for the loads
+    uint32_t x0, x1, x2 = 0u, x3 = 0u, g0 = 0u, g1 = 0u, u0 = 0u, u1 = 0u;
+    if (lowhalf) {
+        x0 = In<TIn>::raw(a.k, kb + l64);
+        x1 = In<TIn>::raw(a.k, kb + 64 + l64);
+        x2 = In<TIn>::raw(a.q, kb + l64);
+        x3 = In<TIn>::raw(a.q, kb + 64 + l64);
+        if (GATED) {
+            const uint32_t *gp = reinterpret_cast<const uint32_t *>(a.gate) + static_cast<size_t>(unit) * D;
+            g0 = gp[l64];
+            g1 = gp[64 + l64];
+        }
+        if (REFIT) {
+            const uint32_t *wp = reinterpret_cast<const uint32_t *>(a.w2) + h * D;
+            u0 = wp[l64];
+            u1 = wp[64 + l64];
+        }
+    } else {
+        x0 = In<TIn>::raw(a.v, static_cast<unsigned>((b * Hv + h) * D + tl));
+        x1 = REFIT ? reinterpret_cast<const uint32_t *>(a.cs)[ub * D + tl]
+                   : reinterpret_cast<const uint32_t *>(a.c)[h * D + tl];
+    }
     // ---- Table C2 step 1: issue the loads of this lane's packed rows
     uint32_t w0[8], w1[8];
     load_codes<N8>(L, w0, w1);
-    // ---- per-row and per-column factors, once per unit
-    if (t < D) {
-        asm volatile("" : "+v"(praw), "+v"(rpv));
+    if (lowhalf) {
+        // ---- per-row and per-column factors, once per unit
         const int p = t;
         const int i = praw & (D - 1);
-        const unsigned kb = static_cast<unsigned>((b * a.Hk + hk) * D);
-        const float kp = In<TIn>::get(a.k, kb + i);
-        const float qp = In<TIn>::get(a.q, kb + i);
+        const int src = (i & 63) << 2;
+        const bool up = (i & 64) != 0;
+        auto pick = [&](uint32_t lo, uint32_t hi) {
+            const uint32_t a0 = __builtin_amdgcn_ds_bpermute(src, static_cast<int>(lo));
+            const uint32_t a1 = __builtin_amdgcn_ds_bpermute(src, static_cast<int>(hi));
+            return up ? a1 : a0;
+        };
+        const float kp = In<TIn>::cvt(pick(x0, x1));
+        const float qp = In<TIn>::cvt(pick(x2, x3));
         const float rp = rpv;
         // 4-bit codes are widened as 16 z; a row gate scales the whole row
         float scale = p < n8 ? rp : rp * 0.0625f;
-        if (GATED) scale *= a.gate[static_cast<size_t>(unit) * D + i];
+        if (GATED) scale *= __uint_as_float(pick(g0, g1));
         {
             // row p = 4 w + gl + 16 m of wave w, lane group gl, slot m
             uint16_t(&cf)[7][8] = sh.coef[(p & 15) >> 2][p & 3];
@@ -611,7 +657,7 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
         const float bk = L.beta * kp;
         // |b k| > 2^-64 |a r| (false when both vanish: then x = 0 * z = 0)
         const bool scaled = fabsf(bk) > fabsf(ar) * kFormTiny;
-        const float w2 = REFIT ? a.w2[h * D + i] : 0.0f;
+        const float w2 = REFIT ? __uint_as_float(pick(u0, u1)) : 0.0f;
         sh.row[p] = make_float4(scaled ? ar * __builtin_amdgcn_rcpf(bk) : ar, scaled ? bk : 1.0f, w2,
                                 __int_as_float(scaled ? 0 : D));
         const float kq = wave_sum(kp * qp);
@@ -620,9 +666,9 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
         // (a use on this side too, so the compiler keeps the two loads ahead
         // of the code loads instead of sinking them into the branch above)
         asm volatile("" ::"v"(praw), "v"(rpv));
-        const int j = t - D;
-        sh.v[j] = In<TIn>::get(a.v, static_cast<unsigned>((b * Hv + h) * D + j));
-        sh.c[j] = REFIT ? a.cs[ub * D + j] : a.c[h * D + j];
+        const int j = tl;
+        sh.v[j] = In<TIn>::cvt(x0);
+        sh.c[j] = __uint_as_float(x1);
         sh.ez[D + j] = 0.0f;
         if (j < 16) *reinterpret_cast<uint4 *>(&sh.coef[j >> 2][j & 3][6][0]) = make_uint4(0u, 0u, 0u, 0u);
     }
