@@ -228,7 +228,7 @@ __device__ __forceinline__ void load_codes(const Lane &L, uint32_t (&w0)[8], uin
     }
 }
 
-// Everything after the staging barrier.
+// Everything after the barrier that follows the per-row factors.
 template <int N8, bool REFIT>
 __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const Lane &L,
                                             const uint32_t (&w0)[8], const uint32_t (&w1)[8]) {
