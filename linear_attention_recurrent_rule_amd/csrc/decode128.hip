@@ -245,25 +245,45 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
     float z[8][8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-        bool is8 = m < M8;
         if constexpr (N8 == kRuntimeN8) {
+            // the slot's class is wave-uniform (a scalar branch) except in
+            // the one slot that straddles n8; there each lane selects, with
+            // no branch, the two words whose bytes are its eight codes
             const int k = slot_class(L, m);
-            is8 = k == 1 || (k == -1 && g + 16 * m < L.n8);
+            const uint32_t w4 = (c & 1) ? w1[m] : w0[m]; // a 4-bit row's 4 bytes
+            const uint32_t hi = w4 & 0xF0F0F0F0u;          // odd columns, x16
+            const uint32_t lo = (w4 << 4) & 0xF0F0F0F0u;   // even columns, x16
+            if (k == 1) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    z[m][e] = sbyte(w0[m], e);
+                    z[m][4 + e] = sbyte(w1[m], e);
+                }
+            } else if (k == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    z[m][2 * e] = sbyte(lo, e);
+                    z[m][2 * e + 1] = sbyte(hi, e);
+                }
+            } else {
+                // bytes in column order: lo0 hi0 lo1 hi1 | lo2 hi2 lo3 hi3
+                const bool own8 = g + 16 * m < L.n8;
+                const uint32_t x0 = own8 ? w0[m] : __builtin_amdgcn_perm(hi, lo, 0x05010400u);
+                const uint32_t x1 = own8 ? w1[m] : __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    z[m][e] = sbyte(x0, e);
+                    z[m][4 + e] = sbyte(x1, e);
+                }
+            }
+            continue;
         }
+        const bool is8 = m < M8;
         if (is8) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 z[m][e] = sbyte(w0[m], e);
                 z[m][4 + e] = sbyte(w1[m], e);
-            }
-        } else if constexpr (N8 == kRuntimeN8) {
-            const uint32_t w4 = (c & 1) ? w1[m] : w0[m];     // the lane's 4 bytes
-            const uint32_t hi = w4 & 0xF0F0F0F0u;
-            const uint32_t lo = (w4 << 4) & 0xF0F0F0F0u;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                z[m][2 * e] = sbyte(lo, e);
-                z[m][2 * e + 1] = sbyte(hi, e);
             }
         } else {
             const uint32_t hi = w0[m] & 0xF0F0F0F0u;         // odd columns, x16
@@ -475,7 +495,9 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
                 }
             };
             const int k = slot_class(L, m);
-            if (k == 1 || (k == -1 && static_cast<int>(p) < n8)) emit(std::true_type{});
+            if (k == 1) emit(std::true_type{});
+            else if (k == 0) emit(std::false_type{});
+            else if (static_cast<int>(p) < n8) emit(std::true_type{});
             else emit(std::false_type{});
         }
     } else {
