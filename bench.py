@@ -32,6 +32,7 @@ HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 COUNTERS_FILE = ROOT / "profiles" / "decode_counters.json"
 # what the measured kernel is built from: its source and the build flags
 DECODE_SRC = [ROOT / "linear_attention_recurrent_rule_amd" / "csrc" / "decode128.hip",
+              ROOT / "linear_attention_recurrent_rule_amd" / "csrc" / "stq_internal.h",
               ROOT / "linear_attention_recurrent_rule_amd" / "build.py"]
 
 
@@ -64,7 +65,7 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=200,
+    p.add_argument("--warmup", type=int, default=400,
                    help="untimed launches first (the clocks ramp up over the first ~100)")
     p.add_argument("--workload", default="highconc_6bit")
     p.add_argument("--pools", type=int, default=4, help="state pools rotated in the timed loop")
