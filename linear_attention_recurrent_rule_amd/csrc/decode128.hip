@@ -37,88 +37,27 @@
 //    wave (a wave-level fence, no workgroup barrier);
 //  * codes: one FMA adds 1.5 * 2^23 (round-half-even to an integer in the low
 //    mantissa bits), then bytes are gathered with v_perm and nibbles with one
-//    shift and one bit-field insert per 8 codes.
+//    shift and one bit-field insert per 8 codes;
+//  * the widened codes feed the matrix cores as they are (tile128.h), so the
+//    column sums take two products per column offset and no repacking.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
 
-#include "stq_internal.h"
+#include "tile128.h"
 
 namespace stq {
 namespace {
 
-constexpr int D = 128;
-constexpr float kRoundMagic = 12582912.0f;               // 1.5 * 2^23
-constexpr float kRowFloor = 1.17549435082228750797e-38f; // 2^-126
-constexpr float kMulMax = 1.70141183460469231732e38f;    // 2^127
-constexpr float kFormTiny = 5.42101086242752217004e-20f; // 2^-64
+using namespace t128;
 
-template <typename T> struct In;
-template <> struct In<float> {
-    static __device__ __forceinline__ float get(const void *p, unsigned i) {
-        return static_cast<const float *>(p)[i];
-    }
-    static __device__ __forceinline__ uint32_t raw(const void *p, unsigned i) {
-        return static_cast<const uint32_t *>(p)[i];
-    }
-    static __device__ __forceinline__ float cvt(uint32_t bits) { return __uint_as_float(bits); }
-};
-template <> struct In<uint16_t> {
-    static __device__ __forceinline__ float get(const void *p, unsigned i) {
-        return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t *>(p)[i]) << 16);
-    }
-    // the element's bits, widened later (a load whose result is only moved
-    // does not wait for it)
-    static __device__ __forceinline__ uint32_t raw(const void *p, unsigned i) {
-        return static_cast<const uint16_t *>(p)[i];
-    }
-    static __device__ __forceinline__ float cvt(uint32_t bits) { return __uint_as_float(bits << 16); }
-};
-
-__device__ __forceinline__ float sbyte(uint32_t w, int k) {
-    return static_cast<float>(static_cast<int8_t>(w >> (8 * k)));
-}
-
-// DPP lane exchange inside 16-lane rows (controls from the GFX9 DPP encoding).
-template <int CTRL> __device__ __forceinline__ uint32_t dpp(uint32_t v) {
-    return static_cast<uint32_t>(
-        __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, true));
-}
-constexpr int kRowRor8 = 0x128;       // lane l <- lane l^8 within the row
-constexpr int kRowHalfMirror = 0x141; // lane l <- lane 7-l within each half row
-constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
-constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
-constexpr int kRowMirror = 0x140;     // lane l <- lane 15-l within the row
-
-template <int CTRL> __device__ __forceinline__ float dppf(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-
-// Sum over the 64 lanes of a wave (valid in every lane): DPP within 16-lane
-// rows, then the four row sums through v_readlane.
-__device__ __forceinline__ float wave_sum(float v) {
-    v += dppf<kQuadXor1>(v);
-    v += dppf<kQuadXor2>(v);
-    v += dppf<kRowHalfMirror>(v);
-    v += dppf<kRowMirror>(v);
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return (r0 + r1) + (r2 + r3);
-}
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-// MFMA operand A for the column sums: per wave w and lane group gl, seven
-// 8-entry bf16 rows: r k (hi, mid, lo), r q (hi, mid, lo) of the lane group's
-// 8 state rows, then a zero row for the unused outputs.
+// Matrix-core operand A for the column sums: per wave and lane group, six
+// rows of 8 words (one per slot), each a bf16 part in its high half: r k
+// (hi, mid, lo), r q (hi, mid, lo).  Lanes of the other output rows read one
+// of these rows too; their products are not used.
 struct Smem {
-    uint16_t coef[4][4][7][8];
-    float4 row[D];          // {P, s, w2, offset of E in ez} per physical row
+    uint32_t coef[4][4][6][8];
+    float4 row[D];          // {P, s, w2, byte offset of E in ez} per physical row
     float v[D], c[D];
     float ez[2 * D];        // e, then a zero vector; each as [e/4][c][e%4]
     float4 red[4][8][2][16]; // per wave, column offset e, lane group, chunk c
@@ -126,32 +65,6 @@ struct Smem {
     float mul[16][8];       // per row group: code multipliers of its 8 rows
     float ra[16][8], rb[16][8]; // column refit: w2 r' s and w2 r'^2 per row
 };
-
-// Round-to-nearest-even fp32 -> bf16 bit pattern (finite inputs).
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-    const uint32_t u = __float_as_uint(x);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-__device__ __forceinline__ float bf16_val(uint32_t h) { return __uint_as_float(h << 16); }
-
-// x = hi + mid + lo exactly (each step removes the leading 8 significant bits
-// and the remainders are exact fp32 differences).
-__device__ __forceinline__ void split3(float x, uint32_t &h0, uint32_t &h1, uint32_t &h2) {
-    h0 = bf16_bits(x);
-    const float r1 = x - bf16_val(h0);
-    h1 = bf16_bits(r1);
-    const float r2 = r1 - bf16_val(h1);
-    h2 = bf16_bits(r2);
-}
-
-// n / d for a wave-uniform n < 2^31, with m = ceil(2^32 / d) (d >= 2) or
-// m = 0 (d = 1): hi(n m) is the quotient or one more (scalar unit only).
-__device__ __forceinline__ unsigned udiv(unsigned n, unsigned d, unsigned m) {
-    if (m == 0) return n;
-    unsigned q = __umulhi(n, m);
-    if (q * d > n) --q;
-    return q;
-}
 
 // N8 = kRuntimeN8 selects the instance whose 4/8-bit split is read at run
 // time (any n8): slot m of wave w holds rows 16 m + 4 w .. 16 m + 4 w + 3, so
@@ -235,16 +148,18 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
     constexpr int M8 = N8 < 0 ? 0 : N8 / 16;
     const int t = L.t, c = L.c, g = L.g;
 
-    // ---- widen the codes; column sums u~ = S~^T (r k), w~ = S~^T (r q) on the
-    // matrix cores: per column offset e, one 16x16x32 bf16 MFMA multiplies the
-    // 6 x 32 coefficient splits of the wave's 32 rows with the 32 x 16 codes of
-    // column 8c + e (codes are small integers, exact in bf16; the splits are
+    // ---- widen the codes into fp32 registers zb[h][e][s] = code of slot
+    // 4h + s in column 8c + e (4-bit codes as 16 z); column sums
+    // u~ = S~^T (r k), w~ = S~^T (r q) on the matrix cores, two 16x16x32 bf16
+    // products per column offset e reading those registers as (0, z) pairs
+    // (codes are small integers, exact in bf16; the coefficient splits are
     // exact, so only the fp32 accumulation rounds)
     const int w = t >> 6;
     const int gl = (t >> 4) & 3;
-    float z[8][8];
+    f32x4 zb[2][8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
+        const int hh = m >> 2, s = m & 3;
         if constexpr (N8 == kRuntimeN8) {
             // the slot's class is wave-uniform (a scalar branch) except in
             // the one slot that straddles n8; there each lane selects, with
@@ -256,60 +171,54 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
             if (k == 1) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    z[m][e] = sbyte(w0[m], e);
-                    z[m][4 + e] = sbyte(w1[m], e);
+                    zb[hh][e][s] = sbyte(w0[m], e);
+                    zb[hh][4 + e][s] = sbyte(w1[m], e);
                 }
             } else if (k == 0) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    z[m][2 * e] = sbyte(lo, e);
-                    z[m][2 * e + 1] = sbyte(hi, e);
+                    zb[hh][2 * e][s] = sbyte(lo, e);
+                    zb[hh][2 * e + 1][s] = sbyte(hi, e);
                 }
             } else {
                 // bytes in column order: lo0 hi0 lo1 hi1 | lo2 hi2 lo3 hi3
-                const bool own8 = g + 16 * m < L.n8;
-                const uint32_t x0 = own8 ? w0[m] : __builtin_amdgcn_perm(hi, lo, 0x05010400u);
-                const uint32_t x1 = own8 ? w1[m] : __builtin_amdgcn_perm(hi, lo, 0x07030602u);
+                const uint32_t own8 = lane_mask(g + 16 * m < L.n8);
+                const uint32_t x0 = sel(own8, w0[m], __builtin_amdgcn_perm(hi, lo, 0x05010400u));
+                const uint32_t x1 = sel(own8, w1[m], __builtin_amdgcn_perm(hi, lo, 0x07030602u));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    z[m][e] = sbyte(x0, e);
-                    z[m][4 + e] = sbyte(x1, e);
+                    zb[hh][e][s] = sbyte(x0, e);
+                    zb[hh][4 + e][s] = sbyte(x1, e);
                 }
             }
             continue;
         }
-        const bool is8 = m < M8;
-        if (is8) {
+        if (m < M8) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                z[m][e] = sbyte(w0[m], e);
-                z[m][4 + e] = sbyte(w1[m], e);
+                zb[hh][e][s] = sbyte(w0[m], e);
+                zb[hh][4 + e][s] = sbyte(w1[m], e);
             }
         } else {
             const uint32_t hi = w0[m] & 0xF0F0F0F0u;         // odd columns, x16
             const uint32_t lo = (w0[m] << 4) & 0xF0F0F0F0u;  // even columns, x16
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                z[m][2 * e] = sbyte(lo, e);
-                z[m][2 * e + 1] = sbyte(hi, e);
+                zb[hh][2 * e][s] = sbyte(lo, e);
+                zb[hh][2 * e + 1][s] = sbyte(hi, e);
             }
         }
     }
     {
-        const u32x4 araw = *reinterpret_cast<const u32x4 *>(&sh.coef[w][gl][c < 6 ? c : 6][0]);
-        const bf16x8 A = __builtin_bit_cast(bf16x8, araw);
-        // lanes of group 0 receive (u hi, u mid, u lo, w hi), group 1 (w mid, w lo);
-        // two accumulators alternate so a result is stored while the next
-        // product is in flight
+        // output row c of the product: lanes c >= 6 read row 5 (unused)
+        const uint32_t *cw = &sh.coef[w][gl][c < 6 ? c : 5][0];
+        const u32x4 A[2] = {*reinterpret_cast<const u32x4 *>(cw), *reinterpret_cast<const u32x4 *>(cw + 4)};
+        // lanes of group 0 receive (u hi, u mid, u lo, w hi), group 1 (w mid,
+        // w lo); two accumulators alternate so a result is stored while the
+        // next product is in flight
         auto product = [&](int e) {
-            u32x4 braw;
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                braw[v] = __builtin_amdgcn_perm(__float_as_uint(z[2 * v + 1][e]),
-                                                __float_as_uint(z[2 * v][e]), 0x07060302u);
-            const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-            return __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, braw), zero,
-                                                           0, 0, 0);
+            const f32x4 zz[2] = {zb[0][e], zb[1][e]};
+            return column_sums(A, zz);
         };
         float4 *red = &sh.red[w][0][gl][c]; // column offset e at red[32 e]
         auto store = [&](int e, const f32x4 &acc) {
@@ -362,54 +271,32 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
 
     // ---- Table C2 steps 2 and 4: updated entries and row absmax
     uint32_t amax[8];
+    const char *ezc = reinterpret_cast<const char *>(&sh.ez[4 * c]);
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
+        const int hh = m >> 2, s = m & 3;
         const float4 rp = sh.row[g + 16 * m];
-        const float *E = &sh.ez[__float_as_int(rp.w) + 4 * c];
+        const float *E = reinterpret_cast<const float *>(ezc + __float_as_int(rp.w));
         const float4 e0 = *reinterpret_cast<const float4 *>(E);
         const float4 e1 = *reinterpret_cast<const float4 *>(E + 64);
         const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
         float mx = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            z[m][e] = __builtin_fmaf(rp.x, z[m][e], ev[e]); // x / s
-            mx = fmaxf(mx, fabsf(z[m][e]));
+            zb[hh][e][s] = __builtin_fmaf(rp.x, zb[hh][e][s], ev[e]); // x / s
+            mx = fmaxf(mx, fabsf(zb[hh][e][s]));
         }
         amax[m] = __float_as_uint(mx);
     }
-    // reduce-scatter over the 16 lanes of the row group: lane c ends with row
-    // c / 2 (non-negative floats order like their bit patterns: integer max)
-    const bool hiHalf = (c & 8) != 0;
-    const bool upper = (c & 4) != 0;
-    const bool q2 = (c & 2) != 0;
-    uint32_t r1[4], r2[2];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t keep = hiHalf ? amax[k + 4] : amax[k];
-        const uint32_t send = hiHalf ? amax[k] : amax[k + 4];
-        r1[k] = max(keep, dpp<kRowRor8>(send));
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const uint32_t keep = upper ? r1[k + 2] : r1[k];
-        const uint32_t send = upper ? r1[k] : r1[k + 2];
-        r2[k] = max(keep, dpp<kRowHalfMirror>(send));
-    }
-    float rmax;
-    {
-        const uint32_t keep = q2 ? r2[1] : r2[0];
-        const uint32_t send = q2 ? r2[0] : r2[1];
-        uint32_t v = max(keep, dpp<kQuadXor2>(send));
-        v = max(v, dpp<kQuadXor1>(v));
-        rmax = __uint_as_float(v);
-    }
+    const uint32_t mk[3] = {lane_mask(c & 8), lane_mask(c & 4), lane_mask(c & 2)};
+    const float rmax = row_max_scatter(amax, mk);
     {
         const int mm = c >> 1;
         const int p = g + 16 * mm;
         const float sc = sh.row[p].y;
         const float mrow = fabsf(sc) * rmax;
         const bool row8 = N8 == kRuntimeN8 ? p < L.n8 : mm < M8;
-        const float qinv = row8 ? (1.0f / 127.0f) : (1.0f / 7.0f);
+        const float qinv = self(lane_mask(row8), 1.0f / 127.0f, 1.0f / 7.0f);
         const float rn = fmaxf(mrow * qinv, kRowFloor);
         const float inv = __builtin_amdgcn_rcpf(rn);
         float mul = sc * inv;
@@ -451,105 +338,59 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
             rbv[e] = sh.rb[g][e];
         }
     }
-    if constexpr (N8 == kRuntimeN8) {
-        const int n8 = L.n8;
-    #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const unsigned p = static_cast<unsigned>(g + 16 * m);
-            // codes, refit sums and the packed store of slot m; the whole body sits
-            // inside the width branch (in the runtime instance this keeps the
-            // codes of one slot live at a time)
-            auto emit = [&](auto W8) __attribute__((always_inline)) {
-                constexpr bool IS8 = decltype(W8)::value;
-                uint32_t bt[8];
-    #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    bt[e] = __float_as_uint(__builtin_fmaf(z[m][e], mulv[m], kRoundMagic));
-                if (REFIT) {
-    #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float zq = __uint_as_float(bt[e]) - kRoundMagic; // the code, exactly
-                        num[e] = __builtin_fmaf(rav[m] * zq, z[m][e], num[e]);
-                        den[e] = __builtin_fmaf(rbv[m] * zq, zq, den[e]);
-                    }
-                }
-                if constexpr (IS8) {
-                    const uint32_t a01 = __builtin_amdgcn_perm(bt[1], bt[0], 0x0C0C0400u);
-                    const uint32_t a23 = __builtin_amdgcn_perm(bt[3], bt[2], 0x04000C0Cu);
-                    const uint32_t a45 = __builtin_amdgcn_perm(bt[5], bt[4], 0x0C0C0400u);
-                    const uint32_t a67 = __builtin_amdgcn_perm(bt[7], bt[6], 0x04000C0Cu);
-                    __builtin_nontemporal_store(u32x2{a01 | a23, a45 | a67},
-                                                reinterpret_cast<u32x2 *>(L.q8 + (p * D + 8 * c)));
-                } else {
-                    // even columns -> low nibbles, odd columns -> high nibbles
-                    const uint32_t ev02 = __builtin_amdgcn_perm(bt[2], bt[0], 0x0C0C0400u);
-                    const uint32_t ev46 = __builtin_amdgcn_perm(bt[6], bt[4], 0x04000C0Cu);
-                    const uint32_t od13 = __builtin_amdgcn_perm(bt[3], bt[1], 0x0C0C0400u);
-                    const uint32_t od57 = __builtin_amdgcn_perm(bt[7], bt[5], 0x04000C0Cu);
-                    const uint32_t evn = ev02 | ev46;
-                    const uint32_t odd = (od13 | od57) << 4;
-                    const uint32_t word = (evn & 0x0F0F0F0Fu) | (odd & 0xF0F0F0F0u);
-                    __builtin_nontemporal_store(
-                        word,
-                        reinterpret_cast<uint32_t *>(L.q4 + ((static_cast<int>(p) - n8) * (D / 2) + 4 * c)));
-                }
-            };
-            const int k = slot_class(L, m);
-            if (k == 1) emit(std::true_type{});
-            else if (k == 0) emit(std::false_type{});
-            else if (static_cast<int>(p) < n8) emit(std::true_type{});
-            else emit(std::false_type{});
+    uint32_t lo4 = 0x0F0F0F0Fu;
+    asm volatile("" : "+v"(lo4));
+    // codes, refit sums and the packed store of slot m; in the runtime
+    // instance the whole body sits inside the width branch (keeps the codes
+    // of one slot live at a time)
+    auto emit = [&](int m, auto W8) __attribute__((always_inline)) {
+        constexpr bool IS8 = decltype(W8)::value;
+        const int hh = m >> 2, s = m & 3;
+        const unsigned p = static_cast<unsigned>(g + 16 * m);
+        uint32_t bt[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            bt[e] = __float_as_uint(__builtin_fmaf(zb[hh][e][s], mulv[m], kRoundMagic));
+        if (REFIT) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float zq = __uint_as_float(bt[e]) - kRoundMagic; // the code, exactly
+                num[e] = __builtin_fmaf(rav[m] * zq, zb[hh][e][s], num[e]);
+                den[e] = __builtin_fmaf(rbv[m] * zq, zq, den[e]);
+            }
         }
-    } else {
-    #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const unsigned p = static_cast<unsigned>(g + 16 * m);
-            uint32_t bt[8];
-    #pragma unroll
-            for (int e = 0; e < 8; ++e) bt[e] = __float_as_uint(__builtin_fmaf(z[m][e], mulv[m], kRoundMagic));
-            if (REFIT) {
-    #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float zq = __uint_as_float(bt[e]) - kRoundMagic; // the code, exactly
-                    num[e] = __builtin_fmaf(rav[m] * zq, z[m][e], num[e]);
-                    den[e] = __builtin_fmaf(rbv[m] * zq, zq, den[e]);
-                }
-            }
-            if (m < M8) {
-                const uint32_t a01 = __builtin_amdgcn_perm(bt[1], bt[0], 0x0C0C0400u);
-                const uint32_t a23 = __builtin_amdgcn_perm(bt[3], bt[2], 0x04000C0Cu);
-                const uint32_t a45 = __builtin_amdgcn_perm(bt[5], bt[4], 0x0C0C0400u);
-                const uint32_t a67 = __builtin_amdgcn_perm(bt[7], bt[6], 0x04000C0Cu);
-                __builtin_nontemporal_store(u32x2{a01 | a23, a45 | a67},
-                                            reinterpret_cast<u32x2 *>(L.q8 + (p * D + 8 * c)));
-            } else {
-                // even columns -> low nibbles, odd columns -> high nibbles
-                const uint32_t ev02 = __builtin_amdgcn_perm(bt[2], bt[0], 0x0C0C0400u);
-                const uint32_t ev46 = __builtin_amdgcn_perm(bt[6], bt[4], 0x04000C0Cu);
-                const uint32_t od13 = __builtin_amdgcn_perm(bt[3], bt[1], 0x0C0C0400u);
-                const uint32_t od57 = __builtin_amdgcn_perm(bt[7], bt[5], 0x04000C0Cu);
-                const uint32_t evn = ev02 | ev46;
-                const uint32_t odd = (od13 | od57) << 4;
-                const uint32_t word = (evn & 0x0F0F0F0Fu) | (odd & 0xF0F0F0F0u);
-                __builtin_nontemporal_store(word,
-                                            reinterpret_cast<uint32_t *>(L.q4 + ((p - N8) * (D / 2) + 4 * c)));
-            }
+        if constexpr (IS8) {
+            __builtin_nontemporal_store(pack_bytes(bt), reinterpret_cast<u32x2 *>(L.q8 + (p * D + 8 * c)));
+        } else {
+            __builtin_nontemporal_store(
+                pack_nibbles(bt, lo4),
+                reinterpret_cast<uint32_t *>(L.q4 + ((static_cast<int>(p) - L.n8) * (D / 2) + 4 * c)));
+        }
+    };
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        if constexpr (N8 == kRuntimeN8) {
+            const int k = slot_class(L, m);
+            if (k == 1) emit(m, std::true_type{});
+            else if (k == 0) emit(m, std::false_type{});
+            else if (g + 16 * m < L.n8) emit(m, std::true_type{});
+            else emit(m, std::false_type{});
+        } else {
+            if (m < M8) emit(m, std::true_type{});
+            else emit(m, std::false_type{});
         }
     }
     if (REFIT) {
         // ---- Table C2 step 5: the column factors refit to the new codes
         // (App. C.1 fixed-code update).  Partials per (wave, lane group,
-        // chunk c, column offset e) go through the MFMA reduction buffer,
-        // free since the column sums were read.
+        // chunk c, column offset e) go through the matrix-core reduction
+        // buffer, free since the column sums were read.
         float2 *red2 = reinterpret_cast<float2 *>(&sh.red[0][0][0][0]); // [4][4][16][8]
         float4 *mine = reinterpret_cast<float4 *>(red2 + ((w * 4 + gl) * 16 + c) * 8);
 #pragma unroll
         for (int e = 0; e < 8; e += 2) mine[e / 2] = make_float4(num[e], den[e], num[e + 1], den[e + 1]);
         __syncthreads();
         if (t < D) {
-            const int cc = t & 15;
-            const int ce = (t >> 4) & 7;
-            const int jcol = 8 * cc + ce;
             float nsum = 0.0f, dsum = 0.0f;
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
@@ -564,8 +405,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
 }
 
 template <int N8, typename TIn, bool REFIT, bool GATED>
-__global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_remap, unsigned hv_m,
-                                                        unsigned g_m) {
+__global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, UnitGeom ug) {
     static_assert(N8 == kRuntimeN8 || (N8 % 16 == 0 && N8 >= 0 && N8 <= D),
                   "n8 must be a multiple of 16 (or read at run time)");
     __shared__ Smem sh;
@@ -575,19 +415,12 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
     L.c = L.t & 15;
     L.g = L.t >> 4;
     const int t = L.t;
-    unsigned unit = blockIdx.x;
-    if (xcd_remap) {
-        // workgroups are dealt round-robin to the 8 XCDs; give each XCD a
-        // contiguous range of units so value heads sharing a key head (and
-        // their q, k) meet in the same L2
-        const unsigned per = gridDim.x >> 3;
-        unit = (blockIdx.x & 7u) * per + (blockIdx.x >> 3);
-    }
+    const unsigned unit = unit_of_block(ug.remap);
     L.unit = unit;
     const int Hv = a.Hv;
-    const int b = static_cast<int>(udiv(unit, static_cast<unsigned>(Hv), hv_m));
+    const int b = static_cast<int>(udiv(unit, static_cast<unsigned>(Hv), ug.hv_m));
     const int h = static_cast<int>(unit - static_cast<unsigned>(b) * static_cast<unsigned>(Hv));
-    const int hk = static_cast<int>(udiv(static_cast<unsigned>(h), static_cast<unsigned>(Hv / a.Hk), g_m));
+    const int hk = static_cast<int>(udiv(static_cast<unsigned>(h), static_cast<unsigned>(ug.G), ug.g_m));
     const int slot = a.slots ? a.slots[b] : b;
     if (slot < 0 || slot >= a.n_slots) { // whole workgroup leaves together
         if (t < D) store_o(a, static_cast<size_t>(unit) * D + t, __int_as_float(0x7fc00000));
@@ -649,39 +482,39 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
         const int p = t;
         const int i = praw & (D - 1);
         const int src = (i & 63) << 2;
-        const bool up = (i & 64) != 0;
+        const uint32_t up = lane_mask(i & 64);
         auto pick = [&](uint32_t lo, uint32_t hi) {
             const uint32_t a0 = __builtin_amdgcn_ds_bpermute(src, static_cast<int>(lo));
             const uint32_t a1 = __builtin_amdgcn_ds_bpermute(src, static_cast<int>(hi));
-            return up ? a1 : a0;
+            return sel(up, a1, a0);
         };
         const float kp = In<TIn>::cvt(pick(x0, x1));
         const float qp = In<TIn>::cvt(pick(x2, x3));
         const float rp = rpv;
         // 4-bit codes are widened as 16 z; a row gate scales the whole row
-        float scale = p < n8 ? rp : rp * 0.0625f;
+        float scale = rp * self(lane_mask(p < n8), 1.0f, 0.0625f);
         if (GATED) scale *= __uint_as_float(pick(g0, g1));
         {
             // row p = 4 w + gl + 16 m of wave w, lane group gl, slot m
-            uint16_t(&cf)[7][8] = sh.coef[(p & 15) >> 2][p & 3];
+            uint32_t(&cf)[6][8] = sh.coef[(p & 15) >> 2][p & 3];
             const int mm = p >> 4;
             uint32_t h0, h1, h2;
-            split3(scale * kp, h0, h1, h2);
-            cf[0][mm] = static_cast<uint16_t>(h0);
-            cf[1][mm] = static_cast<uint16_t>(h1);
-            cf[2][mm] = static_cast<uint16_t>(h2);
-            split3(scale * qp, h0, h1, h2);
-            cf[3][mm] = static_cast<uint16_t>(h0);
-            cf[4][mm] = static_cast<uint16_t>(h1);
-            cf[5][mm] = static_cast<uint16_t>(h2);
+            split3w(scale * kp, h0, h1, h2);
+            cf[0][mm] = h0;
+            cf[1][mm] = h1;
+            cf[2][mm] = h2;
+            split3w(scale * qp, h0, h1, h2);
+            cf[3][mm] = h0;
+            cf[4][mm] = h1;
+            cf[5][mm] = h2;
         }
         const float ar = L.alpha * scale;
         const float bk = L.beta * kp;
         // |b k| > 2^-64 |a r| (false when both vanish: then x = 0 * z = 0)
-        const bool scaled = fabsf(bk) > fabsf(ar) * kFormTiny;
+        const uint32_t scaled = lane_mask(fabsf(bk) > fabsf(ar) * kFormTiny);
         const float w2 = REFIT ? __uint_as_float(pick(u0, u1)) : 0.0f;
-        sh.row[p] = make_float4(scaled ? ar * __builtin_amdgcn_rcpf(bk) : ar, scaled ? bk : 1.0f, w2,
-                                __int_as_float(scaled ? 0 : D));
+        sh.row[p] = make_float4(self(scaled, ar * __builtin_amdgcn_rcpf(bk), ar), self(scaled, bk, 1.0f), w2,
+                                __uint_as_float(sel(scaled, 0u, 4u * D)));
         const float kq = wave_sum(kp * qp);
         if ((t & 63) == 0) sh.kq[t >> 6] = kq;
     } else {
@@ -692,45 +525,34 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, int xcd_re
         sh.v[j] = In<TIn>::cvt(x0);
         sh.c[j] = __uint_as_float(x1);
         sh.ez[D + j] = 0.0f;
-        if (j < 16) *reinterpret_cast<uint4 *>(&sh.coef[j >> 2][j & 3][6][0]) = make_uint4(0u, 0u, 0u, 0u);
     }
     __syncthreads();
     finish_unit<N8, REFIT>(a, sh, L, w0, w1);
 }
 
-// ceil(2^32 / d) for d >= 2, 0 for d = 1 (see udiv)
-unsigned div_magic(unsigned d) {
-    return d <= 1 ? 0u : static_cast<unsigned>(((1ull << 32) + d - 1) / d);
-}
-
 template <int N8, typename TIn, bool REFIT, bool GATED>
-void launch_one(const DecodeArgs &a, unsigned units, int remap, unsigned hv_m, unsigned g_m,
-                hipStream_t s) {
-    hipLaunchKernelGGL((decode128_kernel<N8, TIn, REFIT, GATED>), dim3(units), dim3(256), 0, s, a,
-                       remap, hv_m, g_m);
+void launch_one(const DecodeArgs &a, unsigned units, const UnitGeom &ug, hipStream_t s) {
+    hipLaunchKernelGGL((decode128_kernel<N8, TIn, REFIT, GATED>), dim3(units), dim3(256), 0, s, a, ug);
 }
 
 template <int N8, typename TIn>
-void launch_in(const DecodeArgs &a, unsigned units, int remap, unsigned hv_m, unsigned g_m,
-               hipStream_t s) {
+void launch_in(const DecodeArgs &a, unsigned units, const UnitGeom &ug, hipStream_t s) {
     const bool refit = a.cs != nullptr;
     const bool gated = a.gate != nullptr;
-    if (refit && gated) launch_one<N8, TIn, true, true>(a, units, remap, hv_m, g_m, s);
-    else if (refit) launch_one<N8, TIn, true, false>(a, units, remap, hv_m, g_m, s);
-    else if (gated) launch_one<N8, TIn, false, true>(a, units, remap, hv_m, g_m, s);
-    else launch_one<N8, TIn, false, false>(a, units, remap, hv_m, g_m, s);
+    if (refit && gated) launch_one<N8, TIn, true, true>(a, units, ug, s);
+    else if (refit) launch_one<N8, TIn, true, false>(a, units, ug, s);
+    else if (gated) launch_one<N8, TIn, false, true>(a, units, ug, s);
+    else launch_one<N8, TIn, false, false>(a, units, ug, s);
 }
 
 template <int N8>
 hipError_t launch_n8(bool bf16, const DecodeArgs &a, hipStream_t s) {
     const unsigned units = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.Hv);
-    const int remap = (units % 8u) == 0u ? 1 : 0;
-    const unsigned hv_m = div_magic(static_cast<unsigned>(a.Hv));
-    const unsigned g_m = div_magic(static_cast<unsigned>(a.Hv / a.Hk));
+    const UnitGeom ug = unit_geom(a);
     if (bf16)
-        launch_in<N8, uint16_t>(a, units, remap, hv_m, g_m, s);
+        launch_in<N8, uint16_t>(a, units, ug, s);
     else
-        launch_in<N8, float>(a, units, remap, hv_m, g_m, s);
+        launch_in<N8, float>(a, units, ug, s);
     return hipGetLastError();
 }
 
