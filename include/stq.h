@@ -254,15 +254,19 @@ stq_status stq_calibrate_retention(stq_state *st, const float *alpha, const floa
                                    int32_t B, uint32_t flags, stq_stream_t stream);
 
 /* Lifetime-aware assignment of an ALLOC state (App. C.2 "KDA calibration" and
- * "Allocation optimizers"; App. A.3):
- *   L_u = 1 + sum_{j=1}^{horizon-1} exp(2 j logret_u / nret),
+ * "Allocation optimizers", Table C1; App. A.3 "Mean log retention"):
+ *   L_u = sum_{j=0}^{horizon-1} exp(2 j ell_u), ell_u = logret_u / nret, the
+ *   lifetime weight of row u;
  *   pivots: the desc.n_pivot rows of largest L_u (d_u(nominal) - d_u(FP16))
  *   over all heads (ties to the lower h * dk + i);
- *   every other row starts at the smallest candidate width; on the lower
- *   convex hull of its points (b, L_u d_u(b)) the hull steps of all rows are
- *   taken in order of decreasing distortion saved per bit (ties: lower row,
- *   then lower width) while sum of widths <= nominal_bits * (non-pivot rows);
- *   a row whose next step does not fit keeps its width (the repair).
+ *   every other row takes a width among the vertices of the lower convex hull
+ *   of its points (b, L_u d_u(b)) that lower the objective.  For a shared
+ *   multiplier lambda each row takes its minimiser of L_u d_u(b) + lambda b;
+ *   lambda runs over the hull slopes (distortion saved per bit, ties: lower
+ *   row, then lower width) down to the last at which the widths still sum to
+ *   at most nominal_bits * (non-pivot rows).  The repair then takes the
+ *   remaining hull steps in the same order wherever they still fit; a row
+ *   whose next step does not fit keeps its width.
  * candidates: bit k set for class k (1: 8, 2: 6, 3: 4, 4: 2 bits); 0 picks
  * {8, 6, 4, 2} for nominal_bits <= 4 and {8, 6, 4} otherwise (Table C1).
  * Writes layout and perm and marks the state calibrated; c is left as set by
@@ -272,6 +276,32 @@ stq_status stq_calibrate_retention(stq_state *st, const float *alpha, const floa
  * STQ_E_DEVICE. */
 stq_status stq_allocate(stq_state *st, int32_t horizon, uint32_t candidates,
                         stq_stream_t stream);
+
+/* The assignment of stq_allocate on statistics held in HOST memory (App. C.2
+ * "KDA calibration" and "Allocation optimizers", Table C1; App. A.3 "Mean
+ * log retention"): a planner can run it offline on saved statistics and
+ * install the result with stq_set_alloc_layout.  Host code only: it touches
+ * no device and needs no GPU.
+ *   dist    [n_heads_v][d_k][5] fp64: candidate distortion of each logical
+ *           row at class k (0: FP16 pivot, 1..4: 8, 6, 4, 2 bits), the sums
+ *           of stq_calibrate's DIST pass;
+ *   logret  [n_heads_v][d_k] fp64: sums of log retention over nret samples
+ *           (stq_calibrate_retention), so ell_u = logret_u / nret;
+ *   horizon, candidates, nominal_bits, n_pivot: as stq_allocate and the
+ *           descriptor;
+ *   counts  [n_heads_v][5] int32 and perm [n_heads_v][d_k] int32 (caller
+ *           memory, overwritten): rows per class per head, and the logical
+ *           row of each physical row (classes in order, each ascending).
+ * The result depends on the arguments alone (all ties are broken by row and
+ * width as stq_allocate states).
+ * Errors: STQ_E_ARG (null pointers, n_heads_v or d_k < 1, horizon < 1,
+ * nret <= 0 or NaN, bad candidates, nominal width not a candidate, n_pivot
+ * outside [0, n_heads_v d_k], infeasible budget), STQ_E_SHAPE (more than
+ * 2^24 rows). */
+stq_status stq_assign_rows(int32_t n_heads_v, int32_t d_k, const double *dist,
+                           const double *logret, double nret, int32_t horizon,
+                           uint32_t candidates, int32_t nominal_bits, int32_t n_pivot,
+                           int32_t *counts, int32_t *perm);
 
 /* Install a ragged layout chosen elsewhere: counts [Hv][5] (HOST memory, each
  * head's counts >= 0 and summing to dk), c [Hv][dv] and perm [Hv][dk] (device

@@ -181,7 +181,7 @@ stq_status dev(hipError_t e) { return e == hipSuccess ? STQ_OK : STQ_E_DEVICE; }
 
 extern "C" {
 
-int32_t stq_abi_version(void) { return 5; }
+int32_t stq_abi_version(void) { return 6; }
 
 const char *stq_status_str(int32_t s) {
     switch (s) {
@@ -622,16 +622,41 @@ stq_status stq_calibrate_retention(stq_state *st, const float *alpha, const floa
     return dev(stq::launch_alloc_retention(D, a, s));
 }
 
+// The candidate set of an assignment: 0 picks Table C1's set for the nominal
+// width; otherwise only integer classes, and the nominal width among them.
+static bool candidate_mask(int nominal, uint32_t candidates, uint32_t *mask) {
+    uint32_t m = candidates;
+    if (m == 0) m = nominal <= 4 ? 0x1Eu : 0x0Eu; // {8,6,4,2} or {8,6,4}
+    const int k = class_of_width(nominal);
+    if ((m & ~0x1Eu) || k < 0 || !(m & (1u << k))) return false;
+    *mask = m;
+    return true;
+}
+
+stq_status stq_assign_rows(int32_t n_heads_v, int32_t d_k, const double *dist,
+                           const double *logret, double nret, int32_t horizon,
+                           uint32_t candidates, int32_t nominal_bits, int32_t n_pivot,
+                           int32_t *counts, int32_t *perm) {
+    if (n_heads_v < 1 || d_k < 1 || !dist || !logret || !counts || !perm) return STQ_E_ARG;
+    if (static_cast<int64_t>(n_heads_v) * d_k > (int64_t{1} << 24)) return STQ_E_SHAPE;
+    uint32_t mask = 0;
+    if (horizon < 1 || !(nret > 0.0) || !candidate_mask(nominal_bits, candidates, &mask))
+        return STQ_E_ARG;
+    if (n_pivot < 0 || n_pivot > n_heads_v * d_k) return STQ_E_ARG;
+    return stq::assign_rows(n_heads_v, d_k, dist, logret, nret, horizon, mask, nominal_bits,
+                            n_pivot, counts, perm)
+               ? STQ_OK
+               : STQ_E_ARG;
+}
+
 stq_status stq_allocate(stq_state *st, int32_t horizon, uint32_t candidates,
                         stq_stream_t stream) {
     stq_status e = check_state(st);
     if (e != STQ_OK) return e;
     if (!alloc_format(st->desc.fmt) || horizon < 1) return STQ_E_ARG;
     const int nominal = st->desc.nominal_bits;
-    uint32_t mask = candidates;
-    if (mask == 0) mask = nominal <= 4 ? 0x1Eu : 0x0Eu; // {8,6,4,2} or {8,6,4}
-    if (mask & ~0x1Eu) return STQ_E_ARG;
-    if (!(mask & (1u << class_of_width(nominal)))) return STQ_E_ARG;
+    uint32_t mask = 0;
+    if (!candidate_mask(nominal, candidates, &mask)) return STQ_E_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int D = st->desc.d_k, H = st->desc.n_heads_v;
     const size_t nd = static_cast<size_t>(H) * D;
@@ -646,9 +671,9 @@ stq_status stq_allocate(stq_state *st, int32_t horizon, uint32_t candidates,
         return STQ_E_DEVICE;
     if (!(nret[0] > 0.0)) return STQ_E_STATE;
     std::vector<int32_t> counts(static_cast<size_t>(H) * stq::kNumClasses), perm(nd);
-    if (!stq::assign_rows(H, D, dist.data(), logret.data(), nret[0], horizon, mask, nominal,
-                          st->desc.n_pivot, counts.data(), perm.data()))
-        return STQ_E_ARG;
+    if ((e = stq_assign_rows(H, D, dist.data(), logret.data(), nret[0], horizon, mask, nominal,
+                             st->desc.n_pivot, counts.data(), perm.data())) != STQ_OK)
+        return e;
     std::vector<int32_t> table(static_cast<size_t>(H) * stq::kLayoutStride);
     bool space = false;
     if (!build_layout(&st->desc, st->slot_bytes, counts.data(), table.data(), &space))

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert "stq_decode_step" in names and len(names) >= 8
     for n in names:
         assert hasattr(lib, n), f"libstq.so does not export {n}"
-    assert lib.stq_abi_version() == 5
+    assert lib.stq_abi_version() == 6
 
 
 def _desc(n_slots=4, hv=4, hk=2, d=64, n8=32, fmt=stq.FMT_MIXED48, dv=None, nominal=0, piv=0):

@@ -87,3 +87,54 @@ def test_alloc_fullsize_step_sampled_parity_and_properties(oracle_mod, gated):
     stats = _compare(gp[bs], gr[bs], ref["pool"], ref["r"], counts, d, "ragged full size",
                      o=go[bs], ref_o=ref["o"], pivot_err=pivot_err)
     print(stats)
+
+
+def test_assignment_on_calibrated_workload_statistics(oracle_mod):
+    """The ragged format calibrated on the high-concurrency workload (B =
+    1024 sequences, 32 value heads, d = 128): column factors over the 32
+    calibration steps of the FP32-state kernel, candidate distortions over
+    the same records, retention from their gates; the assignment of
+    stq_allocate at the 6-bit budget with 26 pivot rows over a horizon of T
+    = 100 steps must equal the oracle's assignment of the same statistics,
+    row for row, and so must stq_assign_rows on the statistics read back."""
+    w = wl.WORKLOADS["highconc_6bit"]
+    B, hv, hk, d = w.B, w.hv, w.hk, w.d
+    n_pivot, nominal = 26, 6
+    print(f"[case] calibrated assignment B={B} hv={hv} d={d} P={n_pivot}", flush=True)
+    S0 = gu.dev(wl.initial_state(w))
+    fp = gu.make_state(B, hv, hk, d, 0, fmt=stq.FMT_FP32)
+    cal = stq.State(stq.Geometry(1, hv, hk, d, 0, stq.FMT_ALLOC, nominal_bits=nominal,
+                                 n_pivot=n_pivot))
+    cal.calibrate(None, stq.CAL_RESET)
+    cal.calibrate_retention(None, None, stq.CAL_RESET)
+    for flag in (stq.CAL_COLS, stq.CAL_DIST):
+        fp.pack(S0)
+        for t in range(w.calib_steps):
+            q, k, v, a, b = gu.inputs_to_device(wl.workload_inputs(w, t, calibration=True))
+            fp.decode_step(q, k, v, a, b)
+            cal.calibrate(fp.s32, flag)
+            if flag == stq.CAL_COLS:
+                cal.calibrate_retention(alpha=a)
+        if flag == stq.CAL_COLS:
+            cal.calibrate(None, stq.CAL_FINALIZE)
+        torch.cuda.synchronize()
+        print(f"[case] calibration pass {flag} done", flush=True)
+    del S0, fp
+    torch.cuda.empty_cache()
+    cal.allocate(w.T)
+    torch.cuda.synchronize()
+    dist, logret = cal.dist.cpu().numpy(), cal.logret.cpu().numpy()
+    nret = float(cal.nret.cpu().numpy()[0])
+    assert nret == B * w.calib_steps
+    Lw = oracle_mod.alloc_lifetime(logret, nret, w.T)
+    bits, counts, perm = oracle_mod.alloc_assign(dist, Lw, nominal=nominal, n_pivot=n_pivot,
+                                                 candidates=(8, 6, 4))
+    lay = cal.layout.cpu().numpy()
+    np.testing.assert_array_equal(lay[:, :5], counts)
+    np.testing.assert_array_equal(cal.perm.cpu().numpy(), perm)
+    hcounts, hperm = stq.assign_rows(dist, logret, nret, w.T, nominal, n_pivot)
+    np.testing.assert_array_equal(hcounts, counts)
+    np.testing.assert_array_equal(hperm, perm)
+    used = {b_: int(np.sum(bits == b_)) for b_ in (16, 8, 6, 4)}
+    print("widths used:", used, flush=True)
+    assert used[16] == n_pivot and used[8] > 0 and used[4] > 0
