@@ -11,6 +11,7 @@ import ctypes
 from dataclasses import dataclass
 from pathlib import Path
 
+import numpy as np
 import torch
 
 _PKG = Path(__file__).resolve().parent
@@ -60,7 +61,8 @@ EXPORTS = ("stq_state_bytes", "stq_alloc_state", "stq_calibrate", "stq_calibrate
            "stq_calibrate_impact_gated", "stq_set_calibration", "stq_pack_state",
            "stq_decode_step", "stq_decode_step_into", "stq_decode_step_gated",
            "stq_dequant_state", "stq_stream_copy", "stq_status_str", "stq_abi_version",
-           "stq_calibrate_retention", "stq_allocate", "stq_set_alloc_layout")
+           "stq_calibrate_retention", "stq_allocate", "stq_set_alloc_layout",
+           "stq_assign_rows")
 
 
 def _lib():
@@ -88,6 +90,8 @@ def _lib():
         lib.stq_calibrate_retention.argtypes = [ctypes.POINTER(CState), P, P, I32, U32, P]
         lib.stq_allocate.argtypes = [ctypes.POINTER(CState), I32, U32, P]
         lib.stq_set_alloc_layout.argtypes = [ctypes.POINTER(CState), P, P, P, P]
+        lib.stq_assign_rows.argtypes = [I32, I32, P, P, ctypes.c_double, I32, U32, I32, I32, P,
+                                        P]
         lib.stq_dequant_state.argtypes = [ctypes.POINTER(CState), P, I32, P, P]
         lib.stq_stream_copy.argtypes = [P, P, SZ, P]
         lib.stq_status_str.argtypes = [I32]
@@ -97,7 +101,8 @@ def _lib():
                      "stq_calibrate_impact_gated", "stq_set_calibration",
                      "stq_pack_state", "stq_decode_step", "stq_decode_step_into",
                      "stq_decode_step_gated", "stq_dequant_state", "stq_stream_copy",
-                     "stq_calibrate_retention", "stq_allocate", "stq_set_alloc_layout"):
+                     "stq_calibrate_retention", "stq_allocate", "stq_set_alloc_layout",
+           "stq_assign_rows"):
             getattr(lib, name).restype = I32
         _LIB = lib
     return _LIB
@@ -118,17 +123,59 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _dev_ptr(t: torch.Tensor | None, name: str):
+_FLOAT_IN = (torch.float32, torch.bfloat16)
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+
+
+def _check_meta(t, name: str, shape=None, dtypes=None):
+    """Type, dtype (one of `dtypes`) and exact shape (an entry None matches any
+    extent) of an argument; None passes."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if dtypes is not None and t.dtype not in dtypes:
+        names = " or ".join(str(d).replace("torch.", "") for d in dtypes)
+        raise ValueError(f"{name} must be {names}, got {str(t.dtype).replace('torch.', '')}")
+    if shape is not None:
+        ok = t.dim() == len(shape) and all(e is None or int(n) == e
+                                          for n, e in zip(t.shape, shape))
+        if not ok:
+            want = "[" + "][".join("*" if e is None else str(e) for e in shape) + "]"
+            raise ValueError(f"{name} must have shape {want}, got {list(t.shape)}")
+
+
+def _dev_ptr(t: torch.Tensor | None, name: str, shape=None, dtypes=None, device=None):
+    """Device pointer of `t` after checking it, so that a mismatch raises
+    ValueError before anything is queued: dtype and shape as _check_meta, on a
+    HIP device (on `device` when given), contiguous.  None passes through as
+    NULL."""
     if t is None:
         return None
+    _check_meta(t, name, shape, dtypes)
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the state on {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _dev_ptrs(*specs, device=None):
+    """_dev_ptr over several (tensor, name, shape, dtypes) specs, with every
+    dtype and shape checked before any device check, so that the first error
+    names the argument that is wrong rather than the first one on the host."""
+    for t, name, shape, dtypes in specs:
+        _check_meta(t, name, shape, dtypes)
+    return [_dev_ptr(t, name, shape, dtypes, device) for t, name, shape, dtypes in specs]
+
+
 def _in_dtype(q, k, v) -> int:
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch tensor")
     if q.dtype == torch.float32:
         dt = F32
     elif q.dtype == torch.bfloat16:
@@ -138,6 +185,34 @@ def _in_dtype(q, k, v) -> int:
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share one dtype")
     return dt
+
+
+def _batch(t, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or t.dim() < 1:
+        raise ValueError(f"{name} must be a tensor with a leading batch dimension")
+    return int(t.shape[0])
+
+
+def assign_rows(dist, logret, nret: float, horizon: int, nominal_bits: int, n_pivot: int,
+                candidates: int = 0):
+    """Pivots and row widths from statistics in host memory (stq_assign_rows):
+    dist [Hv][d][5] and logret [Hv][d] (float64 arrays), nret the number of
+    retention samples.  Returns counts [Hv][5] and perm [Hv][d] (int32)."""
+    dist = np.asarray(dist)
+    logret = np.asarray(logret)
+    if dist.dtype != np.float64 or logret.dtype != np.float64:
+        raise ValueError("dist and logret must be float64")
+    if dist.ndim != 3 or dist.shape[2] != 5 or logret.shape != dist.shape[:2]:
+        raise ValueError("dist must be [Hv][d][5] and logret [Hv][d]")
+    dist = np.ascontiguousarray(dist)
+    logret = np.ascontiguousarray(logret)
+    hv, d = logret.shape
+    counts = np.zeros((hv, 5), np.int32)
+    perm = np.zeros((hv, d), np.int32)
+    _check(_lib().stq_assign_rows(hv, d, dist.ctypes.data, logret.ctypes.data, float(nret),
+                                  int(horizon), int(candidates), int(nominal_bits), int(n_pivot),
+                                  counts.ctypes.data, perm.ctypes.data), "stq_assign_rows")
+    return counts, perm
 
 
 def state_bytes(n_slots, n_heads_v, n_heads_k, d, n8, fmt, nominal_bits=0, n_pivot=0) -> int:
@@ -274,11 +349,13 @@ class State:
     def calibrate_retention(self, alpha=None, gate=None, flags: int = 0, stream=None):
         """Fold one step's gates (alpha [B][Hv] or gate [B][Hv][d]) into the
         summed log retention (stq_calibrate_retention)."""
+        g, dv = self.geo, self.buffer.device
         src = gate if gate is not None else alpha
-        B = 0 if src is None else int(src.shape[0])
-        _check(_lib().stq_calibrate_retention(ctypes.byref(self.c_state), _dev_ptr(alpha, "alpha"),
-                                              _dev_ptr(gate, "gate"), B, flags, _stream(stream)),
-               "stq_calibrate_retention")
+        B = 0 if src is None else _batch(src, "gate" if gate is not None else "alpha")
+        pa, pg = _dev_ptrs((alpha, "alpha", (B, g.n_heads_v), _F32),
+                           (gate, "gate", (B, g.n_heads_v, g.d), _F32), device=dv)
+        _check(_lib().stq_calibrate_retention(ctypes.byref(self.c_state), pa, pg, B, flags,
+                                              _stream(stream)), "stq_calibrate_retention")
 
     def allocate(self, horizon: int, candidates: int = 0, stream=None):
         """Pivots and row widths from the calibration statistics (stq_allocate)."""
@@ -287,10 +364,15 @@ class State:
 
     def set_alloc_layout(self, counts, c: torch.Tensor, perm: torch.Tensor, stream=None):
         """Install class counts [Hv][5] (host array), c and perm (device)."""
-        import numpy as np
+        g, dv = self.geo, self.buffer.device
         cnt = np.ascontiguousarray(counts, dtype=np.int32)
-        _check(_lib().stq_set_alloc_layout(ctypes.byref(self.c_state), cnt.ctypes.data,
-                                           _dev_ptr(c, "c"), _dev_ptr(perm, "perm"),
+        if cnt.shape != (g.n_heads_v, 5):
+            raise ValueError(f"counts must have shape [{g.n_heads_v}][5], got {list(cnt.shape)}")
+        if c is None or perm is None:
+            raise ValueError("c and perm are required")
+        pc, pp = _dev_ptrs((c, "c", (g.n_heads_v, g.d), _F32),
+                           (perm, "perm", (g.n_heads_v, g.d), _I32), device=dv)
+        _check(_lib().stq_set_alloc_layout(ctypes.byref(self.c_state), cnt.ctypes.data, pc, pp,
                                            _stream(stream)), "stq_set_alloc_layout")
 
     @property
@@ -299,40 +381,58 @@ class State:
 
     # -- entry points --
     def calibrate(self, records: torch.Tensor | None, flags: int, stream=None):
-        n = 0 if records is None else int(records.shape[0])
-        _check(_lib().stq_calibrate(ctypes.byref(self.c_state), _dev_ptr(records, "records"),
-                                    n, flags, _stream(stream)), "stq_calibrate")
+        """Fold fp32 records [n][Hv][d][d] (logical rows) into the statistics
+        that `flags` name (stq_calibrate)."""
+        g = self.geo
+        n = 0 if records is None else _batch(records, "records")
+        p = _dev_ptr(records, "records", (n, g.n_heads_v, g.d, g.d), _F32, self.buffer.device)
+        _check(_lib().stq_calibrate(ctypes.byref(self.c_state), p, n, flags, _stream(stream)),
+               "stq_calibrate")
 
     def calibrate_impact(self, q, k, alpha, beta, flags: int, stream=None, gate=None):
         """Accumulate row impact over one step's samples (q, k [B][Hk][d], alpha,
         beta [B][Hv]); CAL_RESET / CAL_FINALIZE as in stq_calibrate_impact.
         With gate [B][Hv][d] (logical rows) the row gate replaces alpha
         (stq_calibrate_impact_gated)."""
+        g, dv = self.geo, self.buffer.device
         if q is None:
             B, dt = 0, F32
         else:
-            B = int(q.shape[0])
+            B = _batch(q, "q")
+            if q.dtype not in _FLOAT_IN or k is None or k.dtype != q.dtype:
+                raise ValueError("q and k must share one dtype, float32 or bfloat16")
             dt = BF16 if q.dtype == torch.bfloat16 else F32
-        if gate is not None:
-            _check(_lib().stq_calibrate_impact_gated(
-                ctypes.byref(self.c_state), _dev_ptr(q, "q"), _dev_ptr(k, "k"), dt,
-                _dev_ptr(gate, "gate"), _dev_ptr(beta, "beta"), B, flags, _stream(stream)),
-                "stq_calibrate_impact_gated")
+        gated = gate is not None
+        pq, pk, pr, pb = _dev_ptrs(
+            (q, "q", (B, g.n_heads_k, g.d), _FLOAT_IN), (k, "k", (B, g.n_heads_k, g.d), _FLOAT_IN),
+            (gate, "gate", (B, g.n_heads_v, g.d), _F32) if gated
+            else (alpha, "alpha", (B, g.n_heads_v), _F32),
+            (beta, "beta", (B, g.n_heads_v), _F32), device=dv)
+        if gated:
+            _check(_lib().stq_calibrate_impact_gated(ctypes.byref(self.c_state), pq, pk, dt, pr,
+                                                     pb, B, flags, _stream(stream)),
+                   "stq_calibrate_impact_gated")
             return
-        _check(_lib().stq_calibrate_impact(ctypes.byref(self.c_state), _dev_ptr(q, "q"),
-                                           _dev_ptr(k, "k"), dt, _dev_ptr(alpha, "alpha"),
-                                           _dev_ptr(beta, "beta"), B, flags, _stream(stream)),
-               "stq_calibrate_impact")
+        _check(_lib().stq_calibrate_impact(ctypes.byref(self.c_state), pq, pk, dt, pr, pb, B,
+                                           flags, _stream(stream)), "stq_calibrate_impact")
 
     def set_calibration(self, c: torch.Tensor, perm: torch.Tensor, stream=None):
-        _check(_lib().stq_set_calibration(ctypes.byref(self.c_state), _dev_ptr(c, "c"),
-                                          _dev_ptr(perm, "perm"), _stream(stream)),
+        """Install column factors c [Hv][d] fp32 and row order perm [Hv][d]
+        int32 (stq_set_calibration)."""
+        g, dv = self.geo, self.buffer.device
+        pc, pp = _dev_ptrs((c, "c", (g.n_heads_v, g.d), _F32),
+                           (perm, "perm", (g.n_heads_v, g.d), _I32), device=dv)
+        _check(_lib().stq_set_calibration(ctypes.byref(self.c_state), pc, pp, _stream(stream)),
                "stq_set_calibration")
 
     def pack(self, S: torch.Tensor, slots: torch.Tensor | None = None, stream=None):
-        B = int(S.shape[0])
-        _check(_lib().stq_pack_state(ctypes.byref(self.c_state), _dev_ptr(S, "S"),
-                                     _dev_ptr(slots, "slots"), B, _stream(stream)),
+        """Pack fp32 states S [B][Hv][d][d] (logical rows) into slots
+        (stq_pack_state)."""
+        g = self.geo
+        B = _batch(S, "S")
+        pS, ps = _dev_ptrs((S, "S", (B, g.n_heads_v, g.d, g.d), _F32), (slots, "slots", (B,), _I32),
+                           device=self.buffer.device)
+        _check(_lib().stq_pack_state(ctypes.byref(self.c_state), pS, ps, B, _stream(stream)),
                "stq_pack_state")
 
     def _readout(self, q, k, v, o, o_dtype):
@@ -340,34 +440,49 @@ class State:
         default) and the dtype argument: the input dtype, with STQ_OUT_BF16
         when o is bf16."""
         dt = _in_dtype(q, k, v)
+        B = _batch(q, "q")
         if o is None:
-            o = torch.empty((int(q.shape[0]), self.geo.n_heads_v, self.geo.d),
-                            dtype=o_dtype or torch.float32, device=q.device)
+            o = torch.empty((B, self.geo.n_heads_v, self.geo.d),
+                            dtype=o_dtype or torch.float32, device=self.buffer.device)
+        if not isinstance(o, torch.Tensor) or o.dtype not in _FLOAT_IN:
+            raise ValueError("o must be a float32 or bfloat16 tensor")
         if o.dtype == torch.bfloat16:
             dt |= OUT_BF16
-        elif o.dtype != torch.float32:
-            raise ValueError("o must be float32 or bfloat16")
         return o, dt
 
+    def _step_ptrs(self, q, k, v, o, slots, **rows):
+        """Checked pointers of one decode step's tensors: slots [B] int32, q, k
+        [B][Hk][d], v [B][Hv][d], the per-row arguments given in `rows` (alpha,
+        beta [B][Hv] fp32; gate [B][Hv][d] fp32), then o [B][Hv][d]."""
+        g = self.geo
+        B = _batch(q, "q")
+        specs = [(slots, "slots", (B,), _I32), (q, "q", (B, g.n_heads_k, g.d), _FLOAT_IN),
+                 (k, "k", (B, g.n_heads_k, g.d), _FLOAT_IN),
+                 (v, "v", (B, g.n_heads_v, g.d), _FLOAT_IN)]
+        for name, t in rows.items():
+            if t is None:
+                raise ValueError(f"{name} is required")
+            shape = (B, g.n_heads_v, g.d) if name == "gate" else (B, g.n_heads_v)
+            specs.append((t, name, shape, _F32))
+        specs.append((o, "o", (B, g.n_heads_v, g.d), _FLOAT_IN))
+        return B, _dev_ptrs(*specs, device=self.buffer.device)
+
     def decode_step(self, q, k, v, alpha, beta, o=None, slots=None, stream=None, o_dtype=None):
-        B = int(q.shape[0])
         o, dt = self._readout(q, k, v, o, o_dtype)
-        _check(_lib().stq_decode_step(ctypes.byref(self.c_state), _dev_ptr(slots, "slots"), B,
-                                      _dev_ptr(q, "q"), _dev_ptr(k, "k"), _dev_ptr(v, "v"), dt,
-                                      _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
-                                      _dev_ptr(o, "o"), _stream(stream)), "stq_decode_step")
+        B, (ps, pq, pk, pv, pa, pb, po) = self._step_ptrs(q, k, v, o, slots, alpha=alpha,
+                                                         beta=beta)
+        _check(_lib().stq_decode_step(ctypes.byref(self.c_state), ps, B, pq, pk, pv, dt, pa, pb,
+                                      po, _stream(stream)), "stq_decode_step")
         return o
 
     def decode_step_into(self, dst: "State", q, k, v, alpha, beta, o=None, slots=None,
                          stream=None, o_dtype=None):
         """Decode reading this state and writing the updated one into `dst`."""
-        B = int(q.shape[0])
         o, dt = self._readout(q, k, v, o, o_dtype)
+        B, (ps, pq, pk, pv, pa, pb, po) = self._step_ptrs(q, k, v, o, slots, alpha=alpha,
+                                                         beta=beta)
         _check(_lib().stq_decode_step_into(ctypes.byref(self.c_state), ctypes.byref(dst.c_state),
-                                           _dev_ptr(slots, "slots"), B, _dev_ptr(q, "q"),
-                                           _dev_ptr(k, "k"), _dev_ptr(v, "v"), dt,
-                                           _dev_ptr(alpha, "alpha"), _dev_ptr(beta, "beta"),
-                                           _dev_ptr(o, "o"), _stream(stream)),
+                                           ps, B, pq, pk, pv, dt, pa, pb, po, _stream(stream)),
                "stq_decode_step_into")
         return o
 
@@ -375,31 +490,38 @@ class State:
                           dst: "State | None" = None, o_dtype=None):
         """Decode with a per-key-row gate [B][Hv][d] (logical rows, fp32),
         in place or, with dst, into another state (stq_decode_step_gated)."""
-        B = int(q.shape[0])
         o, dt = self._readout(q, k, v, o, o_dtype)
+        B, (ps, pq, pk, pv, pg, pb, po) = self._step_ptrs(q, k, v, o, slots, gate=gate,
+                                                         beta=beta)
         target = self if dst is None else dst
         _check(_lib().stq_decode_step_gated(ctypes.byref(self.c_state),
-                                            ctypes.byref(target.c_state),
-                                            _dev_ptr(slots, "slots"), B, _dev_ptr(q, "q"),
-                                            _dev_ptr(k, "k"), _dev_ptr(v, "v"), dt,
-                                            _dev_ptr(gate, "gate"), _dev_ptr(beta, "beta"),
-                                            _dev_ptr(o, "o"), _stream(stream)),
+                                            ctypes.byref(target.c_state), ps, B, pq, pk, pv, dt,
+                                            pg, pb, po, _stream(stream)),
                "stq_decode_step_gated")
         return o
 
     def dequant(self, B: int | None = None, slots=None, out=None, stream=None):
+        g = self.geo
         if B is None:
-            B = int(slots.shape[0]) if slots is not None else self.geo.n_slots
+            B = _batch(slots, "slots") if slots is not None else g.n_slots
         if out is None:
-            out = torch.empty((B, self.geo.n_heads_v, self.geo.d, self.geo.d),
-                              dtype=torch.float32, device=self.buffer.device)
-        _check(_lib().stq_dequant_state(ctypes.byref(self.c_state), _dev_ptr(slots, "slots"), B,
-                                        _dev_ptr(out, "S_out"), _stream(stream)),
+            out = torch.empty((B, g.n_heads_v, g.d, g.d), dtype=torch.float32,
+                              device=self.buffer.device)
+        po, ps = _dev_ptrs((out, "out", (B, g.n_heads_v, g.d, g.d), _F32),
+                           (slots, "slots", (B,), _I32), device=self.buffer.device)
+        _check(_lib().stq_dequant_state(ctypes.byref(self.c_state), ps, B, po, _stream(stream)),
                "stq_dequant_state")
         return out
 
 
 def stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
+    """Copy src's bytes into dst (same byte size, same device) on the stream
+    (stq_stream_copy)."""
+    ps = _dev_ptr(src, "src")
+    pd = _dev_ptr(dst, "dst", device=src.device)
+    if ps is None or pd is None:
+        raise ValueError("src and dst are required")
     n = src.numel() * src.element_size()
-    _check(_lib().stq_stream_copy(_dev_ptr(src, "src"), _dev_ptr(dst, "dst"), n,
-                                  _stream(stream)), "stq_stream_copy")
+    if dst.numel() * dst.element_size() != n:
+        raise ValueError(f"dst holds {dst.numel() * dst.element_size()} bytes, src {n}")
+    _check(_lib().stq_stream_copy(ps, pd, n, _stream(stream)), "stq_stream_copy")
