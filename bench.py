@@ -32,6 +32,7 @@ HBM_PEAK_GBPS = 8000.0  # MI355X published HBM3E bandwidth
 COUNTERS_FILE = ROOT / "profiles" / "decode_counters.json"
 # what the measured kernel is built from: its source and the build flags
 DECODE_SRC = [ROOT / "linear_attention_recurrent_rule_amd" / "csrc" / "decode128.hip",
+              ROOT / "linear_attention_recurrent_rule_amd" / "csrc" / "tile128.h",
               ROOT / "linear_attention_recurrent_rule_amd" / "csrc" / "stq_internal.h",
               ROOT / "linear_attention_recurrent_rule_amd" / "build.py"]
 
@@ -64,9 +65,14 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=400,
-                   help="untimed launches first (the clocks ramp up over the first ~100)")
+    p.add_argument("--steps", type=int, default=200, help="launches per timed block")
+    p.add_argument("--warmup", type=int, default=400, help="untimed launches first")
+    p.add_argument("--warmup-floor-ms", type=float, default=100.0,
+                   help="after the --warmup launches, keep launching (untimed, counted and "
+                        "reported as warmup_launches) until this much wall time has passed: "
+                        "the clocks need about 30 ms of load to leave their idle state")
+    p.add_argument("--blocks", type=int, default=3,
+                   help="timed blocks of --steps launches; ms_per_step is their median")
     p.add_argument("--workload", default="highconc_6bit")
     p.add_argument("--pools", type=int, default=4, help="state pools rotated in the timed loop")
     p.add_argument("--mode", choices=("in_place", "double_buffered"), default="in_place",
@@ -82,6 +88,13 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only-decode", action="store_true",
                    help="time the main workload only (for profiler runs)")
+    p.add_argument("--trace-summary", default=None, metavar="KERNEL_TRACE_CSV",
+                   help="no GPU work: summarise a rocprofv3 kernel trace (calls, avg, min, max "
+                        "per kernel, and the average over each kernel's last --timed-launches "
+                        "dispatches) and exit")
+    p.add_argument("--timed-launches", type=int, default=None,
+                   help="with --trace-summary: dispatches at the end of the trace that were "
+                        "timed (default: --blocks x --steps)")
     p.add_argument("--with-copy", action="store_true",
                    help="also run the 1 GiB reference copy (with --only-decode)")
     p.add_argument("--drift", action="store_true",
@@ -209,8 +222,89 @@ def alloc_unit_bytes(counts, d: int) -> float:
     return float(seg.mean() + 4 * d)
 
 
+def _time_oracle_steps(oracle, wl, w, ps, n_max, budget_s, threads):
+    """Successive oracle decode steps of workload w from packed state ps (each
+    from the previous step's result) until n_max steps or budget_s seconds;
+    returns (steps, seconds)."""
+    p8, p4, r = ps.pool8, ps.pool4, ps.r
+    n, dt = 0, 0.0
+    while n < n_max and dt < budget_s:
+        x = wl.workload_inputs(w, n)
+        t1 = time.perf_counter()
+        res = oracle.step(p8, p4, r, ps.c, ps.perm, x.q, x.k, x.v, x.alpha, x.beta, n8=w.n8,
+                          nthreads=threads)
+        dt += time.perf_counter() - t1
+        p8, p4, r = res["pool8"], res["pool4"], res["r"]
+        n += 1
+    return n, dt
+
+
+def cpu_baseline(np, wl, w, B, hv, d) -> dict:
+    """The oracle timed on the host cores: the benchmarked workload over about
+    10 s, the small mixed workload over its whole T = 256 steps, one full step
+    of the serving workload and of the 4.5-bit high-concurrency workload, and
+    a single-thread sample."""
+    import oracle
+
+    threads = oracle.default_threads()
+    ps = wl.random_packed_state(B, hv, d, w.n8, seed=w.seed + 700)
+    n_steps, dt = _time_oracle_steps(oracle, wl, w, ps, 32, 10.0, threads)
+    cpu = dict(value=B * hv * n_steps / dt, unit="state-updates/s", cores=threads, kind="oracle",
+               sample=f"{n_steps} successive full decode steps of the workload ({B * hv} "
+                      f"units each, d={d}, n8={w.n8}) from a seeded random packed state, "
+                      f"{dt:.1f}s wall on {threads} threads")
+    configs = {}
+    for name, n_max in (("small_mixed", None), ("serving_6bit", 1), ("highconc_4p5bit", 1)):
+        wc = wl.WORKLOADS[name]
+        n_max = wc.T if n_max is None else n_max
+        psc = wl.random_packed_state(wc.B, wc.hv, wc.d, wc.n8, seed=wc.seed + 700)
+        n, t_ = _time_oracle_steps(oracle, wl, wc, psc, n_max, 60.0, threads)
+        configs[name] = dict(value=wc.B * wc.hv * n / t_, unit="state-updates/s", cores=threads,
+                             sample=f"{n} decode step(s) of {wc.B * wc.hv} units (d={wc.d}, "
+                                    f"n8={wc.n8}), {t_:.2f}s wall")
+    cpu["configs"] = configs
+    # the same oracle on one thread, over the first 64 sequences of one step
+    nb = min(B, 64)
+    x = wl.workload_inputs(w, 0)
+    t1 = time.perf_counter()
+    oracle.step(ps.pool8[:nb], ps.pool4[:nb], ps.r[:nb], ps.c, ps.perm, x.q[:nb], x.k[:nb],
+                x.v[:nb], x.alpha[:nb], x.beta[:nb], n8=w.n8, nthreads=1)
+    dt1 = time.perf_counter() - t1
+    cpu["single_thread"] = dict(value=nb * hv / dt1, unit="state-updates/s", cores=1,
+                                sample=f"one decode step of {nb * hv} units, {dt1:.2f}s")
+    log(f"[bench] oracle: {cpu['value']:.0f} updates/s on {threads} threads, "
+        f"{cpu['single_thread']['value']:.0f} on one; "
+        + ", ".join(f"{k}: {v['value']:.0f}" for k, v in configs.items()))
+    return cpu
+
+
+def trace_summary(path: str, timed: int) -> str:
+    """Per-kernel calls / avg / min / max (us) of a rocprofv3 kernel-trace CSV,
+    and each kernel's average over its last `timed` dispatches."""
+    import csv
+    import re
+
+    durs: dict[str, list[float]] = {}
+    with open(path, newline="") as f:
+        rows = sorted(csv.DictReader(f), key=lambda r_: int(r_["Start_Timestamp"]))
+    for r_ in rows:
+        name = re.sub(r"\(.*$", "", r_["Kernel_Name"]).replace("void ", "").strip()
+        durs.setdefault(name, []).append(
+            (int(r_["End_Timestamp"]) - int(r_["Start_Timestamp"])) / 1e3)
+    out = [f"{'kernel':<58} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} "
+           f"{'last_' + str(timed) + '_avg_us':>16}"]
+    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        tail = v[-timed:] if len(v) >= timed else v
+        out.append(f"{name[:58]:<58} {len(v):>6} {sum(v) / len(v):>9.1f} {min(v):>9.1f} "
+                   f"{max(v):>9.1f} {sum(tail) / len(tail):>16.1f}")
+    return "\n".join(out)
+
+
 def main():
     args = parse()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary, args.timed_launches or args.blocks * args.steps))
+        return
     if args.gpus != 1:
         log("bench.py measures one GPU only: the decode step has no exchange between units, "
             "so a multi-GPU run would shard sequence slots and run this same kernel on each "
@@ -279,6 +373,13 @@ def main():
     o = o_f32
 
     alloc_cal = {}  # gated -> (counts, c, perm, w2) of the ragged format
+    gate_cache = []
+
+    def gate_window():
+        if not gate_cache:
+            gate_cache.extend(dev(wl.draw_gate(B, hv, d, seed=w.seed, step=t))
+                              for t in range(len(window)))
+        return gate_cache
 
     def make_pools(fmt: int, n8: int, n: int, gated: bool = False):
         pools = []
@@ -310,24 +411,47 @@ def main():
         else:
             src.decode_step(q, k, v, a, b, o=o)
 
+    def warm_up(pools, warmup, into, run):
+        """The --warmup launches, then more until --warmup-floor-ms of wall
+        time has passed since the first; returns the launches made (all of
+        them reported).  `run(t)` issues launch t and returns how many it
+        issued."""
+        t0 = time.perf_counter()
+        n = 0
+        while n < warmup:
+            n += run(n)
+        torch.cuda.synchronize()
+        while (time.perf_counter() - t0) * 1e3 < args.warmup_floor_ms:
+            for _ in range(16):
+                n += run(n)
+            torch.cuda.synchronize()
+        return n
+
     def time_decode(pools, steps, warmup, into=False):
-        """HIP events on the launch stream around the K back-to-back launches:
-        their mean is the average launch duration (no event between launches)."""
+        """Warm-up, then --blocks timed blocks of `steps` back-to-back
+        launches, each bracketed by HIP events on the launch stream (no event
+        between launches); the blocks follow each other without a host
+        synchronisation.  Returns per-block ms per launch and the warm-up
+        launch count."""
         if args.graph:
             return time_decode_graph(pools, steps, warmup, into)
         stream = torch.cuda.current_stream()
-        for t in range(warmup):
+
+        def run(t):
             launch(pools, t, into)
+            return 1
+        n_warm = warm_up(pools, warmup, into, run)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.blocks)]
+        t = n_warm
+        for start, end in ev:
+            start.record(stream)
+            for _ in range(steps):
+                launch(pools, t, into)
+                t += 1
+            end.record(stream)
         torch.cuda.synchronize()
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        for t in range(steps):
-            launch(pools, t, into)
-        end.record(stream)
-        torch.cuda.synchronize()
-        total_ms = start.elapsed_time(end)
-        return total_ms, total_ms / steps
+        return [start.elapsed_time(end) / steps for start, end in ev], n_warm
 
     def time_decode_graph(pools, steps, warmup, into=False):
         """The same launches captured once in a HIP graph (one pass over the
@@ -347,39 +471,41 @@ def main():
             for t in range(period):
                 launch(pools, t, into)
         reps = max(1, -(-steps // period))
-        for _ in range(max(1, -(-warmup // period))):
+
+        def run(_t):
             graph.replay()
-        torch.cuda.synchronize()
+            return period
+        n_warm = warm_up(pools, warmup, into, run) + period  # + the eager pass
         stream = torch.cuda.current_stream()
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        for _ in range(reps):
-            graph.replay()
-        end.record(stream)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.blocks)]
+        for start, end in ev:
+            start.record(stream)
+            for _ in range(reps):
+                graph.replay()
+            end.record(stream)
         torch.cuda.synchronize()
-        total_ms = start.elapsed_time(end) * steps / (reps * period)
         del graph
-        return total_ms, total_ms / steps
+        return [start.elapsed_time(end) / (reps * period) for start, end in ev], n_warm
 
     def measure(fmt_name: str, fmt: int, n8: int, npools: int, steps: int, warmup: int,
                 into: bool = False, gated: bool = False, out_bf16: bool = False):
         nonlocal gates, o
         o = torch.empty((B, hv, d), dtype=torch.bfloat16, device="cuda") if out_bf16 else o_f32
+        if gated:  # per-key-row gates of the KDA form, one per window step (drawn first,
+            gates = gate_window()  # so that no host work separates set-up and warm-up)
         pools = make_pools(fmt, n8, npools, gated)
-        if gated:  # per-key-row gates of the KDA form, one per window step
-            gates = [dev(wl.draw_gate(B, hv, d, seed=w.seed, step=t))
-                     for t in range(len(window))]
-        total_ms, mean_ms = time_decode(pools, steps, warmup, into)
+        blocks, n_warm = time_decode(pools, steps, warmup, into)
         gates = None
         o = o_f32
+        mean_ms = sorted(blocks)[len(blocks) // 2]  # the median block
         nbytes = algorithmic_bytes(fmt_name, B, hv, hk, d, n8, in_el, gated, 2 if out_bf16 else 4)
         if fmt in (stq.FMT_ALLOC, stq.FMT_ALLOC_REFIT):
             unit = alloc_unit_bytes(alloc_cal[gated][0], d)
             nbytes = int(2 * unit * B * hv) + algorithmic_bytes("fp32", B, hv, hk, d, 0, in_el,
                                                                  gated) - 2 * 4 * d * d * B * hv
-        res = dict(updates_per_s=B * hv * steps / (total_ms / 1e3), ms_per_step=total_ms / steps,
-                   kernel_ms_mean=mean_ms,
+        res = dict(updates_per_s=B * hv / (mean_ms / 1e3), ms_per_step=mean_ms,
+                   kernel_ms_mean=mean_ms, blocks_ms_per_step=blocks, warmup_launches=n_warm,
                    algorithmic_bytes_per_launch=nbytes,
                    hbm_gbps=nbytes / (mean_ms / 1e3) / 1e9,
                    frac_of_peak=nbytes / (mean_ms / 1e3) / 1e9 / HBM_PEAK_GBPS,
@@ -453,38 +579,7 @@ def main():
     # ------------------------------------------------------- CPU baseline --
     cpu = None
     if not args.no_cpu_baseline and not args.only_decode:
-        import oracle
-
-        threads = oracle.default_threads()
-        ps = wl.random_packed_state(B, hv, d, w.n8, seed=w.seed + 700)
-        p8, p4, r = ps.pool8, ps.pool4, ps.r
-        # successive full decode steps of the workload until about 10 s of CPU
-        # work (at most 32 steps), each from the previous step's packed state
-        n_steps, dt = 0, 0.0
-        while n_steps < 32 and dt < 10.0:
-            x = wl.workload_inputs(w, n_steps)
-            t1 = time.perf_counter()
-            res = oracle.step(p8, p4, r, ps.c, ps.perm, x.q, x.k, x.v, x.alpha, x.beta,
-                              n8=w.n8, nthreads=threads)
-            dt += time.perf_counter() - t1
-            p8, p4, r = res["pool8"], res["pool4"], res["r"]
-            n_steps += 1
-        cpu = dict(value=B * hv * n_steps / dt, unit="state-updates/s", cores=threads,
-                   kind="oracle",
-                   sample=f"{n_steps} successive full decode steps of the workload ({B * hv} "
-                          f"units each, d={d}, n8={w.n8}) from a seeded random packed state, "
-                          f"{dt:.1f}s wall on {threads} threads")
-        # the same oracle on one thread, over the first 64 sequences of one step
-        nb = min(B, 64)
-        x = wl.workload_inputs(w, 0)
-        t1 = time.perf_counter()
-        oracle.step(p8[:nb], p4[:nb], r[:nb], ps.c, ps.perm, x.q[:nb], x.k[:nb], x.v[:nb],
-                    x.alpha[:nb], x.beta[:nb], n8=w.n8, nthreads=1)
-        dt1 = time.perf_counter() - t1
-        cpu["single_thread"] = dict(value=nb * hv / dt1, unit="state-updates/s", cores=1,
-                                    sample=f"one decode step of {nb * hv} units, {dt1:.2f}s")
-        log(f"[bench] oracle: {cpu['value']:.0f} updates/s on {threads} threads, "
-            f"{cpu['single_thread']['value']:.0f} on one")
+        cpu = cpu_baseline(np, wl, w, B, hv, d)
 
     # -------------------------------------------------------- roofline etc --
     traffic = None
@@ -505,6 +600,11 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": main_res["ms_per_step"],
+        "timing": {"blocks": args.blocks, "steps_per_block": args.steps,
+                   "blocks_ms_per_step": main_res["blocks_ms_per_step"],
+                   "statistic": "median block",
+                   "warmup_launches": main_res["warmup_launches"],
+                   "warmup_floor_ms": args.warmup_floor_ms},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -185,11 +185,19 @@ typedef struct {
  * stq_set_alloc_layout installs a layout chosen elsewhere. */
 
 /* Bytes of device memory a state with this geometry needs (host arithmetic
- * only, no device call); 0 if the descriptor is invalid or unsupported. */
+ * only, no device call); 0 if the descriptor is invalid or unsupported.  The
+ * state is the representation of Sec. 4.3 (X = r_i c_j z_ij: low-bit codes
+ * z, a factor per key row, a factor per value column) stored as the
+ * slot-indexed packed pages of App. F.1, one page per request slot, sized
+ * for the reserved slots of App. F.3: per (slot, head) the code rows of each
+ * width plus the fp32 row factors; per head the calibration arrays. */
 size_t stq_state_bytes(const stq_desc *desc);
 
 /* Carve a state out of the caller's device buffer `dev` (256-byte aligned,
- * `bytes` >= stq_state_bytes) and queue its initialisation on `stream`:
+ * `bytes` >= stq_state_bytes) and queue its initialisation on `stream`: the
+ * packed pages of App. F.1 (slot s of the pool is request slot s; slots are
+ * initialised and reused by the caller) holding the Sec. 4.3 representation,
+ * every page starting as the zero state:
  * codes 0, r = 2^-126 (the state S = 0), c = 1, cs = 1, w2 = 1,
  * perm = identity, fp32 state 0, statistics 0.  INT8ROW and FP32 states are
  * ready to decode at once; a MIXED48 or REFIT state must be calibrated
@@ -321,8 +329,11 @@ stq_status stq_set_calibration(stq_state *st, const float *c, const int32_t *per
 
 /* Pack fp32 states S [B][Hv][dk][dv] (logical order) into slots[b] (slots: a
  * device int32 array of B distinct slots, or NULL for slots 0..B-1): the
- * requantization half of a decode step applied to a given state (the
- * prefill-boundary pack).  FP32 format: copies S.  REFIT: codes and row
+ * requantization half of a decode step applied to a given state: the pack at
+ * the prefill boundary (App. F.1: prefill runs on unpacked states and packs
+ * the boundary states; App. B.2: the uncompressed prefill state is packed
+ * once, and decode then reads and rewrites the packed state), with the
+ * quantizer of App. C.3 Table C2 steps 4 and 6.  FP32 format: copies S.  REFIT: codes and row
  * factors against the calibrated per-head c, then each state's column factors
  * refit (see "Online column refit").
  * Errors: STQ_E_ARG, STQ_E_SHAPE (B < 1 or B > n_slots), STQ_E_STATE

@@ -1,6 +1,7 @@
 """Per-step parity along the GPU's own trajectory of the serving and the
 high-concurrency workloads (B = 256 and 1024 sequences, 32 value heads over
-16 key heads, d = 128, bf16 inputs, the 6-bit mix), in the launch
+16 key heads, d = 128, bf16 inputs, the 6-bit mix and, at B = 1024, the
+4.5-bit mix of 16 int8 rows), in the launch
 configuration the benchmark times.  The library generates nothing here: S0
 and the inputs come from the seeded generators, the library calibrates from
 32 unquantized steps, packs S0 and runs the workload's T = 100 steps in
@@ -47,7 +48,7 @@ def _calibrate(w, S0_dev):
     return cal.c.clone(), cal.perm.clone()
 
 
-@pytest.mark.parametrize("name", ["serving_6bit", "highconc_6bit"])
+@pytest.mark.parametrize("name", ["serving_6bit", "highconc_6bit", "highconc_4p5bit"])
 def test_workload_trajectory_checkpoints(oracle_mod, name):
     w = wl.WORKLOADS[name]
     checks = {1, 2, w.T // 2, w.T}
