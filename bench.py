@@ -282,13 +282,21 @@ def trace_summary(path: str, timed: int) -> str:
     """Per-kernel calls / avg / min / max (us) of a rocprofv3 kernel-trace CSV,
     and each kernel's average over its last `timed` dispatches."""
     import csv
-    import re
 
     durs: dict[str, list[float]] = {}
     with open(path, newline="") as f:
         rows = sorted(csv.DictReader(f), key=lambda r_: int(r_["Start_Timestamp"]))
+    def short(name):
+        name = name.replace("(anonymous namespace)::", "").replace("void ", "").strip()
+        depth = 0
+        for i, ch in enumerate(name):  # cut the argument list after the template
+            depth += (ch == "<") - (ch == ">")
+            if ch == "(" and depth == 0:
+                return name[:i]
+        return name
+
     for r_ in rows:
-        name = re.sub(r"\(.*$", "", r_["Kernel_Name"]).replace("void ", "").strip()
+        name = short(r_["Kernel_Name"])
         durs.setdefault(name, []).append(
             (int(r_["End_Timestamp"]) - int(r_["Start_Timestamp"])) / 1e3)
     out = [f"{'kernel':<58} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} "

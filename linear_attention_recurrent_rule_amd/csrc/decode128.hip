@@ -252,7 +252,9 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
             const float4 f = sh.red[ww][ce][0][cc];
             u += (f.x + f.y) + f.z;
         }
-        sh.ez[ezi] = __builtin_fmaf(-L.alpha, u, sh.v[jcol] * __builtin_amdgcn_rcpf(sh.c[jcol]));
+        // v / c to within a hair of correct rounding: a row whose update nearly
+        // cancels its decayed content amplifies any rounding of e
+        sh.ez[ezi] = __builtin_fmaf(-L.alpha, u, div_refined(sh.v[jcol], sh.c[jcol]));
     } else {
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
@@ -296,8 +298,9 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
         const float sc = sh.row[p].y;
         const float mrow = fabsf(sc) * rmax;
         const bool row8 = N8 == kRuntimeN8 ? p < L.n8 : mm < M8;
-        const float qinv = self(lane_mask(row8), 1.0f / 127.0f, 1.0f / 7.0f);
-        const float rn = fmaxf(mrow * qinv, kRowFloor);
+        const uint32_t m8 = lane_mask(row8);
+        const float rn = fmaxf(div_refined(mrow, self(m8, 127.0f, 7.0f), self(m8, 1.0f / 127.0f, 1.0f / 7.0f)),
+                               kRowFloor);
         const float inv = __builtin_amdgcn_rcpf(rn);
         float mul = sc * inv;
         mul = fminf(fmaxf(mul, -kMulMax), kMulMax);
@@ -513,7 +516,7 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, UnitGeom u
         // |b k| > 2^-64 |a r| (false when both vanish: then x = 0 * z = 0)
         const uint32_t scaled = lane_mask(fabsf(bk) > fabsf(ar) * kFormTiny);
         const float w2 = REFIT ? __uint_as_float(pick(u0, u1)) : 0.0f;
-        sh.row[p] = make_float4(self(scaled, ar * __builtin_amdgcn_rcpf(bk), ar), self(scaled, bk, 1.0f), w2,
+        sh.row[p] = make_float4(self(scaled, div_refined(ar, bk), ar), self(scaled, bk, 1.0f), w2,
                                 __uint_as_float(sel(scaled, 0u, 4u * D)));
         const float kq = wave_sum(kp * qp);
         if ((t & 63) == 0) sh.kq[t >> 6] = kq;

@@ -83,6 +83,22 @@ __device__ __forceinline__ float self(uint32_t m, float a, float b) {
     return __uint_as_float(sel(m, __float_as_uint(a), __float_as_uint(b)));
 }
 
+// n / d to within a hair of correct rounding: the hardware reciprocal r of d
+// (about 1 ulp), the quotient q = n r, and one Newton correction of q by its
+// exactly computed residual n - d q (Markstein's scheme).  Where a row factor
+// or a scaled coefficient ends in a near-cancellation, an ulp more in a
+// quotient shows up amplified in the result.
+__device__ __forceinline__ float div_refined(float n, float d) {
+    const float r = __builtin_amdgcn_rcpf(d);
+    const float q = n * r;
+    return __builtin_fmaf(__builtin_fmaf(-d, q, n), r, q);
+}
+// The same with the reciprocal of d supplied (r ~ 1/d to about 1 ulp).
+__device__ __forceinline__ float div_refined(float n, float d, float r) {
+    const float q = n * r;
+    return __builtin_fmaf(__builtin_fmaf(-d, q, n), r, q);
+}
+
 // ---- lane exchange inside 16-lane rows (GFX9 DPP controls)
 template <int CTRL> __device__ __forceinline__ uint32_t dpp(uint32_t v) {
     return static_cast<uint32_t>(
