@@ -227,6 +227,19 @@ stq_status stq_alloc_state(const stq_desc *desc, void *dev, size_t bytes,
 stq_status stq_calibrate(stq_state *st, const float *records, int64_t n_rec,
                          uint32_t flags, stq_stream_t stream);
 
+/* stq_calibrate for callers that cannot allocate device memory (code under
+ * graph capture, serving loops, harnesses that forbid allocation): the same
+ * arguments, rules and results, with the per-chunk partial results held in a
+ * fixed 6 MiB array of the library (one copy per GPU, kept until the process
+ * ends) instead of the state's partial arrays.  Allocates nothing.  Limit:
+ * n_heads_v * d_k <= 8192 head rows, else STQ_E_SPACE before anything is
+ * queued.  The state must live on the current device.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other host threads) race and must be ordered by the caller.
+ * Errors: as stq_calibrate, plus STQ_E_SPACE (too many head rows). */
+stq_status stq_calibrate_static(stq_state *st, const float *records, int64_t n_rec,
+                                uint32_t flags, stq_stream_t stream);
+
 /* Row-impact calibration of a REFIT state (Sec. 4.1; App. C.1 with the
  * scalar gate; App. B.3 for the exponent): for B calibration samples of one
  * step (q, k [B][Hk][dk] fp32 or bf16 by `dtype`, alpha, beta [B][Hv] fp32),

@@ -274,6 +274,19 @@ stq_status stq_calibrate(stq_state *st, const float *records, int64_t n_rec, uin
                          stq_stream_t stream) {
     stq_status e = check_state(st);
     if (e != STQ_OK) return e;
+    return stq::calibrate_with(st, records, n_rec, flags, stream, st->cal_colpart,
+                               st->cal_rowpart);
+}
+
+} // extern "C"
+
+// The body of stq_calibrate with the per-chunk partial results in colpart and
+// rowpart (the state's own arrays, or another buffer of the same size).
+stq_status stq::calibrate_with(stq_state *st, const float *records, int64_t n_rec,
+                               uint32_t flags, stq_stream_t stream, float *colpart,
+                               double *rowpart) {
+    stq_status e = check_state(st);
+    if (e != STQ_OK) return e;
     if (!calibrated_format(st->desc.fmt)) return STQ_E_ARG;
     const bool ragged = alloc_format(st->desc.fmt);
     const uint32_t allowed = ragged ? (STQ_CAL_RESET | STQ_CAL_COLS | STQ_CAL_FINALIZE | STQ_CAL_DIST)
@@ -293,8 +306,8 @@ stq_status stq_calibrate(stq_state *st, const float *records, int64_t n_rec, uin
     a.do_rows = (flags & STQ_CAL_ROWS) ? 1 : 0;
     a.colmax = st->colmax;
     a.rowscore = st->rowscore;
-    a.colpart = st->cal_colpart;
-    a.rowpart = st->cal_rowpart;
+    a.colpart = colpart;
+    a.rowpart = rowpart;
     a.c = st->c;
     a.perm = ragged ? nullptr : st->perm; // ragged: perm comes from stq_allocate
     if (flags & STQ_CAL_RESET) {
@@ -332,6 +345,8 @@ stq_status stq_calibrate(stq_state *st, const float *records, int64_t n_rec, uin
     }
     return STQ_OK;
 }
+
+extern "C" {
 
 stq_status stq_set_calibration(stq_state *st, const float *c, const int32_t *perm,
                                stq_stream_t stream) {

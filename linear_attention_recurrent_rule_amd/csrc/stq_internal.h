@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "stq.h"
+
 namespace stq {
 
 // One decode launch: B sequences x Hv value heads, in place on slots[b].
@@ -153,5 +155,11 @@ hipError_t launch_copy_bytes(const void *src, void *dst, size_t bytes, hipStream
 bool assign_rows(int Hv, int D, const double *dist, const double *logret, double n,
                  int horizon, unsigned cand_mask, int nominal, int n_pivot, int32_t *counts,
                  int32_t *perm);
+
+// stq_calibrate with its per-chunk partial results in colpart [Hv][kCalChunks][D]
+// and rowpart [Hv][kCalChunks][D] instead of the state's own arrays (both
+// device memory, 16-byte aligned).  Defined in stq_api.cpp.
+stq_status calibrate_with(stq_state *st, const float *records, int64_t n_rec, uint32_t flags,
+                          stq_stream_t stream, float *colpart, double *rowpart);
 
 } // namespace stq

@@ -62,7 +62,7 @@ EXPORTS = ("stq_state_bytes", "stq_alloc_state", "stq_calibrate", "stq_calibrate
            "stq_decode_step", "stq_decode_step_into", "stq_decode_step_gated",
            "stq_dequant_state", "stq_stream_copy", "stq_status_str", "stq_abi_version",
            "stq_calibrate_retention", "stq_allocate", "stq_set_alloc_layout",
-           "stq_assign_rows")
+           "stq_assign_rows", "stq_calibrate_static")
 
 
 def _lib():
@@ -79,6 +79,7 @@ def _lib():
         lib.stq_state_bytes.restype = SZ
         lib.stq_alloc_state.argtypes = [ctypes.POINTER(Desc), P, SZ, P, ctypes.POINTER(CState)]
         lib.stq_calibrate.argtypes = [ctypes.POINTER(CState), P, I64, U32, P]
+        lib.stq_calibrate_static.argtypes = lib.stq_calibrate.argtypes
         lib.stq_set_calibration.argtypes = [ctypes.POINTER(CState), P, P, P]
         lib.stq_calibrate_impact.argtypes = [ctypes.POINTER(CState), P, P, I32, P, P, I32, U32, P]
         lib.stq_calibrate_impact_gated.argtypes = lib.stq_calibrate_impact.argtypes
@@ -102,7 +103,7 @@ def _lib():
                      "stq_pack_state", "stq_decode_step", "stq_decode_step_into",
                      "stq_decode_step_gated", "stq_dequant_state", "stq_stream_copy",
                      "stq_calibrate_retention", "stq_allocate", "stq_set_alloc_layout",
-           "stq_assign_rows"):
+           "stq_assign_rows", "stq_calibrate_static"):
             getattr(lib, name).restype = I32
         _LIB = lib
     return _LIB
@@ -388,6 +389,16 @@ class State:
         p = _dev_ptr(records, "records", (n, g.n_heads_v, g.d, g.d), _F32, self.buffer.device)
         _check(_lib().stq_calibrate(ctypes.byref(self.c_state), p, n, flags, _stream(stream)),
                "stq_calibrate")
+
+    def calibrate_static(self, records: torch.Tensor | None, flags: int, stream=None):
+        """stq_calibrate_static: as calibrate, with the partial results in the
+        library's fixed per-GPU array (allocates nothing; calls on one GPU
+        must not overlap)."""
+        g = self.geo
+        n = 0 if records is None else _batch(records, "records")
+        p = _dev_ptr(records, "records", (n, g.n_heads_v, g.d, g.d), _F32, self.buffer.device)
+        _check(_lib().stq_calibrate_static(ctypes.byref(self.c_state), p, n, flags,
+                                           _stream(stream)), "stq_calibrate_static")
 
     def calibrate_impact(self, q, k, alpha, beta, flags: int, stream=None, gate=None):
         """Accumulate row impact over one step's samples (q, k [B][Hk][d], alpha,

@@ -350,3 +350,14 @@ def test_alloc_rejections():
     fat = np.tile(np.array([64, 0, 0, 0, 0], np.int32), (4, 1))  # all pivots: too big
     assert lib.stq_set_alloc_layout(ctypes.byref(st), fat.ctypes.data, FAKE, FAKE,
                                     None) == E_SPACE
+
+
+def test_calibrate_static_rejections():
+    lib = stq.lib()
+    big = stq.CState()
+    big.desc = _desc(hv=128, hk=64, d=128, n8=64)  # 16384 head rows: over the fixed array
+    assert lib.stq_calibrate_static(ctypes.byref(big), FAKE, 1, stq.CAL_COLS, None) == E_SPACE
+    assert lib.stq_calibrate_static(None, FAKE, 1, stq.CAL_COLS, None) == E_ARG
+    bad = stq.CState()
+    bad.desc = _desc(hv=0)
+    assert lib.stq_calibrate_static(ctypes.byref(bad), FAKE, 1, stq.CAL_COLS, None) == E_SHAPE
