@@ -3,28 +3,28 @@
 // (STEPQuant paper, arXiv 2609.38169: App. C.2 Table C1 for the classes,
 // App. C.3 Table C2 for the step with pivots; Sec. 2.1 Eq. (1) with either
 // gate; Sec. 2.2 quantizer; Sec. 4.3 representation).  Same arithmetic
-// contract as decode_alloc_kernel in alloc_kernels.hip, arranged like the
-// fixed-split 128 x 128 kernel:
+// contract as decode_alloc_kernel in alloc_kernels.hip, on the tile and the
+// helpers of the fixed-split 128 x 128 kernel (tile128.h):
 //
-//  * lane (g, c), g = lane / 16, c = lane % 16, owns columns 8c..8c+7 of
-//    physical rows g + 16 m, m = 0..7; wave w therefore holds rows
-//    16 m + 4 w .. 16 m + 4 w + 3 in slot m.  A head's rows are sorted by
-//    class, so those four rows almost always share one class: the wave then
-//    branches on a scalar class and runs the code of that class; only a slot
-//    that straddles a class boundary takes a per-lane branch;
+//  * lane (g, c) owns columns 8c..8c+7 of physical rows g + 16 m; wave w
+//    holds rows 16 m + 4 w .. 16 m + 4 w + 3 in slot m.  A head's rows are
+//    sorted by class, so those four rows almost always share one class: the
+//    wave then branches on a scalar class and runs the code of that class;
+//    only a slot that straddles a class boundary takes a per-lane branch;
 //  * the per-unit vectors (perm, r, k, q, v, c, gate) are loaded before the
-//    codes at addresses that depend on no other load: k and q are read in
-//    logical order, two entries per lane, and brought into physical row order
-//    by lane permutes instead of a gather through perm;
+//    codes at addresses that depend on no other load; k and q are brought
+//    into physical row order by lane permutes;
 //  * integer codes are widened so that every class fits a signed byte: 8-bit
 //    codes as z, 6-bit as 4 z, 4-bit as 16 z, 2-bit as 64 z (the row
-//    coefficients carry the inverse power of two);
-//  * column sums u~ = S~^T (r k), w~ = S~^T (r q) on the matrix cores as bf16
-//    products with exact three-way splits of the row coefficients; a pivot
-//    row enters with its binary16 value h split exactly into two bf16 parts
-//    (hi: the top 8 significant bits, lo: the remaining 3) and its
-//    coefficients in separate output rows, whose sums are divided by c_j
-//    afterwards (a pivot row has no column factor: its contribution to the
+//    coefficients carry the inverse power of two).  A widened code is an fp32
+//    register whose low 16 bits are zero, fed to the matrix cores as the
+//    bf16 pair (0, z) with the coefficient words at the odd K positions;
+//  * a pivot row holds its binary16 value h in that register: the matrix
+//    core reads its high half, h truncated to 8 significant bits, and a
+//    second product adds the remainder h - hi (at most 3 significant bits,
+//    exact in bf16) where the wave holds pivot rows.  Pivot coefficients sit
+//    in separate output rows, whose sums are divided by c_j afterwards (a
+//    pivot row has no column factor: its contribution to the
 //    column-normalised sums is k_i h_ij / c_j);
 //  * the update x_ij = X_ij / c_j = s_i (P_i z_ij + E_ij), the DPP row-max
 //    reduce-scatter, the row factors and the code FMA against 1.5 * 2^23 are
@@ -33,33 +33,16 @@
 //    even, saturated at +-65504), with r = 0 and no part in the column refit.
 #include <hip/hip_runtime.h>
 
-#include "stq_internal.h"
+#include <type_traits>
+
+#include "tile128.h"
 
 namespace stq {
 namespace {
 
-constexpr int D = 128;
-constexpr float kRoundMagic = 12582912.0f;               // 1.5 * 2^23
-constexpr float kRowFloor = 1.17549435082228750797e-38f; // 2^-126
-constexpr float kMulMax = 1.70141183460469231732e38f;    // 2^127
-constexpr float kFormTiny = 5.42101086242752217004e-20f; // 2^-64
-constexpr float kHalfMax = 65504.0f;
+using namespace t128;
 
-// Input elements as raw bits (a load whose result is only moved does not
-// wait for it) and their fp32 value.
-template <typename T> struct In;
-template <> struct In<float> {
-    static __device__ __forceinline__ uint32_t raw(const void *p, unsigned i) {
-        return static_cast<const uint32_t *>(p)[i];
-    }
-    static __device__ __forceinline__ float cvt(uint32_t bits) { return __uint_as_float(bits); }
-};
-template <> struct In<uint16_t> {
-    static __device__ __forceinline__ uint32_t raw(const void *p, unsigned i) {
-        return static_cast<const uint16_t *>(p)[i];
-    }
-    static __device__ __forceinline__ float cvt(uint32_t bits) { return __uint_as_float(bits << 16); }
-};
+constexpr float kHalfMax = 65504.0f;
 
 // Bytes per row of each class (pivot, 8, 6, 4, 2 bits).
 template <int K> struct Cls;
@@ -95,17 +78,18 @@ template <int K> __device__ __forceinline__ int slot_base(const Bounds &L, int m
 
 template <typename F> __device__ __forceinline__ void with_class(int k, F &&f) {
     switch (k) {
-    case 0: f(IC<0>{}); break;
+    case 2: f(IC<2>{}); break; // the commonest classes first
     case 1: f(IC<1>{}); break;
-    case 2: f(IC<2>{}); break;
     case 3: f(IC<3>{}); break;
+    case 0: f(IC<0>{}); break;
     default: f(IC<4>{}); break;
     }
 }
 
 // Per wave, once per unit: the class of each slot's four rows (4 bits per
 // slot), or 7 where they straddle a class boundary.  Lane m computes slot m
-// and the eight results are read back into a scalar.
+// and the eight results are read back into a scalar (so the per-slot class
+// branches below are scalar branches).
 __device__ __forceinline__ unsigned slot_table(const Bounds &L, int wv, int lane) {
     const int m = lane & 7;
     const int p0 = 16 * m + 4 * wv;
@@ -128,6 +112,14 @@ __device__ __forceinline__ void per_slot(const Bounds &L, unsigned tab, int g, i
     if (k != 7) with_class(k, f);
     else with_class(class_of(L, g + 16 * m), f);
 }
+
+// Lane constants of the chunk layouts: masks of c & 1 and c & 2, and the
+// shift 16 (c & 1) that brings the lane's 16-bit field of a 32-bit word down.
+struct ChunkLane {
+    uint32_t odd;  // lane mask of c & 1
+    uint32_t half; // lane mask of c & 2
+    uint32_t sh;   // 16 (c & 1)
+};
 
 // Every slot issues the same two 8-byte loads, A and B, whatever its class
 // (so no register is written by different instructions on different paths
@@ -158,76 +150,42 @@ __device__ __forceinline__ void chunk_offsets(unsigned row, int c, unsigned &off
     }
 }
 
-// The raw words of the lane's chunk from the two loads.
-template <int K>
-__device__ __forceinline__ void chunk_words(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1,
-                                            int c, uint32_t (&w)[4]) {
-    if constexpr (K == 0) {
-        w[0] = a0; w[1] = a1; w[2] = b0; w[3] = b1;
-    } else if constexpr (K == 1) {
-        w[0] = a0; w[1] = a1;
-    } else if constexpr (K == 2) {
-        w[0] = (c & 1) ? a1 : a0;
-        w[1] = (((c & 2) ? b1 : b0) >> (16 * (c & 1))) & 0xFFFFu;
-    } else if constexpr (K == 3) {
-        w[0] = (c & 1) ? a1 : a0;
-    } else {
-        w[0] = (((c & 2) ? a1 : a0) >> (16 * (c & 1))) & 0xFFFFu;
-    }
-}
-
-__device__ __forceinline__ float sbyte(uint32_t w, int k) {
-    return static_cast<float>(static_cast<int8_t>(w >> (8 * k)));
-}
-
 // Byte e' of the result holds nibble e' of the 16-bit value x (e' = 0..3).
 __device__ __forceinline__ uint32_t nibbles_to_bytes(uint32_t x) {
     const uint32_t t = __builtin_amdgcn_perm(x, x, 0x01010000u); // bytes [x0, x0, x1, x1]
     return (t & 0x000F000Fu) | ((t >> 4) & 0x0F000F00u);
 }
 
-// Widen a chunk: z = W code as fp32 for integer rows (W = 1, 4, 16, 64 for
-// 8, 6, 4, 2 bits); the binary16 value for pivot rows.
-template <int K> __device__ __forceinline__ void widen(const uint32_t (&w)[4], float (&z)[8]) {
+// The codes of one integer slot as two words of left-aligned bytes: byte j
+// of ev (od) is the code of column 8c + 2j (2j + 1) times W = 1, 4, 16, 64
+// for 8, 6, 4, 2 bits.  Only these two words depend on the class, so the
+// class branch defines two registers and the conversions to fp32 follow it.
+// ld = the slot's two loads (A.x, A.y, B.x, B.y).
+template <int K>
+__device__ __forceinline__ void code_words(const uint32_t (&ld)[4], const ChunkLane &cl, uint32_t &ev,
+                                           uint32_t &od) {
     if constexpr (K == 0) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            z[e] = static_cast<float>(
-                __builtin_bit_cast(_Float16, static_cast<uint16_t>(w[e >> 1] >> (16 * (e & 1)))));
+        ev = 0u; // a pivot slot: its values are converted separately
+        od = 0u;
     } else if constexpr (K == 1) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            z[e] = sbyte(w[0], e);
-            z[4 + e] = sbyte(w[1], e);
-        }
-    } else if constexpr (K == 2) {
-        // code bits 0..3 from the nibble word, bits 4..5 from the 2-bit
-        // fields; byte e' of ev (od) = code of column 2e' (2e'+1) << 2
-        const uint32_t s = nibbles_to_bytes(w[1]);
-        const uint32_t ev = ((w[0] << 2) & 0x3C3C3C3Cu) | ((s << 6) & 0xC0C0C0C0u);
-        const uint32_t od = ((w[0] >> 2) & 0x3C3C3C3Cu) | ((s << 4) & 0xC0C0C0C0u);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            z[2 * e] = sbyte(ev, e);
-            z[2 * e + 1] = sbyte(od, e);
-        }
+        ev = __builtin_amdgcn_perm(ld[1], ld[0], 0x06040200u);
+        od = __builtin_amdgcn_perm(ld[1], ld[0], 0x07050301u);
     } else if constexpr (K == 3) {
-        const uint32_t hi = w[0] & 0xF0F0F0F0u;        // odd columns, x16
-        const uint32_t lo = (w[0] << 4) & 0xF0F0F0F0u; // even columns, x16
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            z[2 * e] = sbyte(lo, e);
-            z[2 * e + 1] = sbyte(hi, e);
-        }
+        const uint32_t w = sel(cl.odd, ld[1], ld[0]);
+        ev = (w << 4) & 0xF0F0F0F0u;
+        od = w & 0xF0F0F0F0u;
+    } else if constexpr (K == 2) {
+        // code bits 0..3 from the nibble word, bits 4..5 from the 2-bit fields
+        const uint32_t w = sel(cl.odd, ld[1], ld[0]);
+        const uint32_t f = sel(cl.half, ld[3], ld[2]) >> cl.sh;
+        const uint32_t n = nibbles_to_bytes(f);
+        ev = ((w << 2) & 0x3C3C3C3Cu) | ((n << 6) & 0xC0C0C0C0u);
+        od = ((w >> 2) & 0x3C3C3C3Cu) | ((n << 4) & 0xC0C0C0C0u);
     } else {
-        const uint32_t s = nibbles_to_bytes(w[0]);
-        const uint32_t ev = (s << 6) & 0xC0C0C0C0u;
-        const uint32_t od = (s << 4) & 0xC0C0C0C0u;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            z[2 * e] = sbyte(ev, e);
-            z[2 * e + 1] = sbyte(od, e);
-        }
+        const uint32_t f = sel(cl.half, ld[1], ld[0]) >> cl.sh;
+        const uint32_t n = nibbles_to_bytes(f);
+        ev = (n << 6) & 0xC0C0C0C0u;
+        od = (n << 4) & 0xC0C0C0C0u;
     }
 }
 
@@ -242,33 +200,23 @@ __device__ __forceinline__ uint32_t bytes_to_nibbles(uint32_t n) {
 // whose low byte is the code in two's complement.
 template <int K>
 __device__ __forceinline__ void store_codes(uint8_t *base, unsigned off, int c,
-                                            const uint32_t (&bt)[8]) {
+                                            const uint32_t (&bt)[8], uint32_t lo4) {
     if constexpr (K == 1) {
-        const uint32_t a01 = __builtin_amdgcn_perm(bt[1], bt[0], 0x0C0C0400u);
-        const uint32_t a23 = __builtin_amdgcn_perm(bt[3], bt[2], 0x04000C0Cu);
-        const uint32_t a45 = __builtin_amdgcn_perm(bt[5], bt[4], 0x0C0C0400u);
-        const uint32_t a67 = __builtin_amdgcn_perm(bt[7], bt[6], 0x04000C0Cu);
-        *reinterpret_cast<uint2 *>(base + (off + 8u * c)) = make_uint2(a01 | a23, a45 | a67);
+        *reinterpret_cast<u32x2 *>(base + (off + 8u * c)) = pack_bytes(bt);
     } else {
-        // bytes of the even columns 0, 2, 4, 6 and of the odd columns
-        const uint32_t evn = __builtin_amdgcn_perm(bt[2], bt[0], 0x0C0C0400u) |
-                             __builtin_amdgcn_perm(bt[6], bt[4], 0x04000C0Cu);
-        const uint32_t odd = __builtin_amdgcn_perm(bt[3], bt[1], 0x0C0C0400u) |
-                             __builtin_amdgcn_perm(bt[7], bt[5], 0x04000C0Cu);
+        uint32_t evn, odd;
+        even_odd_bytes(bt, evn, odd);
         if constexpr (K == 2 || K == 3) {
-            const uint32_t word = (evn & 0x0F0F0F0Fu) | ((odd << 4) & 0xF0F0F0F0u);
-            *reinterpret_cast<uint32_t *>(base + (off + 4u * c)) = word;
+            *reinterpret_cast<uint32_t *>(base + (off + 4u * c)) = sel(lo4, evn, odd << 4);
         }
         if constexpr (K == 2) {
             // bits 4..5 of each code: column e in bits 2e of a 16-bit field
             const uint32_t n = ((evn >> 4) & 0x03030303u) | ((odd >> 2) & 0x0C0C0C0Cu);
-            *reinterpret_cast<uint16_t *>(base + (off + D / 2 + 2u * c)) =
-                static_cast<uint16_t>(bytes_to_nibbles(n));
+            *reinterpret_cast<uint16_t *>(base + (off + D / 2 + 2u * c)) = static_cast<uint16_t>(bytes_to_nibbles(n));
         }
         if constexpr (K == 4) {
             const uint32_t n = (evn & 0x03030303u) | ((odd << 2) & 0x0C0C0C0Cu);
-            *reinterpret_cast<uint16_t *>(base + (off + 2u * c)) =
-                static_cast<uint16_t>(bytes_to_nibbles(n));
+            *reinterpret_cast<uint16_t *>(base + (off + 2u * c)) = static_cast<uint16_t>(bytes_to_nibbles(n));
         }
     }
 }
@@ -278,75 +226,31 @@ __device__ __forceinline__ uint32_t half_bits(float x) {
     return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(x)));
 }
 
-template <int CTRL> __device__ __forceinline__ uint32_t dpp(uint32_t v) {
-    return static_cast<uint32_t>(
-        __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, true));
-}
-template <int CTRL> __device__ __forceinline__ float dppf(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-constexpr int kRowRor8 = 0x128;
-constexpr int kRowHalfMirror = 0x141;
-constexpr int kQuadXor2 = 0x4E;
-constexpr int kQuadXor1 = 0xB1;
-constexpr int kRowMirror = 0x140;
-
-__device__ __forceinline__ float wave_sum(float v) {
-    v += dppf<kQuadXor1>(v);
-    v += dppf<kQuadXor2>(v);
-    v += dppf<kRowHalfMirror>(v);
-    v += dppf<kRowMirror>(v);
-    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-    return (r0 + r1) + (r2 + r3);
-}
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-// Matrix-core operand A: per wave and lane group, 13 rows of 8 bf16 (one per
-// slot): 0..2 r k (hi, mid, lo) and 3..5 r q of integer rows; 6..8 d k and
-// 9..11 d q of pivot rows (d the row gate, 1 for the scalar gate); 12 zero.
-constexpr int kCoefRows = 13;
+// Matrix-core operand A: per wave and lane group, 12 rows of 8 words (one
+// per slot), each a bf16 part in its high half: 0..2 r k (hi, mid, lo) and
+// 3..5 r q of integer rows; 6..8 d k and 9..11 d q of pivot rows (d the row
+// gate, 1 for the scalar gate).  A row's words of the other kind are zero.
+constexpr int kCoefRows = 12;
 struct Smem {
-    uint16_t coef[4][4][kCoefRows][8];
-    float4 row[D];          // {P, s, w2, offset of E in ez} per physical row
-    float qinv[D];          // 1 / q_b per physical row, 0 for pivot rows
+    // per lane group G = 4 w + gl (wave w), padded by 16 bytes so that the
+    // staging lanes, which write one word each into 16 groups, spread over
+    // all 64 banks
+    struct {
+        uint32_t w[kCoefRows][8];
+        uint32_t pad[4];
+    } coef[16];
+    float4 row[D];          // {P, s, w2, byte offset of E in ez} per physical row
+    float qb[D];            // q_b per physical row, 0 for pivot rows
     float v[D], c[D];
     float ez[2 * D];        // e, then a zero vector; each as [e/4][c][e%4]
     float4 red[4][8][3][16]; // per wave, column offset e, lane group, chunk c
     float kq[2];
-    float mul[16][8];
-    float ra[16][8], rb[16][8];
+    float mul[16][8];       // per row group: code multipliers of its 8 rows
+    float ra[16][8], rb[16][8]; // column refit: w2 r' s and w2 r'^2 per row
 };
 
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-    const uint32_t u = __float_as_uint(x);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-__device__ __forceinline__ float bf16_val(uint32_t h) { return __uint_as_float(h << 16); }
-
-__device__ __forceinline__ void split3(float x, uint32_t &h0, uint32_t &h1, uint32_t &h2) {
-    h0 = bf16_bits(x);
-    const float r1 = x - bf16_val(h0);
-    h1 = bf16_bits(r1);
-    const float r2 = r1 - bf16_val(h1);
-    h2 = bf16_bits(r2);
-}
-
-__device__ __forceinline__ unsigned udiv(unsigned n, unsigned d, unsigned m) {
-    if (m == 0) return n;
-    unsigned q = __umulhi(n, m);
-    if (q * d > n) --q;
-    return q;
-}
-
 template <typename TIn, bool REFIT, bool GATED>
-__global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int xcd_remap,
-                                                              unsigned hv_m, unsigned g_m) {
+__global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, UnitGeom ug) {
     __shared__ Smem sh;
     const int t = threadIdx.x;
     const int c = t & 15;
@@ -355,15 +259,11 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
     const int gl = (t >> 4) & 3;
     const int wv = __builtin_amdgcn_readfirstlane(w);
 
-    unsigned unit = blockIdx.x;
-    if (xcd_remap) {
-        const unsigned per = gridDim.x >> 3;
-        unit = (blockIdx.x & 7u) * per + (blockIdx.x >> 3);
-    }
+    const unsigned unit = unit_of_block(ug.remap);
     const int Hv = a.Hv;
-    const int b = static_cast<int>(udiv(unit, static_cast<unsigned>(Hv), hv_m));
+    const int b = static_cast<int>(udiv(unit, static_cast<unsigned>(Hv), ug.hv_m));
     const int h = static_cast<int>(unit - static_cast<unsigned>(b) * static_cast<unsigned>(Hv));
-    const int hk = static_cast<int>(udiv(static_cast<unsigned>(h), static_cast<unsigned>(Hv / a.Hk), g_m));
+    const int hk = static_cast<int>(udiv(static_cast<unsigned>(h), static_cast<unsigned>(ug.G), ug.g_m));
     const int slot = a.slots ? a.slots[b] : b;
     if (slot < 0 || slot >= a.n_slots) { // whole workgroup leaves together
         if (t < D) store_o(a, static_cast<size_t>(unit) * D + t, __int_as_float(0x7fc00000));
@@ -373,7 +273,12 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
     const float beta = a.beta[unit];
     const size_t ub = static_cast<size_t>(slot) * Hv + h;
 
-    const int32_t *lay = a.layout + static_cast<size_t>(h) * kLayoutStride;
+    // the head's layout, read through the constant address space: nothing
+    // writes it during the step, and so it comes through the scalar cache,
+    // where the workgroups of a head find it, instead of a vector load whose
+    // latency would delay every row address
+    typedef __attribute__((address_space(4))) const int32_t cint32_t;
+    cint32_t *lay = (cint32_t *)(reinterpret_cast<uintptr_t>(a.layout) + static_cast<size_t>(h) * kLayoutStride * 4);
     Bounds L;
     {
         const int n0 = lay[0], n1 = lay[1], n2 = lay[2], n3 = lay[3];
@@ -393,7 +298,6 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
     const float *rr = a.r + ub * D;
     float *rw = a.r_out + ub * D;
 
-    const unsigned tab = slot_table(L, wv, t);
     // ---- the per-unit vectors, loaded at logical indices so that no load
     // waits for another one (the gathers through perm are lane permutes
     // below); they are issued before the codes, because loads complete in
@@ -428,7 +332,9 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
                    : reinterpret_cast<const uint32_t *>(a.c)[h * D + tl];
     }
 
-    // ---- Table C2 step 1: issue the loads of this lane's row chunks
+    // ---- Table C2 step 1: issue the loads of this lane's row chunks (their
+    // addresses are the first use of the head's layout)
+    const unsigned tab = slot_table(L, wv, t);
     uint32_t ld[8][4]; // per slot: A.x, A.y, B.x, B.y
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
@@ -438,12 +344,12 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
             chunk_offsets<K>(static_cast<unsigned>(slot_base<K>(L, m) + g * Cls<K>::row), c, offA,
                              offB);
         });
-        const uint2 A = *reinterpret_cast<const uint2 *>(seg_in + offA);
-        const uint2 Bw = *reinterpret_cast<const uint2 *>(seg_in + offB);
-        ld[m][0] = A.x;
-        ld[m][1] = A.y;
-        ld[m][2] = Bw.x;
-        ld[m][3] = Bw.y;
+        const u32x2 A = *reinterpret_cast<const u32x2 *>(seg_in + offA);
+        const u32x2 Bw = *reinterpret_cast<const u32x2 *>(seg_in + offB);
+        ld[m][0] = A[0];
+        ld[m][1] = A[1];
+        ld[m][2] = Bw[0];
+        ld[m][3] = Bw[1];
     }
 
     // ---- per-row and per-column factors, once per unit
@@ -452,45 +358,44 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
         const int k = class_of(L, p);
         const int i = praw & (D - 1);
         const int src = (i & 63) << 2;
-        const bool up = (i & 64) != 0;
+        const uint32_t up = lane_mask(i & 64);
         auto pick = [&](uint32_t lo, uint32_t hi) {
             const uint32_t a0 = __builtin_amdgcn_ds_bpermute(src, static_cast<int>(lo));
             const uint32_t a1 = __builtin_amdgcn_ds_bpermute(src, static_cast<int>(hi));
-            return up ? a1 : a0;
+            return sel(up, a1, a0);
         };
         const float kp = In<TIn>::cvt(pick(x0, x1));
         const float qp = In<TIn>::cvt(pick(x2, x3));
         // integer rows: r / W (codes are widened as W z); pivot rows: 1
-        const float winv = k == 1 ? 1.0f : (k == 2 ? 0.25f : (k == 3 ? 0.0625f : 0.015625f));
-        float scale = k == 0 ? 1.0f : rpv * winv;
+        const uint32_t piv = lane_mask(k == 0);
+        const float winv = __uint_as_float((127u - 2u * static_cast<unsigned>(k - 1)) << 23); // 2^(2 - 2k)
+        float scale = self(piv, 1.0f, rpv * winv);
         if (GATED) scale *= __uint_as_float(pick(g0, g1));
         {
-            uint16_t(&cf)[kCoefRows][8] = sh.coef[(p & 15) >> 2][p & 3];
+            uint32_t(&cf)[kCoefRows][8] = sh.coef[p & 15].w;
             const int mm = p >> 4;
-            const int on = k == 0 ? 6 : 0; // this row's coefficient rows
-            const int off = 6 - on;        // the other class's rows stay zero
-            uint32_t h0, h1, h2;
-            split3(scale * kp, h0, h1, h2);
-            cf[on + 0][mm] = static_cast<uint16_t>(h0);
-            cf[on + 1][mm] = static_cast<uint16_t>(h1);
-            cf[on + 2][mm] = static_cast<uint16_t>(h2);
-            split3(scale * qp, h0, h1, h2);
-            cf[on + 3][mm] = static_cast<uint16_t>(h0);
-            cf[on + 4][mm] = static_cast<uint16_t>(h1);
-            cf[on + 5][mm] = static_cast<uint16_t>(h2);
+            uint32_t wk[3], wq[3];
+            split3w(scale * kp, wk[0], wk[1], wk[2]);
+            split3w(scale * qp, wq[0], wq[1], wq[2]);
+            // this row's coefficient words in its kind's rows, zero in the other's
 #pragma unroll
-            for (int q = 0; q < 6; ++q) cf[off + q][mm] = 0;
+            for (int q = 0; q < 3; ++q) {
+                cf[q][mm] = sel(piv, 0u, wk[q]);
+                cf[3 + q][mm] = sel(piv, 0u, wq[q]);
+                cf[6 + q][mm] = sel(piv, wk[q], 0u);
+                cf[9 + q][mm] = sel(piv, wq[q], 0u);
+            }
         }
         const float ar = alpha * scale;
         const float bk = beta * kp;
-        const bool scaled = fabsf(bk) > fabsf(ar) * kFormTiny;
-        const float w2v = REFIT ? __uint_as_float(pick(u0, u1)) : 0.0f;
-        const float w2 = k != 0 ? w2v : 0.0f;
-        sh.row[p] = make_float4(scaled ? ar * __builtin_amdgcn_rcpf(bk) : ar, scaled ? bk : 1.0f, w2,
-                                __int_as_float(scaled ? 0 : D));
-        sh.qinv[p] = k == 0 ? 0.0f
-                            : (k == 1 ? (1.0f / 127.0f)
-                                      : (k == 2 ? (1.0f / 31.0f) : (k == 3 ? (1.0f / 7.0f) : 1.0f)));
+        // |b k| > 2^-64 |a r| (false when both vanish: then x = 0 * z = 0)
+        const uint32_t scaled = lane_mask(fabsf(bk) > fabsf(ar) * kFormTiny);
+        const float w2 = REFIT ? __uint_as_float(sel(piv, 0u, pick(u0, u1))) : 0.0f;
+        sh.row[p] = make_float4(self(scaled, div_refined(ar, bk), ar), self(scaled, bk, 1.0f), w2,
+                                __uint_as_float(sel(scaled, 0u, 4u * D)));
+        // q_b = 2^(b-1) - 1 for b = 8, 6, 4, 2; 0 marks a pivot row
+        const float qbk = static_cast<float>((1 << (9 - 2 * k)) - 1);
+        sh.qb[p] = self(piv, 0.0f, qbk);
         const float kq = wave_sum(kp * qp);
         if ((t & 63) == 0) sh.kq[t >> 6] = kq;
     } else {
@@ -501,78 +406,99 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
         sh.v[j] = In<TIn>::cvt(x0);
         sh.c[j] = __uint_as_float(x1);
         sh.ez[D + j] = 0.0f;
-        if (j < 16)
-            *reinterpret_cast<uint4 *>(&sh.coef[j >> 2][j & 3][kCoefRows - 1][0]) =
-                make_uint4(0u, 0u, 0u, 0u);
     }
     __syncthreads();
 
-    // ---- widen the codes
+    // ---- widen the codes: z[m][e] = code (or pivot value) of slot m in
+    // column 8c + e
+    ChunkLane cl;
+    cl.odd = lane_mask(c & 1);
+    cl.half = lane_mask(c & 2);
+    cl.sh = static_cast<uint32_t>(16 * (c & 1));
+    uint32_t lo4 = 0x0F0F0F0Fu;
+    asm volatile("" : "+v"(lo4));
     float z[8][8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
+        uint32_t ev = 0u, od = 0u;
         per_slot(L, tab, g, m, [&](auto KC) __attribute__((always_inline)) {
             constexpr int K = decltype(KC)::value;
-            uint32_t w[4];
-            chunk_words<K>(ld[m][0], ld[m][1], ld[m][2], ld[m][3], c, w);
-            widen<K>(w, z[m]);
+            code_words<K>(ld[m], cl, ev, od);
         });
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            z[m][2 * j] = sbyte(ev, j);
+            z[m][2 * j + 1] = sbyte(od, j);
+        }
+        // pivot rows (the first s1 rows of the head): their binary16 values
+        if (16 * m + 4 * wv < L.s1) {
+            const uint32_t pm = lane_mask(g + 16 * m < L.s1);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                z[m][e] = self(pm,
+                               static_cast<float>(__builtin_bit_cast(
+                                   _Float16, static_cast<uint16_t>(ld[m][e >> 1] >> (16 * (e & 1))))),
+                               z[m][e]);
+        }
     }
 
-    // ---- column sums on the matrix cores: per column offset e, one
-    // 16x16x32 bf16 product of the 12 coefficient rows of the wave's 32 rows
-    // with the 32 x 16 widened entries of column 8c + e (integer codes and
-    // the hi part of pivot values are exact in bf16); waves holding pivot
-    // rows add a second product with the lo parts of the pivot values
+    // ---- column sums on the matrix cores: per column offset e, two
+    // 16x16x32 bf16 products of the 12 coefficient rows of the wave's 32
+    // rows with their widened entries of column 8c + e; waves holding pivot
+    // rows add the products with the low parts of the pivot values
     const bool wave_pivots = 4 * wv < L.s1;
     {
-        const u32x4 araw =
-            *reinterpret_cast<const u32x4 *>(&sh.coef[w][gl][c < 12 ? c : 12][0]);
-        const bf16x8 A = __builtin_bit_cast(bf16x8, araw);
-        auto product = [&](int e) {
-            u32x4 braw;
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                braw[v] = __builtin_amdgcn_perm(__float_as_uint(z[2 * v + 1][e]),
-                                                __float_as_uint(z[2 * v][e]), 0x07060302u);
-            const f32x4 zero = {0.0f, 0.0f, 0.0f, 0.0f};
-            f32x4 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, braw),
-                                                               zero, 0, 0, 0);
-            if (wave_pivots) {
-                // lo = h - hi (exact, at most 3 significant bits) on pivot rows
-                float lo[8];
-#pragma unroll
-                for (int m = 0; m < 8; ++m) {
-                    lo[m] = 0.0f;
-                    if (16 * m + 4 * wv < L.s1 && g + 16 * m < L.s1) {
-                        const float x = z[m][e];
-                        lo[m] = x - __uint_as_float(__float_as_uint(x) & 0xFFFF0000u);
-                    }
-                }
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    braw[v] = __builtin_amdgcn_perm(__float_as_uint(lo[2 * v + 1]),
-                                                    __float_as_uint(lo[2 * v]), 0x07060302u);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8, braw),
-                                                             acc, 0, 0, 0);
-            }
-            return acc;
-        };
+        const uint32_t *cw = &sh.coef[4 * w + gl].w[c < kCoefRows ? c : kCoefRows - 1][0];
+        const u32x4 A[2] = {*reinterpret_cast<const u32x4 *>(cw), *reinterpret_cast<const u32x4 *>(cw + 4)};
         float4 *red = &sh.red[w][0][gl][c]; // column offset e at red[48 e]
         auto store = [&](int e, const f32x4 &acc) {
             if (gl < 3) red[48 * e] = make_float4(acc[0], acc[1], acc[2], acc[3]);
         };
-        f32x4 acc0 = product(0);
-        f32x4 acc1 = product(1);
+        // the eight products as one straight run, with or without the pivot
+        // low parts (two copies, so that the waves without pivot rows do not
+        // issue those products)
+        auto run = [&](auto PIV) __attribute__((always_inline)) {
+            constexpr bool WITH = decltype(PIV)::value;
+            auto product = [&](int e) {
+                const f32x4 zz[2] = {f32x4{z[0][e], z[1][e], z[2][e], z[3][e]},
+                                     f32x4{z[4][e], z[5][e], z[6][e], z[7][e]}};
+                f32x4 acc = column_sums(A, zz);
+                if constexpr (WITH) {
+                    // h - hi, where hi = h with its low 16 bits cleared (what
+                    // the matrix core read), in the slots holding pivot rows
+                    f32x4 lo[2];
 #pragma unroll
-        for (int e = 2; e < 8; e += 2) {
-            store(e - 2, acc0);
-            acc0 = product(e);
-            store(e - 1, acc1);
-            acc1 = product(e + 1);
+                    for (int m = 0; m < 8; ++m) {
+                        const float x = z[m][e];
+                        lo[m >> 2][m & 3] = 16 * m + 4 * wv < L.s1
+                                                ? x - __uint_as_float(__float_as_uint(x) & 0xFFFF0000u)
+                                                : 0.0f;
+                    }
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, A[0]), __builtin_bit_cast(bf16x8, lo[0]), acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, A[1]), __builtin_bit_cast(bf16x8, lo[1]), acc, 0, 0, 0);
+                }
+                return acc;
+            };
+            f32x4 acc0 = product(0);
+            f32x4 acc1 = product(1);
+#pragma unroll
+            for (int e = 2; e < 8; e += 2) {
+                store(e - 2, acc0);
+                acc0 = product(e);
+                store(e - 1, acc1);
+                acc1 = product(e + 1);
+            }
+            store(6, acc0);
+            store(7, acc1);
+        };
+        if (wave_pivots) {
+            asm volatile(""); // keeps this copy behind its branch
+            run(std::true_type{});
+        } else {
+            run(std::false_type{});
         }
-        store(6, acc0);
-        store(7, acc1);
     }
     // pivot rows enter the update as h / c
     if (wave_pivots) {
@@ -598,7 +524,6 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
     const int ce = (t >> 4) & 7;
     const int jcol = 8 * cc + ce;
     const int ezi = (ce >> 2) * 64 + cc * 4 + (ce & 3);
-    const float cinv_j = __builtin_amdgcn_rcpf(sh.c[jcol]);
     if (t < D) {
         float u = 0.0f, up = 0.0f;
 #pragma unroll
@@ -606,6 +531,7 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
             const float4 f = sh.red[ww][ce][0][cc];
             u += (f.x + f.y) + f.z;
         }
+        float vp = sh.v[jcol];
         if (head_pivots) {
 #pragma unroll
             for (int ww = 0; ww < 4; ++ww) {
@@ -613,9 +539,11 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
                 const float4 f2 = sh.red[ww][ce][2][cc];
                 up += (f1.z + f1.w) + f2.x;
             }
-            u = __builtin_fmaf(up, cinv_j, u);
+            vp = __builtin_fmaf(-alpha, up, vp); // v - a u_pivots, divided by c below
         }
-        sh.ez[ezi] = __builtin_fmaf(-alpha, u, sh.v[jcol] * cinv_j);
+        // e = (v - a u_pivots) / c - a u, the quotient to within a hair of
+        // correct rounding (see the fixed-split kernel)
+        sh.ez[ezi] = __builtin_fmaf(-alpha, u, div_refined(vp, sh.c[jcol]));
     } else {
         float wp = 0.0f;
 #pragma unroll
@@ -630,7 +558,7 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
                 const float4 f2 = sh.red[ww][ce][2][cc];
                 wp += (f2.y + f2.z) + f2.w;
             }
-            wsum = __builtin_fmaf(wp, cinv_j, wsum);
+            wsum += div_refined(wp, sh.c[jcol]);
         }
     }
     __syncthreads();
@@ -643,10 +571,11 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
 
     // ---- Table C2 steps 2 and 4: updated entries and row absmax
     uint32_t amax[8];
+    const char *ezc = reinterpret_cast<const char *>(&sh.ez[4 * c]);
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
         const float4 rp = sh.row[g + 16 * m];
-        const float *E = &sh.ez[__float_as_int(rp.w) + 4 * c];
+        const float *E = reinterpret_cast<const float *>(ezc + __float_as_int(rp.w));
         const float4 e0 = *reinterpret_cast<const float4 *>(E);
         const float4 e1 = *reinterpret_cast<const float4 *>(E + 64);
         const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
@@ -658,39 +587,16 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
         }
         amax[m] = __float_as_uint(mx);
     }
-    // reduce-scatter over the 16 lanes of the row group: lane c ends with row c / 2
-    const bool hiHalf = (c & 8) != 0;
-    const bool upper = (c & 4) != 0;
-    const bool q2 = (c & 2) != 0;
-    uint32_t r1[4], r2[2];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t keep = hiHalf ? amax[k + 4] : amax[k];
-        const uint32_t send = hiHalf ? amax[k] : amax[k + 4];
-        r1[k] = max(keep, dpp<kRowRor8>(send));
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const uint32_t keep = upper ? r1[k + 2] : r1[k];
-        const uint32_t send = upper ? r1[k] : r1[k + 2];
-        r2[k] = max(keep, dpp<kRowHalfMirror>(send));
-    }
-    float rmax;
-    {
-        const uint32_t keep = q2 ? r2[1] : r2[0];
-        const uint32_t send = q2 ? r2[0] : r2[1];
-        uint32_t v = max(keep, dpp<kQuadXor2>(send));
-        v = max(v, dpp<kQuadXor1>(v));
-        rmax = __uint_as_float(v);
-    }
+    const uint32_t mk[3] = {lane_mask(c & 8), lane_mask(c & 4), lane_mask(c & 2)};
+    const float rmax = row_max_scatter(amax, mk);
     {
         const int mm = c >> 1;
         const int p = g + 16 * mm;
         const float sc = sh.row[p].y;
-        const float qinv = sh.qinv[p];
+        const float qb = sh.qb[p];
         float rn = 0.0f, mul = 0.0f;
-        if (qinv != 0.0f) {
-            rn = fmaxf((fabsf(sc) * rmax) * qinv, kRowFloor);
+        if (qb != 0.0f) {
+            rn = fmaxf(div_refined(fabsf(sc) * rmax, qb), kRowFloor);
             mul = fminf(fmaxf(sc * __builtin_amdgcn_rcpf(rn), -kMulMax), kMulMax);
         }
         if ((c & 1) == 0) {
@@ -732,7 +638,22 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
         // one slot at a time: keeps the codes of later slots from being
-        // formed early (they would hold registers through the stores)
+        // formed early (they would hold registers through the stores).  The
+        // codes and the refit sums are formed for every row (a pivot row has
+        // multiplier 0 and weight 0, so its codes are 0 and add nothing);
+        // only the packing depends on the class
+        uint32_t bt[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bt[e] = __float_as_uint(__builtin_fmaf(z[m][e], mulv[m], kRoundMagic));
+        if (REFIT) {
+            const float ram = sh.ra[gs][m], rbm = sh.rb[gs][m];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float zq = __uint_as_float(bt[e]) - kRoundMagic; // the code, exactly
+                num[e] = __builtin_fmaf(ram * zq, z[m][e], num[e]);
+                den[e] = __builtin_fmaf(rbm * zq, zq, den[e]);
+            }
+        }
         per_slot(L, tab, gs, m, [&](auto KC) __attribute__((always_inline)) {
             constexpr int K = decltype(KC)::value;
             const int p = gs + 16 * m;
@@ -744,25 +665,15 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
                     const float4 cq = *reinterpret_cast<const float4 *>(&sh.c[8 * cs_ + 4 * hf]);
-                    const float *y = &z[m][4 * hf];
-                    const uint32_t lo = half_bits(cq.x * (sc * y[0])) | (half_bits(cq.y * (sc * y[1])) << 16);
-                    const uint32_t hi = half_bits(cq.z * (sc * y[2])) | (half_bits(cq.w * (sc * y[3])) << 16);
-                    *reinterpret_cast<uint2 *>(base + (off + 16u * cs_ + 8u * hf)) = make_uint2(lo, hi);
+                    const int e0 = 4 * hf;
+                    const uint32_t lo = half_bits(cq.x * (sc * z[m][e0])) |
+                                        (half_bits(cq.y * (sc * z[m][e0 + 1])) << 16);
+                    const uint32_t hi = half_bits(cq.z * (sc * z[m][e0 + 2])) |
+                                        (half_bits(cq.w * (sc * z[m][e0 + 3])) << 16);
+                    *reinterpret_cast<u32x2 *>(base + (off + 16u * cs_ + 8u * hf)) = u32x2{lo, hi};
                 }
             } else {
-                uint32_t bt[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) bt[e] = __float_as_uint(__builtin_fmaf(z[m][e], mulv[m], kRoundMagic));
-                if (REFIT) {
-                    const float ram = sh.ra[g][m], rbm = sh.rb[g][m];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float zq = __uint_as_float(bt[e]) - kRoundMagic; // the code, exactly
-                        num[e] = __builtin_fmaf(ram * zq, z[m][e], num[e]);
-                        den[e] = __builtin_fmaf(rbm * zq, zq, den[e]);
-                    }
-                }
-                store_codes<K>(base, off, cs_, bt);
+                store_codes<K>(base, off, cs_, bt, lo4);
             }
         });
     }
@@ -787,39 +698,30 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, int 
     }
 }
 
-unsigned div_magic(unsigned d) {
-    return d <= 1 ? 0u : static_cast<unsigned>(((1ull << 32) + d - 1) / d);
-}
-
 template <typename TIn, bool REFIT, bool GATED>
-void launch_one(const DecodeArgs &a, unsigned units, int remap, unsigned hv_m, unsigned g_m,
-                hipStream_t s) {
-    hipLaunchKernelGGL((decode_alloc128_kernel<TIn, REFIT, GATED>), dim3(units), dim3(256), 0, s, a,
-                       remap, hv_m, g_m);
+void launch_one(const DecodeArgs &a, unsigned units, const UnitGeom &ug, hipStream_t s) {
+    hipLaunchKernelGGL((decode_alloc128_kernel<TIn, REFIT, GATED>), dim3(units), dim3(256), 0, s, a, ug);
 }
 
 template <typename TIn>
-void launch_in(const DecodeArgs &a, unsigned units, int remap, unsigned hv_m, unsigned g_m,
-               hipStream_t s) {
+void launch_in(const DecodeArgs &a, unsigned units, const UnitGeom &ug, hipStream_t s) {
     const bool refit = a.cs != nullptr;
     const bool gated = a.gate != nullptr;
-    if (refit && gated) launch_one<TIn, true, true>(a, units, remap, hv_m, g_m, s);
-    else if (refit) launch_one<TIn, true, false>(a, units, remap, hv_m, g_m, s);
-    else if (gated) launch_one<TIn, false, true>(a, units, remap, hv_m, g_m, s);
-    else launch_one<TIn, false, false>(a, units, remap, hv_m, g_m, s);
+    if (refit && gated) launch_one<TIn, true, true>(a, units, ug, s);
+    else if (refit) launch_one<TIn, true, false>(a, units, ug, s);
+    else if (gated) launch_one<TIn, false, true>(a, units, ug, s);
+    else launch_one<TIn, false, false>(a, units, ug, s);
 }
 
 } // namespace
 
 hipError_t launch_decode_alloc128(bool bf16, const DecodeArgs &a, hipStream_t s) {
     const unsigned units = static_cast<unsigned>(a.B) * static_cast<unsigned>(a.Hv);
-    const int remap = (units % 8u) == 0u ? 1 : 0;
-    const unsigned hv_m = div_magic(static_cast<unsigned>(a.Hv));
-    const unsigned g_m = div_magic(static_cast<unsigned>(a.Hv / a.Hk));
+    const UnitGeom ug = unit_geom(a);
     if (bf16)
-        launch_in<uint16_t>(a, units, remap, hv_m, g_m, s);
+        launch_in<uint16_t>(a, units, ug, s);
     else
-        launch_in<float>(a, units, remap, hv_m, g_m, s);
+        launch_in<float>(a, units, ug, s);
     return hipGetLastError();
 }
 

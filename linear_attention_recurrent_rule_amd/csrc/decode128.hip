@@ -56,7 +56,13 @@ using namespace t128;
 // (hi, mid, lo), r q (hi, mid, lo).  Lanes of the other output rows read one
 // of these rows too; their products are not used.
 struct Smem {
-    uint32_t coef[4][4][6][8];
+    // per lane group G = 4 w + gl (wave w): six rows of 8 words, padded by 16
+    // bytes so that the staging lanes, which write one word each into 16
+    // groups, spread over all 64 banks
+    struct {
+        uint32_t w[6][8];
+        uint32_t pad[4];
+    } coef[16];
     float4 row[D];          // {P, s, w2, byte offset of E in ez} per physical row
     float v[D], c[D];
     float ez[2 * D];        // e, then a zero vector; each as [e/4][c][e%4]
@@ -211,7 +217,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
     }
     {
         // output row c of the product: lanes c >= 6 read row 5 (unused)
-        const uint32_t *cw = &sh.coef[w][gl][c < 6 ? c : 5][0];
+        const uint32_t *cw = &sh.coef[4 * w + gl].w[c < 6 ? c : 5][0];
         const u32x4 A[2] = {*reinterpret_cast<const u32x4 *>(cw), *reinterpret_cast<const u32x4 *>(cw + 4)};
         // lanes of group 0 receive (u hi, u mid, u lo, w hi), group 1 (w mid,
         // w lo); two accumulators alternate so a result is stored while the
@@ -331,14 +337,12 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
     // column refit partial sums over this lane's 8 rows (REFIT): with
     // x = s y, X = c x and v = r' z', sum_i w2 v X = c sum_i (w2 r' s) z' y
     // and sum_i w2 v^2 = sum_i (w2 r'^2) z'^2
-    float num[8], den[8], rav[8], rbv[8];
+    float num[8], den[8];
     if (REFIT) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             num[e] = 0.0f;
             den[e] = 0.0f;
-            rav[e] = sh.ra[g][e];
-            rbv[e] = sh.rb[g][e];
         }
     }
     uint32_t lo4 = 0x0F0F0F0Fu;
@@ -355,11 +359,14 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
         for (int e = 0; e < 8; ++e)
             bt[e] = __float_as_uint(__builtin_fmaf(zb[hh][e][s], mulv[m], kRoundMagic));
         if (REFIT) {
+            // the row's refit factors from LDS slot by slot (holding all eight
+            // in registers would cost the kernel a wave of occupancy)
+            const float ram = sh.ra[g][m], rbm = sh.rb[g][m];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float zq = __uint_as_float(bt[e]) - kRoundMagic; // the code, exactly
-                num[e] = __builtin_fmaf(rav[m] * zq, zb[hh][e][s], num[e]);
-                den[e] = __builtin_fmaf(rbv[m] * zq, zq, den[e]);
+                num[e] = __builtin_fmaf(ram * zq, zb[hh][e][s], num[e]);
+                den[e] = __builtin_fmaf(rbm * zq, zq, den[e]);
             }
         }
         if constexpr (IS8) {
@@ -499,7 +506,7 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, UnitGeom u
         if (GATED) scale *= __uint_as_float(pick(g0, g1));
         {
             // row p = 4 w + gl + 16 m of wave w, lane group gl, slot m
-            uint32_t(&cf)[6][8] = sh.coef[(p & 15) >> 2][p & 3];
+            uint32_t(&cf)[6][8] = sh.coef[p & 15].w;
             const int mm = p >> 4;
             uint32_t h0, h1, h2;
             split3w(scale * kp, h0, h1, h2);
