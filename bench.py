@@ -93,8 +93,15 @@ def parse():
                         "per kernel, and the average over each kernel's last --timed-launches "
                         "dispatches) and exit")
     p.add_argument("--timed-launches", type=int, default=None,
-                   help="with --trace-summary: dispatches at the end of the trace that were "
-                        "timed (default: --blocks x --steps)")
+                   help="with --trace-summary: dispatches of each kernel that were timed "
+                        "(default: --blocks x --steps)")
+    p.add_argument("--pmc-summary", default=None, metavar="COUNTER_COLLECTION_CSV",
+                   help="no GPU work: average each counter of a rocprofv3 --pmc CSV per "
+                        "dispatch, per kernel, and exit")
+    p.add_argument("--skip", type=int, default=None,
+                   help="with --trace-summary: average the timed launches over dispatches "
+                        "skip .. skip + timed - 1 of each kernel (the line's warmup_launches for "
+                        "the main measurement) instead of its last ones")
     p.add_argument("--with-copy", action="store_true",
                    help="also run the 1 GiB reference copy (with --only-decode)")
     p.add_argument("--drift", action="store_true",
@@ -278,9 +285,10 @@ def cpu_baseline(np, wl, w, B, hv, d) -> dict:
     return cpu
 
 
-def trace_summary(path: str, timed: int) -> str:
+def trace_summary(path: str, timed: int, skip: int | None = None) -> str:
     """Per-kernel calls / avg / min / max (us) of a rocprofv3 kernel-trace CSV,
-    and each kernel's average over its last `timed` dispatches."""
+    and each kernel's average over `timed` of its dispatches: the last ones,
+    or those after the first `skip`."""
     import csv
 
     durs: dict[str, list[float]] = {}
@@ -299,19 +307,53 @@ def trace_summary(path: str, timed: int) -> str:
         name = short(r_["Kernel_Name"])
         durs.setdefault(name, []).append(
             (int(r_["End_Timestamp"]) - int(r_["Start_Timestamp"])) / 1e3)
-    out = [f"{'kernel':<58} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} "
-           f"{'last_' + str(timed) + '_avg_us':>16}"]
+    label = f"last_{timed}_avg_us" if skip is None else f"{skip}+{timed}_avg_us"
+    out = [f"{'kernel':<58} {'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {label:>16}"]
     for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
-        tail = v[-timed:] if len(v) >= timed else v
+        if skip is None:
+            tail = v[-timed:] if len(v) >= timed else v
+        else:
+            tail = v[skip:skip + timed] or v
         out.append(f"{name[:58]:<58} {len(v):>6} {sum(v) / len(v):>9.1f} {min(v):>9.1f} "
                    f"{max(v):>9.1f} {sum(tail) / len(tail):>16.1f}")
     return "\n".join(out)
 
 
+def pmc_summary(path: str) -> str:
+    """Per kernel: dispatches and the average of each counter per dispatch
+    (summed over the per-agent/per-block rows of a dispatch) of a rocprofv3
+    --pmc counter-collection CSV."""
+    import csv
+    from collections import defaultdict
+
+    per = defaultdict(float)
+    kern = {}
+    with open(path, newline="") as f:
+        for r_ in csv.DictReader(f):
+            key = (r_["Dispatch_Id"], r_["Counter_Name"])
+            per[key] += float(r_["Counter_Value"])
+            kern[r_["Dispatch_Id"]] = r_["Kernel_Name"]
+    by = defaultdict(lambda: defaultdict(list))
+    for (disp, ctr), v in per.items():
+        name = kern[disp].replace("(anonymous namespace)::", "").replace("void ", "")
+        by[name.split("(")[0] if "<" not in name else name[:name.index(">") + 1]][ctr].append(v)
+    out = []
+    for name, ctrs in sorted(by.items()):
+        n = max(len(v) for v in ctrs.values())
+        out.append(f"{name}  ({n} dispatches)")
+        for ctr, v in sorted(ctrs.items()):
+            out.append(f"    {ctr:28s} {sum(v) / len(v):20.1f}")
+    return "\n".join(out)
+
+
 def main():
     args = parse()
+    if args.pmc_summary:
+        print(pmc_summary(args.pmc_summary))
+        return
     if args.trace_summary:
-        print(trace_summary(args.trace_summary, args.timed_launches or args.blocks * args.steps))
+        print(trace_summary(args.trace_summary, args.timed_launches or args.blocks * args.steps,
+                            args.skip))
         return
     if args.gpus != 1:
         log("bench.py measures one GPU only: the decode step has no exchange between units, "

@@ -95,22 +95,64 @@ def _compare(gpu_pool, gpu_r, ref_pool, ref_r, counts, d, label, *, o=None, ref_
     return stats
 
 
-def pivot_allowance(pool, counts, perm, X, d, *, alpha=None, gate=None):
-    """Per pivot value [B][Hv][d][d] (physical rows): the fp32 evaluation error
-    of its two terms, 2^-20 (|d_i h_ij| + |X_ij - d_i h_ij|), with h the
-    binary16 values of the input pool, d_i the gate (alpha for the scalar
-    gate) and X the oracle's double state (logical rows).  Where the gated old
-    value and the delta write nearly cancel, the GPU's fp32 result carries an
-    error of a few ulps of the terms, which can exceed half a binary16 ulp of
-    the small result."""
-    _, h_old, _ = wl.unpack_ragged(pool, counts, d)
-    Xp = np.take_along_axis(X, perm[None, :, :, None], axis=2)  # physical rows
+U = 2.0 ** -24  # fp32 unit roundoff
+# fp32 roundings that the column sums u~ (and so e) may carry, relative to the
+# sum of the magnitudes of their terms: up to 32 in the matrix-core products
+# of a wave (16 products of a row group into the accumulator per product,
+# two chained products), 2 joining the three coefficient parts, 4 joining the
+# waves, 2 adding the pivot rows; the d < 128 kernel's chain (8 per-lane
+# FMAs, at most 16 row-group partials) is shorter
+SUM_ROUNDINGS = 40
+
+
+def pivot_allowance(pool, r, counts, perm, c, k, v, beta, X, d, *, alpha=None, gate=None):
+    """Per pivot value [B][Hv][d][d] (physical rows): a bound on the distance
+    between the kernel's fp32 value of X_ij and the exact one, from its
+    rounding chain.  With T1 = g_i h_ij (the gated old value, g the gate:
+    alpha or the row gate d_i) and T2 = X_ij - T1 (the delta write):
+      * the d = 128 kernel forms z = h fl(rcp(c)) (rcp within 1 ulp = 2u,
+        the product u), y = fl(P z + e) with P = ar / bk refined to within
+        1.5u, ar = fl(a g) (u when a row gate multiplies), bk = fl(b k), and
+        X = fl(c fl(bk y)): the old value carries the roundings of rcp,
+        z, ar, P, y, bk y and c (.), at most 7.5u |T1|; the delta write those
+        of bk, y, bk y and c (.), 4u |T2|;
+      * the d < 128 kernel forms x = fl(ar z + fl(bk e)), X = fl(c x): 6u |T1|
+        and 4u |T2|, within the same bound;
+      * e itself: e = (v - a u_pivots) / c - a u, the quotient within 1.5u of
+        |v / c|, the final FMA u |e|, and the column sums within
+        SUM_ROUNDINGS u of the sum of the magnitudes of their terms
+        (g_i r_i k_i z_ij for integer rows, g_i k_i h_ij / c_j for pivots),
+        scaled by a; it enters X through c bk.
+    The oracle's binary16 value of the exact X and the kernel's of its fp32
+    value then differ by at most one binary16 ulp plus this bound."""
+    codes, hbits, cls = wl.unpack_ragged(pool, counts, d)
+    B, hv = r.shape[:2]
+    G = hv // k.shape[1]
+    kh = k.astype(np.float64)[:, np.arange(hv) // G, :]            # [B][Hv][d] logical
+    kp = np.take_along_axis(kh, np.broadcast_to(perm[None], kh.shape), axis=2)  # physical
     if gate is not None:
-        dp = np.take_along_axis(gate.astype(np.float64), perm[None], axis=2)[..., None]
+        gp = np.take_along_axis(gate.astype(np.float64), np.broadcast_to(perm[None], kh.shape), axis=2)
+        a = np.ones((B, hv))
     else:
-        dp = alpha.astype(np.float64)[:, :, None, None]
-    t1 = dp * h_old.view(np.float16).astype(np.float64)
-    return 2.0 ** -20 * (np.abs(t1) + np.abs(Xp - t1))
+        gp = np.ones_like(kp)
+        a = alpha.astype(np.float64)
+    piv = (cls == 0)[None, :, :, None]                               # [1][Hv][d][1]
+    h = hbits.view(np.float16).astype(np.float64)
+    cc = c.astype(np.float64)[None, :, None, :]                      # [1][Hv][1][d]
+    rr = r.astype(np.float64)[..., None]
+    coef = np.where(piv, gp[..., None] * kp[..., None] / cc, gp[..., None] * rr * kp[..., None])
+    val = np.where(piv, h, codes.astype(np.float64))
+    terms = coef * val                                              # [B][Hv][d][d]
+    u_sum = terms.sum(axis=2)                                       # [B][Hv][d] per column
+    u_abs = np.abs(terms).sum(axis=2)
+    vc = v.astype(np.float64) / c.astype(np.float64)[None]
+    e = vc - a[..., None] * u_sum
+    de = U * (1.5 * np.abs(vc) + np.abs(e) + SUM_ROUNDINGS * a[..., None] * u_abs)
+    Xp = np.take_along_axis(X, perm[None, :, :, None], axis=2)        # physical rows
+    t1 = a[..., None, None] * gp[..., None] * h
+    t2 = Xp - t1
+    cbk = np.abs(cc * beta.astype(np.float64)[..., None, None] * kp[..., None])
+    return U * (7.5 * np.abs(t1) + 4.0 * np.abs(t2)) + cbk * de[:, :, None, :]
 
 
 @pytest.mark.parametrize("d", [16, 32, 64, 128])

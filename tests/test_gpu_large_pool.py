@@ -74,7 +74,8 @@ def test_ragged_top_slots_of_a_large_pool(oracle_mod):
                                 nthreads=16, want_X=True)
     print(_compare(gp, gr, ref["pool"], ref["r"], counts, D, "ragged top slots",
                    o=o.cpu().numpy(), ref_o=ref["o"],
-                   pivot_err=pivot_allowance(pool, counts, perm, ref["X"], D, alpha=x.alpha)))
+                   pivot_err=pivot_allowance(pool, r, counts, perm, c, x.k, x.v, x.beta, ref["X"], D,
+                                             alpha=x.alpha)))
     assert not st.pool[N_SLOTS - B - 1].any().item()
     del st
     torch.cuda.empty_cache()
