@@ -227,20 +227,26 @@ __device__ __forceinline__ uint32_t half_bits(float x) {
 }
 
 // Matrix-core operand A: per wave and lane group, 12 rows of 8 words (one
-// per slot), each a bf16 part in its high half: 0..2 r k (hi, mid, lo) and
-// 3..5 r q of integer rows; 6..8 d k and 9..11 d q of pivot rows (d the row
-// gate, 1 for the scalar gate).  A row's words of the other kind are zero.
+// per slot), each a bf16 part in its high half, in the order of the
+// product's output rows: 0..2 r k (hi, mid, lo) of integer rows, 3..5 d k of
+// pivot rows, 6..7 d q (hi, mid) of pivot rows, 8..10 r q of integer rows,
+// 11 d q (lo) of pivot rows (d the row gate, 1 for the scalar gate).  A
+// row's words of the other kind are zero.  The product's lane groups 0, 1
+// and 2 then hold (u hi, mid, lo, pivot u hi), (pivot u mid, lo, pivot w hi,
+// mid) and (w hi, mid, lo, pivot w lo): each reader takes whole 16-byte
+// entries.
 constexpr int kCoefRows = 12;
+// Words of lane group G: slot m of row r at 24 (m / 2) + 2 r + m % 2 (slot
+// pairs 8-byte aligned for ds_read2_b64), groups 98 words apart, so that
+// the staging lanes (16 groups, two slots per half wave) and the operand
+// reads (two groups per 32 lanes) both spread over all banks.
+constexpr int kCoefStride = 98;
 struct Smem {
-    // per lane group G = 4 w + gl (wave w), padded by 16 bytes so that the
-    // staging lanes, which write one word each into 16 groups, spread over
-    // all 64 banks
-    struct {
-        uint32_t w[kCoefRows][8];
-        uint32_t pad[4];
-    } coef[16];
-    float4 row[D];          // {P, s, w2, byte offset of E in ez} per physical row
-    float qb[D];            // q_b per physical row, 0 for pivot rows
+    uint32_t coef[16 * kCoefStride];
+    float2 row[D];          // {P, byte offset of E in ez} per physical row
+    float srow[D];          // s per row, at srow_index(g, m)
+    float qbrow[D];         // q_b per row, 0 for pivot rows, at srow_index(g, m)
+    float w2row[D];         // column refit: w2 per row, at srow_index(g, m)
     float v[D], c[D];
     float ez[2 * D];        // e, then a zero vector; each as [e/4][c][e%4]
     float4 red[4][8][3][16]; // per wave, column offset e, lane group, chunk c
@@ -372,30 +378,33 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, Unit
         float scale = self(piv, 1.0f, rpv * winv);
         if (GATED) scale *= __uint_as_float(pick(g0, g1));
         {
-            uint32_t(&cf)[kCoefRows][8] = sh.coef[p & 15].w;
             const int mm = p >> 4;
+            uint32_t *cf = &sh.coef[(p & 15) * kCoefStride + 24 * (mm >> 1) + (mm & 1)]; // row r at 2 r
             uint32_t wk[3], wq[3];
             split3w(scale * kp, wk[0], wk[1], wk[2]);
             split3w(scale * qp, wq[0], wq[1], wq[2]);
             // this row's coefficient words in its kind's rows, zero in the other's
+            constexpr int kInt[2][3] = {{0, 1, 2}, {8, 9, 10}};
+            constexpr int kPiv[2][3] = {{3, 4, 5}, {6, 7, 11}};
 #pragma unroll
             for (int q = 0; q < 3; ++q) {
-                cf[q][mm] = sel(piv, 0u, wk[q]);
-                cf[3 + q][mm] = sel(piv, 0u, wq[q]);
-                cf[6 + q][mm] = sel(piv, wk[q], 0u);
-                cf[9 + q][mm] = sel(piv, wq[q], 0u);
+                cf[2 * kInt[0][q]] = sel(piv, 0u, wk[q]);
+                cf[2 * kInt[1][q]] = sel(piv, 0u, wq[q]);
+                cf[2 * kPiv[0][q]] = sel(piv, wk[q], 0u);
+                cf[2 * kPiv[1][q]] = sel(piv, wq[q], 0u);
             }
         }
         const float ar = alpha * scale;
         const float bk = beta * kp;
         // |b k| > 2^-64 |a r| (false when both vanish: then x = 0 * z = 0)
         const uint32_t scaled = lane_mask(fabsf(bk) > fabsf(ar) * kFormTiny);
-        const float w2 = REFIT ? __uint_as_float(sel(piv, 0u, pick(u0, u1))) : 0.0f;
-        sh.row[p] = make_float4(self(scaled, div_refined(ar, bk), ar), self(scaled, bk, 1.0f), w2,
-                                __uint_as_float(sel(scaled, 0u, 4u * D)));
+        sh.row[p] = make_float2(self(scaled, div_refined(ar, bk), ar), __uint_as_float(sel(scaled, 0u, 4u * D)));
+        const int si = srow_index(p & 15, p >> 4);
+        sh.srow[si] = self(scaled, bk, 1.0f);
+        if (REFIT) sh.w2row[si] = __uint_as_float(sel(piv, 0u, pick(u0, u1)));
         // q_b = 2^(b-1) - 1 for b = 8, 6, 4, 2; 0 marks a pivot row
         const float qbk = static_cast<float>((1 << (9 - 2 * k)) - 1);
-        sh.qb[p] = self(piv, 0.0f, qbk);
+        sh.qbrow[si] = self(piv, 0.0f, qbk);
         const float kq = wave_sum(kp * qp);
         if ((t & 63) == 0) sh.kq[t >> 6] = kq;
     } else {
@@ -448,8 +457,10 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, Unit
     // rows add the products with the low parts of the pivot values
     const bool wave_pivots = 4 * wv < L.s1;
     {
-        const uint32_t *cw = &sh.coef[4 * w + gl].w[c < kCoefRows ? c : kCoefRows - 1][0];
-        const u32x4 A[2] = {*reinterpret_cast<const u32x4 *>(cw), *reinterpret_cast<const u32x4 *>(cw + 4)};
+        const int crow = c < kCoefRows ? c : kCoefRows - 1;
+        const u32x2 *cw = reinterpret_cast<const u32x2 *>(&sh.coef[(4 * w + gl) * kCoefStride + 2 * crow]);
+        const u32x2 a0 = cw[0], a1 = cw[12], a2 = cw[24], a3 = cw[36]; // slot pairs
+        const u32x4 A[2] = {u32x4{a0[0], a0[1], a1[0], a1[1]}, u32x4{a2[0], a2[1], a3[0], a3[1]}};
         float4 *red = &sh.red[w][0][gl][c]; // column offset e at red[48 e]
         auto store = [&](int e, const f32x4 &acc) {
             if (gl < 3) red[48 * e] = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -504,7 +515,13 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, Unit
     if (wave_pivots) {
         float cinv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cinv[e] = __builtin_amdgcn_rcpf(sh.c[8 * c + e]);
+        for (int h4 = 0; h4 < 2; ++h4) {
+            const float4 cq = *reinterpret_cast<const float4 *>(&sh.c[8 * c + 4 * h4]);
+            cinv[4 * h4] = __builtin_amdgcn_rcpf(cq.x);
+            cinv[4 * h4 + 1] = __builtin_amdgcn_rcpf(cq.y);
+            cinv[4 * h4 + 2] = __builtin_amdgcn_rcpf(cq.z);
+            cinv[4 * h4 + 3] = __builtin_amdgcn_rcpf(cq.w);
+        }
 #pragma unroll
         for (int m = 0; m < 8; ++m)
             if (16 * m + 4 * wv < L.s1 && g + 16 * m < L.s1) {
@@ -515,29 +532,40 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, Unit
     __syncthreads();
 
     // ---- column sums over the 4 waves: u~ (lanes 0..127) -> e; w~ (128..255)
-    // kept for o.  Lane t handles column 8 (t % 16) + (t / 16) % 8.  Output
-    // rows per lane group: 0: u hi, mid, lo, w hi; 1: w mid, lo, pivot u hi,
-    // mid; 2: pivot u lo, pivot w hi, mid, lo.
+    // kept for o.  Lane t takes column 8 cc + ce, cc = t % 16, with ce =
+    // (t / 16) % 8 rotated by 2 (cc / 4): the 16 lanes of a row group still
+    // read 16 different chunks of the sums, and the 32 lanes of a half wave
+    // read v and c from 32 different banks.  Output rows per lane group: 0: u hi, mid,
+    // lo, pivot u hi; 1: pivot u mid, lo, pivot w hi, mid; 2: w hi, mid, lo,
+    // pivot w lo.  Each entry is read whole (16 bytes, or the first 12):
+    // narrower reads of 16-byte entries collide in the LDS banks.
     const bool head_pivots = L.s1 > 0;
-    float wsum = 0.0f;
+    float wsum;
     const int cc = t & 15;
-    const int ce = (t >> 4) & 7;
+    const int ce = ((t >> 4) + ((t >> 1) & 6)) & 7;
     const int jcol = 8 * cc + ce;
     const int ezi = (ce >> 2) * 64 + cc * 4 + (ce & 3);
+    auto whole = [](const float4 &f) __attribute__((always_inline)) {
+        asm volatile("" ::"v"(f.x), "v"(f.y), "v"(f.z), "v"(f.w));
+    };
     if (t < D) {
-        float u = 0.0f, up = 0.0f;
+        const float4 u0 = sh.red[0][ce][0][cc];
+        float u = (u0.x + u0.y) + u0.z;
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
+        for (int ww = 1; ww < 4; ++ww) {
             const float4 f = sh.red[ww][ce][0][cc];
             u += (f.x + f.y) + f.z;
         }
         float vp = sh.v[jcol];
         if (head_pivots) {
+            float up = 0.0f;
 #pragma unroll
             for (int ww = 0; ww < 4; ++ww) {
+                const float4 f0 = sh.red[ww][ce][0][cc];
                 const float4 f1 = sh.red[ww][ce][1][cc];
-                const float4 f2 = sh.red[ww][ce][2][cc];
-                up += (f1.z + f1.w) + f2.x;
+                whole(f0);
+                whole(f1);
+                up += (f0.w + f1.x) + f1.y;
             }
             vp = __builtin_fmaf(-alpha, up, vp); // v - a u_pivots, divided by c below
         }
@@ -545,18 +573,22 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, Unit
         // correct rounding (see the fixed-split kernel)
         sh.ez[ezi] = __builtin_fmaf(-alpha, u, div_refined(vp, sh.c[jcol]));
     } else {
-        float wp = 0.0f;
+        const float4 w0 = sh.red[0][ce][2][cc];
+        wsum = (w0.x + w0.y) + w0.z;
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
-            const float4 f0 = sh.red[ww][ce][0][cc];
-            const float4 f1 = sh.red[ww][ce][1][cc];
-            wsum += (f0.w + f1.x) + f1.y;
+        for (int ww = 1; ww < 4; ++ww) {
+            const float4 f2 = sh.red[ww][ce][2][cc];
+            wsum += (f2.x + f2.y) + f2.z;
         }
         if (head_pivots) {
+            float wp = 0.0f;
 #pragma unroll
             for (int ww = 0; ww < 4; ++ww) {
+                const float4 f1 = sh.red[ww][ce][1][cc];
                 const float4 f2 = sh.red[ww][ce][2][cc];
-                wp += (f2.y + f2.z) + f2.w;
+                whole(f1);
+                whole(f2);
+                wp += (f1.z + f1.w) + f2.w;
             }
             wsum += div_refined(wp, sh.c[jcol]);
         }
@@ -574,8 +606,8 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, Unit
     const char *ezc = reinterpret_cast<const char *>(&sh.ez[4 * c]);
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-        const float4 rp = sh.row[g + 16 * m];
-        const float *E = reinterpret_cast<const float *>(ezc + __float_as_int(rp.w));
+        const float2 rp = sh.row[g + 16 * m];
+        const float *E = reinterpret_cast<const float *>(ezc + __float_as_int(rp.y));
         const float4 e0 = *reinterpret_cast<const float4 *>(E);
         const float4 e1 = *reinterpret_cast<const float4 *>(E + 64);
         const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
@@ -592,8 +624,9 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, Unit
     {
         const int mm = c >> 1;
         const int p = g + 16 * mm;
-        const float sc = sh.row[p].y;
-        const float qb = sh.qb[p];
+        const int si = srow_index(g, mm);
+        const float sc = sh.srow[si];
+        const float qb = sh.qbrow[si];
         float rn = 0.0f, mul = 0.0f;
         if (qb != 0.0f) {
             rn = fmaxf(div_refined(fabsf(sc) * rmax, qb), kRowFloor);
@@ -603,7 +636,7 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, Unit
             rw[p] = rn;
             sh.mul[g][mm] = mul;
             if (REFIT) {
-                const float w2 = sh.row[p].z; // 0 on pivot rows
+                const float w2 = sh.w2row[si]; // 0 on pivot rows
                 sh.ra[g][mm] = (w2 * rn) * sc;
                 sh.rb[g][mm] = (w2 * rn) * rn;
             }
@@ -661,7 +694,8 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, Unit
             const unsigned off = static_cast<unsigned>(gs * Cls<K>::row);
             if constexpr (K == 0) {
                 // X = c_j s y, stored in binary16, four columns at a time
-                const float sc = sh.row[p].y;
+                (void)p;
+                const float sc = sh.srow[srow_index(gs, m)];
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
                     const float4 cq = *reinterpret_cast<const float4 *>(&sh.c[8 * cs_ + 4 * hf]);
@@ -678,17 +712,22 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, Unit
         });
     }
     if (REFIT) {
-        // ---- Table C2 step 5: the column factors refit over the integer rows
-        float2 *red2 = reinterpret_cast<float2 *>(&sh.red[0][0][0][0]); // [4][4][16][8]
-        float4 *mine = reinterpret_cast<float4 *>(red2 + ((w * 4 + gl) * 16 + c) * 8);
+        // ---- Table C2 step 5: the column factors refit over the integer rows.
+        // Partials per (wave and lane group q, column-offset pair e / 2,
+        // chunk c), written 16 bytes and read 8 bytes per lane without bank
+        // conflicts
+        float4 *red4 = &sh.red[0][0][0][0]; // [16 q][4 e/2][16 c]
+        const int q0 = w * 4 + gl;
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) mine[e / 2] = make_float4(num[e], den[e], num[e + 1], den[e + 1]);
+        for (int e = 0; e < 8; e += 2)
+            red4[(q0 * 4 + e / 2) * 16 + c] = make_float4(num[e], den[e], num[e + 1], den[e + 1]);
         __syncthreads();
         if (t < D) {
+            const float2 *red2 = reinterpret_cast<const float2 *>(red4);
             float nsum = 0.0f, dsum = 0.0f;
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                const float2 f = red2[(q * 16 + cc) * 8 + ce];
+                const float2 f = red2[((q * 4 + (ce >> 1)) * 16 + cc) * 2 + (ce & 1)];
                 nsum += f.x;
                 dsum += f.y;
             }

@@ -53,17 +53,22 @@ using namespace t128;
 
 // Matrix-core operand A for the column sums: per wave and lane group, six
 // rows of 8 words (one per slot), each a bf16 part in its high half: r k
-// (hi, mid, lo), r q (hi, mid, lo).  Lanes of the other output rows read one
-// of these rows too; their products are not used.
+// (hi, mid, lo), r q (hi, mid, lo).  The r k parts are output rows 0-2 of
+// the product and the r q parts rows 4-6, so each lane group of the result
+// holds one sum's three parts; lanes of the other output rows read one of
+// these rows too and their products are not used.
+// Every array below is laid out for the LDS banks (tile128.h) as seen by
+// the lanes that write it and the lanes that read it.
+constexpr int kCoefStride = 52; // words per lane group (6 x 8 used)
 struct Smem {
-    // per lane group G = 4 w + gl (wave w): six rows of 8 words, padded by 16
-    // bytes so that the staging lanes, which write one word each into 16
-    // groups, spread over all 64 banks
-    struct {
-        uint32_t w[6][8];
-        uint32_t pad[4];
-    } coef[16];
-    float4 row[D];          // {P, s, w2, byte offset of E in ez} per physical row
+    // coefficient words, group G = 4 w + gl at G * kCoefStride, row r at 8 r,
+    // slot m at m: the operand reads (16 bytes per lane) are free of
+    // conflicts; the staging writes (16 groups, two slots per half wave)
+    // meet two to a bank, which no 16-byte aligned stride avoids
+    uint32_t coef[16 * kCoefStride];
+    float2 row[D];          // {P, byte offset of E in ez} per physical row
+    float srow[D + 8];      // s of row p at p + p / 16
+    float w2row[D + 8];     // column refit: w2 of row p at p + p / 16
     float v[D], c[D];
     float ez[2 * D];        // e, then a zero vector; each as [e/4][c][e%4]
     float4 red[4][8][2][16]; // per wave, column offset e, lane group, chunk c
@@ -216,12 +221,14 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
         }
     }
     {
-        // output row c of the product: lanes c >= 6 read row 5 (unused)
-        const uint32_t *cw = &sh.coef[4 * w + gl].w[c < 6 ? c : 5][0];
-        const u32x4 A[2] = {*reinterpret_cast<const u32x4 *>(cw), *reinterpret_cast<const u32x4 *>(cw + 4)};
-        // lanes of group 0 receive (u hi, u mid, u lo, w hi), group 1 (w mid,
-        // w lo); two accumulators alternate so a result is stored while the
-        // next product is in flight
+        // output row c of the product: rows 0-2 the r k parts, 3 and 4 the
+        // r q high part, 5 and 6 its other parts, 7-15 the last one (unused)
+        const int crow = c < 4 ? c : (c < 7 ? c - 1 : 5);
+        const u32x4 *cw = reinterpret_cast<const u32x4 *>(&sh.coef[(4 * w + gl) * kCoefStride + 8 * crow]);
+        const u32x4 A[2] = {cw[0], cw[1]};
+        // lanes of group 0 receive (u hi, u mid, u lo, -), group 1 (w hi,
+        // w mid, w lo, -); two accumulators alternate so a result is stored
+        // while the next product is in flight
         auto product = [&](int e) {
             const f32x4 zz[2] = {zb[0][e], zb[1][e]};
             return column_sums(A, zz);
@@ -245,16 +252,21 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
     __syncthreads();
 
     // ---- column sums over the 4 waves: u~ (lanes 0..127) -> e; w~ (128..255)
-    // kept for o.  Lane t handles column 8 (t % 16) + (t / 16) % 8.
-    float wsum = 0.0f;
+    // kept for o.  Lane t takes column 8 cc + ce, cc = t % 16, with ce =
+    // (t / 16) % 8 rotated by 2 (cc / 4): the 16 lanes of a row group still
+    // read 16 different chunks of the sums, and the 32 lanes of a half wave
+    // read v and c from 32 different banks
     const int cc = t & 15;
-    const int ce = (t >> 4) & 7;
+    const int ce = ((t >> 4) + ((t >> 1) & 6)) & 7;
     const int jcol = 8 * cc + ce;
     const int ezi = (ce >> 2) * 64 + cc * 4 + (ce & 3);
+    // the three parts of the column's sum in each wave, then the four waves
+    float wsum = 0.0f;
     if (t < D) {
-        float u = 0.0f;
+        const float4 f0 = sh.red[0][ce][0][cc];
+        float u = (f0.x + f0.y) + f0.z;
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
+        for (int ww = 1; ww < 4; ++ww) {
             const float4 f = sh.red[ww][ce][0][cc];
             u += (f.x + f.y) + f.z;
         }
@@ -262,11 +274,12 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
         // cancels its decayed content amplifies any rounding of e
         sh.ez[ezi] = __builtin_fmaf(-L.alpha, u, div_refined(sh.v[jcol], sh.c[jcol]));
     } else {
+        const float4 f0 = sh.red[0][ce][1][cc];
+        wsum = (f0.x + f0.y) + f0.z;
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
-            const float4 f0 = sh.red[ww][ce][0][cc];
-            const float4 f1 = sh.red[ww][ce][1][cc];
-            wsum += (f0.w + f1.x) + f1.y;
+        for (int ww = 1; ww < 4; ++ww) {
+            const float4 f = sh.red[ww][ce][1][cc];
+            wsum += (f.x + f.y) + f.z;
         }
     }
     __syncthreads();
@@ -283,8 +296,8 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
         const int hh = m >> 2, s = m & 3;
-        const float4 rp = sh.row[g + 16 * m];
-        const float *E = reinterpret_cast<const float *>(ezc + __float_as_int(rp.w));
+        const float2 rp = sh.row[g + 16 * m];
+        const float *E = reinterpret_cast<const float *>(ezc + __float_as_int(rp.y));
         const float4 e0 = *reinterpret_cast<const float4 *>(E);
         const float4 e1 = *reinterpret_cast<const float4 *>(E + 64);
         const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
@@ -301,7 +314,8 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
     {
         const int mm = c >> 1;
         const int p = g + 16 * mm;
-        const float sc = sh.row[p].y;
+        const int si = p + mm;
+        const float sc = sh.srow[si];
         const float mrow = fabsf(sc) * rmax;
         const bool row8 = N8 == kRuntimeN8 ? p < L.n8 : mm < M8;
         const uint32_t m8 = lane_mask(row8);
@@ -314,7 +328,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
             L.rw[p] = rn;
             sh.mul[g][mm] = mul;
             if (REFIT) {
-                const float w2 = sh.row[p].z;
+                const float w2 = sh.w2row[si];
                 sh.ra[g][mm] = (w2 * rn) * sc;
                 sh.rb[g][mm] = (w2 * rn) * rn;
             }
@@ -350,10 +364,19 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
     // codes, refit sums and the packed store of slot m; in the runtime
     // instance the whole body sits inside the width branch (keeps the codes
     // of one slot live at a time)
+    // In the run-time split instance the lane's coordinates are formed
+    // afresh here (an opaque copy), so that the compiler does not hold the
+    // row addresses of the loads through the whole kernel: that instance
+    // needs the registers.  The fixed-split instances reuse them.
+    int gs = g, cs = c;
+    if constexpr (N8 == kRuntimeN8) asm volatile("" : "+v"(gs), "+v"(cs));
+    // this lane's first byte in row g of each pool (slot m adds a
+    // compile-time offset in the fixed-split instances)
+    int8_t *const q8l = L.q8 + (static_cast<unsigned>(gs) * D + 8u * cs);
+    uint8_t *const q4l = L.q4 + (static_cast<unsigned>(gs) * (D / 2) + 4u * cs);
     auto emit = [&](int m, auto W8) __attribute__((always_inline)) {
         constexpr bool IS8 = decltype(W8)::value;
         const int hh = m >> 2, s = m & 3;
-        const unsigned p = static_cast<unsigned>(g + 16 * m);
         uint32_t bt[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -361,7 +384,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
         if (REFIT) {
             // the row's refit factors from LDS slot by slot (holding all eight
             // in registers would cost the kernel a wave of occupancy)
-            const float ram = sh.ra[g][m], rbm = sh.rb[g][m];
+            const float ram = sh.ra[gs][m], rbm = sh.rb[gs][m];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float zq = __uint_as_float(bt[e]) - kRoundMagic; // the code, exactly
@@ -370,11 +393,10 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
             }
         }
         if constexpr (IS8) {
-            __builtin_nontemporal_store(pack_bytes(bt), reinterpret_cast<u32x2 *>(L.q8 + (p * D + 8 * c)));
+            __builtin_nontemporal_store(pack_bytes(bt), reinterpret_cast<u32x2 *>(q8l + 16 * m * D));
         } else {
-            __builtin_nontemporal_store(
-                pack_nibbles(bt, lo4),
-                reinterpret_cast<uint32_t *>(L.q4 + ((static_cast<int>(p) - L.n8) * (D / 2) + 4 * c)));
+            __builtin_nontemporal_store(pack_nibbles(bt, lo4),
+                                        reinterpret_cast<uint32_t *>(q4l + (16 * m - L.n8) * (D / 2)));
         }
     };
 #pragma unroll
@@ -383,7 +405,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
             const int k = slot_class(L, m);
             if (k == 1) emit(m, std::true_type{});
             else if (k == 0) emit(m, std::false_type{});
-            else if (g + 16 * m < L.n8) emit(m, std::true_type{});
+            else if (gs + 16 * m < L.n8) emit(m, std::true_type{});
             else emit(m, std::false_type{});
         } else {
             if (m < M8) emit(m, std::true_type{});
@@ -392,24 +414,32 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
     }
     if (REFIT) {
         // ---- Table C2 step 5: the column factors refit to the new codes
-        // (App. C.1 fixed-code update).  Partials per (wave, lane group,
-        // chunk c, column offset e) go through the matrix-core reduction
-        // buffer, free since the column sums were read.
-        float2 *red2 = reinterpret_cast<float2 *>(&sh.red[0][0][0][0]); // [4][4][16][8]
-        float4 *mine = reinterpret_cast<float4 *>(red2 + ((w * 4 + gl) * 16 + c) * 8);
+        // (App. C.1 fixed-code update).  Partials per (wave and lane group
+        // q, column-offset pair e / 2, chunk c) go through the matrix-core
+        // reduction buffer, free since the column sums were read: written 16
+        // bytes per lane, read 8 bytes per lane, both without bank conflicts.
+        // (the lane's coordinates formed afresh from its index: keeps the
+        // compiler from holding them in registers through the codes)
+        int tt = L.t;
+        asm volatile("" : "+v"(tt));
+        float4 *red4 = &sh.red[0][0][0][0]; // [16 q][4 e/2][16 c]
+        const int q0 = tt >> 4, cq = tt & 15;
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) mine[e / 2] = make_float4(num[e], den[e], num[e + 1], den[e + 1]);
+        for (int e = 0; e < 8; e += 2)
+            red4[(q0 * 4 + e / 2) * 16 + cq] = make_float4(num[e], den[e], num[e + 1], den[e + 1]);
         __syncthreads();
-        if (t < D) {
+        if (tt < D) {
+            const int c2 = tt & 15, e2 = ((tt >> 4) + ((tt >> 1) & 6)) & 7; // as above
+            const float2 *red2 = reinterpret_cast<const float2 *>(red4);
             float nsum = 0.0f, dsum = 0.0f;
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                const float2 f = red2[(q * 16 + cc) * 8 + ce];
+                const float2 f = red2[((q * 4 + (e2 >> 1)) * 16 + c2) * 2 + (e2 & 1)];
                 nsum += f.x;
                 dsum += f.y;
             }
-            const float cold = sh.c[jcol];
-            L.cw[jcol] = dsum > 0.0f ? fmaxf(cold * (nsum / dsum), kRowFloor) : cold;
+            const float cold = sh.c[8 * c2 + e2];
+            L.cw[8 * c2 + e2] = dsum > 0.0f ? fmaxf(cold * (nsum / dsum), kRowFloor) : cold;
         }
     }
 }
@@ -506,25 +536,25 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, UnitGeom u
         if (GATED) scale *= __uint_as_float(pick(g0, g1));
         {
             // row p = 4 w + gl + 16 m of wave w, lane group gl, slot m
-            uint32_t(&cf)[6][8] = sh.coef[p & 15].w;
-            const int mm = p >> 4;
+            uint32_t *cf = &sh.coef[(p & 15) * kCoefStride + (p >> 4)]; // row r at 8 r
             uint32_t h0, h1, h2;
             split3w(scale * kp, h0, h1, h2);
-            cf[0][mm] = h0;
-            cf[1][mm] = h1;
-            cf[2][mm] = h2;
+            cf[0] = h0;
+            cf[8] = h1;
+            cf[16] = h2;
             split3w(scale * qp, h0, h1, h2);
-            cf[3][mm] = h0;
-            cf[4][mm] = h1;
-            cf[5][mm] = h2;
+            cf[24] = h0;
+            cf[32] = h1;
+            cf[40] = h2;
         }
         const float ar = L.alpha * scale;
         const float bk = L.beta * kp;
         // |b k| > 2^-64 |a r| (false when both vanish: then x = 0 * z = 0)
         const uint32_t scaled = lane_mask(fabsf(bk) > fabsf(ar) * kFormTiny);
-        const float w2 = REFIT ? __uint_as_float(pick(u0, u1)) : 0.0f;
-        sh.row[p] = make_float4(self(scaled, div_refined(ar, bk), ar), self(scaled, bk, 1.0f), w2,
-                                __uint_as_float(sel(scaled, 0u, 4u * D)));
+        sh.row[p] = make_float2(self(scaled, div_refined(ar, bk), ar), __uint_as_float(sel(scaled, 0u, 4u * D)));
+        const int si = p + (p >> 4);
+        sh.srow[si] = self(scaled, bk, 1.0f);
+        if (REFIT) sh.w2row[si] = __uint_as_float(pick(u0, u1));
         const float kq = wave_sum(kp * qp);
         if ((t & 63) == 0) sh.kq[t >> 6] = kq;
     } else {
