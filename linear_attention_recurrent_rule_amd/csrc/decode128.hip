@@ -489,16 +489,20 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, UnitGeom u
     const int tl = t & (D - 1);
     const int l64 = t & 63;
     const bool lowhalf = __builtin_amdgcn_readfirstlane(t) < D; // wave-uniform
-    const unsigned kb = static_cast<unsigned>((b * a.Hk + hk) * D);
-    const int praw = a.perm[h * D + tl];
+    // (each vector's unit-wide offset goes into its base pointer, so that the
+    // loads take a scalar base and a small per-lane offset)
+    const size_t kb = static_cast<size_t>(b * a.Hk + hk) * D;
+    const TIn *kp0 = static_cast<const TIn *>(a.k) + kb;
+    const TIn *qp0 = static_cast<const TIn *>(a.q) + kb;
+    const int praw = (a.perm + h * D)[tl];
     const float rpv = L.rr[tl];
     // raw bits only: widening here would make the branch wait for the loads
     uint32_t x0, x1, x2 = 0u, x3 = 0u, g0 = 0u, g1 = 0u, u0 = 0u, u1 = 0u;
     if (lowhalf) {
-        x0 = In<TIn>::raw(a.k, kb + l64);
-        x1 = In<TIn>::raw(a.k, kb + 64 + l64);
-        x2 = In<TIn>::raw(a.q, kb + l64);
-        x3 = In<TIn>::raw(a.q, kb + 64 + l64);
+        x0 = In<TIn>::raw(kp0, l64);
+        x1 = In<TIn>::raw(kp0, 64 + l64);
+        x2 = In<TIn>::raw(qp0, l64);
+        x3 = In<TIn>::raw(qp0, 64 + l64);
         if (GATED) {
             const uint32_t *gp = reinterpret_cast<const uint32_t *>(a.gate) + static_cast<size_t>(unit) * D;
             g0 = gp[l64];
@@ -510,9 +514,10 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, UnitGeom u
             u1 = wp[64 + l64];
         }
     } else {
-        x0 = In<TIn>::raw(a.v, static_cast<unsigned>((b * Hv + h) * D + tl));
-        x1 = REFIT ? reinterpret_cast<const uint32_t *>(a.cs)[ub * D + tl]
-                   : reinterpret_cast<const uint32_t *>(a.c)[h * D + tl];
+        x0 = In<TIn>::raw(static_cast<const TIn *>(a.v) + static_cast<size_t>(b * Hv + h) * D, tl);
+        const uint32_t *cp0 = REFIT ? reinterpret_cast<const uint32_t *>(a.cs) + ub * D
+                                    : reinterpret_cast<const uint32_t *>(a.c) + h * D;
+        x1 = cp0[tl];
     }
     // ---- Table C2 step 1: issue the loads of this lane's packed rows
     uint32_t w0[8], w1[8];
