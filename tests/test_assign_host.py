@@ -229,3 +229,60 @@ def test_rejections():
         stq.assign_rows(dist.astype(np.float32), logret, 1.0, 4, 6, 0)
     with pytest.raises(ValueError):
         stq.assign_rows(dist[:, :, :4], logret, 1.0, 4, 6, 0)
+
+
+def _brute_force(cost, widths, budget):
+    """min over every choice of one width per row of the summed cost, among
+    the choices whose widths fit the budget (exhaustive)."""
+    best = np.inf
+    n = cost.shape[0]
+    idx = np.indices((len(widths),) * n).reshape(n, -1).T
+    w = np.asarray(widths)[idx].sum(axis=1)
+    tot = cost[np.arange(n)[None, :], idx].sum(axis=1)
+    ok = w <= budget
+    if ok.any():
+        best = tot[ok].min()
+    return best
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_library_optimal_on_convex_instances(seed):
+    """The library's assignment alone, checked against exhaustive search
+    (no oracle involved): with convex decreasing distortion per row over
+    equally spaced widths (2 bits apart), taking the largest weighted saving
+    per bit first is optimal, so the result must reach the brute-force
+    minimum of sum_i L_i D_i(b_i) for the budget.  L_i is the App. A.3
+    lifetime weight, sum over t < H of a_i^(2 t) with a_i the row's mean
+    retention, here in closed form (1 - a^(2H)) / (1 - a^2)."""
+    g = np.random.default_rng(7100 + seed)
+    d, n, H = 7, 5, 40
+    # decrements D(2)-D(4) > D(4)-D(6) > D(6)-D(8) > 0, and D(8) >= 0
+    dec = np.sort(g.uniform(0.05, 5.0, size=(d, 3)), axis=1)[:, ::-1]
+    d8 = g.uniform(0.0, 1.0, size=d)
+    dist = np.zeros((1, d, 5))
+    dist[0, :, CLASS[8]] = d8
+    dist[0, :, CLASS[6]] = d8 + dec[:, 2]
+    dist[0, :, CLASS[4]] = d8 + dec[:, 2] + dec[:, 1]
+    dist[0, :, CLASS[2]] = d8 + dec[:, 2] + dec[:, 1] + dec[:, 0]
+    a = g.uniform(0.6, 0.99, size=d)
+    logret = (n * np.log(a))[None, :]
+    L = (1.0 - a ** (2 * H)) / (1.0 - a ** 2)
+    cls_w = (16, 8, 6, 4, 2)
+    cases = 0
+    for widths in ((4, 6, 8), (2, 4, 6, 8)):
+        cost = np.stack([L * dist[0, :, CLASS[b]] for b in widths], axis=1)
+        for nominal in widths[1:-1]:  # the nominal width is one of the candidates
+            counts, perm = stq.assign_rows(dist, logret, n, H, nominal, 0, _mask(widths))
+            # widths per row from the class counts and the rows in class order
+            bits = np.zeros(d, int)
+            j = 0
+            for k, cnt in enumerate(counts[0]):
+                bits[perm[0, j:j + cnt]] = cls_w[k]
+                j += cnt
+            assert j == d and set(bits) <= set(widths)
+            assert bits.sum() <= nominal * d
+            got = sum(cost[i, widths.index(int(bits[i]))] for i in range(d))
+            best = _brute_force(cost, widths, nominal * d)
+            assert got <= best * (1 + 1e-9) + 1e-12, (widths, nominal, got, best)
+            cases += 1
+    assert cases == 3
