@@ -17,6 +17,7 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -74,6 +75,9 @@ def parse():
     p.add_argument("--blocks", type=int, default=3,
                    help="timed blocks of --steps launches; ms_per_step is their median")
     p.add_argument("--workload", default="highconc_6bit")
+    p.add_argument("--batch", type=int, default=None,
+                   help="override the workload's number of sequences B (a batch-size sweep; "
+                        "the workload is then named <workload>_B<B>)")
     p.add_argument("--pools", type=int, default=4, help="state pools rotated in the timed loop")
     p.add_argument("--mode", choices=("in_place", "double_buffered"), default="in_place",
                    help="in_place: each step rewrites the pool it reads; double_buffered: "
@@ -371,6 +375,10 @@ def main():
     torch.cuda.set_device(0)
     stq.lib()  # fails loudly if libstq.so is missing
     w = wl.WORKLOADS[args.workload]
+    if args.batch is not None:
+        if args.batch < 1:
+            raise SystemExit("--batch must be at least 1")
+        w = dataclasses.replace(w, B=args.batch, name=f"{w.name}_B{args.batch}")
     B, hv, hk, d = w.B, w.hv, w.hk, w.d
     in_el = 2 if w.dtype == "bf16" else 4
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
