@@ -721,23 +721,29 @@ __global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, Unit
         // Partials per (wave and lane group q, column-offset pair e / 2,
         // chunk c), written 16 bytes and read 8 bytes per lane without bank
         // conflicts
+        // (the lane's coordinates formed afresh from its index: keeps the
+        // compiler from holding them in registers through the codes)
+        int tt = t;
+        asm volatile("" : "+v"(tt));
         float4 *red4 = &sh.red[0][0][0][0]; // [16 q][4 e/2][16 c]
-        const int q0 = w * 4 + gl;
+        const int q0 = tt >> 4, cq = tt & 15;
 #pragma unroll
         for (int e = 0; e < 8; e += 2)
-            red4[(q0 * 4 + e / 2) * 16 + c] = make_float4(num[e], den[e], num[e + 1], den[e + 1]);
+            red4[(q0 * 4 + e / 2) * 16 + cq] = make_float4(num[e], den[e], num[e + 1], den[e + 1]);
         __syncthreads();
-        if (t < D) {
+        if (tt < D) {
+            const int c2 = tt & 15, e2 = ((tt >> 4) + ((tt >> 1) & 6)) & 7; // as in the reduction
             const float2 *red2 = reinterpret_cast<const float2 *>(red4);
             float nsum = 0.0f, dsum = 0.0f;
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                const float2 f = red2[((q * 4 + (ce >> 1)) * 16 + cc) * 2 + (ce & 1)];
+                const float2 f = red2[((q * 4 + (e2 >> 1)) * 16 + c2) * 2 + (e2 & 1)];
                 nsum += f.x;
                 dsum += f.y;
             }
-            const float cold = sh.c[jcol];
-            a.cs_out[ub * D + jcol] = dsum > 0.0f ? fmaxf(cold * (nsum / dsum), kRowFloor) : cold;
+            const int j = 8 * c2 + e2;
+            const float cold = sh.c[j];
+            a.cs_out[ub * D + j] = dsum > 0.0f ? fmaxf(cold * (nsum / dsum), kRowFloor) : cold;
         }
     }
 }
