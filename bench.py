@@ -430,7 +430,7 @@ def main():
     o_f32 = torch.empty((B, hv, d), dtype=torch.float32, device="cuda")
     o = o_f32
 
-    alloc_cal = {}  # gated -> (counts, c, perm, w2) of the ragged format
+    alloc_cal = {}  # (gated, refit) -> (counts, c, perm, w2) of the ragged format
     gate_cache = []
 
     def gate_window():
@@ -443,10 +443,13 @@ def main():
         pools = []
         for _ in range(n):
             if fmt in (stq.FMT_ALLOC, stq.FMT_ALLOC_REFIT):
-                counts, ca, pa, _ = alloc_cal[gated]
+                refit_ = fmt == stq.FMT_ALLOC_REFIT
+                counts, ca, pa, w2a = alloc_cal[(gated, refit_)]
                 st = stq.State(stq.Geometry(B, hv, hk, d, 0, fmt, nominal_bits=alloc_nominal(w),
                                             n_pivot=alloc_pivots(hv, d)))
                 st.set_alloc_layout(counts, ca, pa)
+                if refit_:
+                    st.w2.copy_(w2a)
             else:
                 st = stq.State(stq.Geometry(B, hv, hk, d, n8, fmt))
             if fmt in (stq.FMT_MIXED48, stq.FMT_REFIT):
@@ -559,7 +562,9 @@ def main():
         mean_ms = sorted(blocks)[len(blocks) // 2]  # the median block
         nbytes = algorithmic_bytes(fmt_name, B, hv, hk, d, n8, in_el, gated, 2 if out_bf16 else 4)
         if fmt in (stq.FMT_ALLOC, stq.FMT_ALLOC_REFIT):
-            unit = alloc_unit_bytes(alloc_cal[gated][0], d)
+            refit_ = fmt == stq.FMT_ALLOC_REFIT
+            # segment + row factors, plus the state's own column factors when refit
+            unit = alloc_unit_bytes(alloc_cal[(gated, refit_)][0], d) + (4 * d if refit_ else 0)
             nbytes = int(2 * unit * B * hv) + algorithmic_bytes("fp32", B, hv, hk, d, 0, in_el,
                                                                  gated) - 2 * 4 * d * d * B * hv
         res = dict(updates_per_s=B * hv / (mean_ms / 1e3), ms_per_step=mean_ms,
@@ -607,19 +612,21 @@ def main():
             variants["row_gate_kda"] = measure("mixed", stq.FMT_MIXED48, w.n8, args.pools,
                                                args.steps, args.warmup, gated=True)
         # ragged rows (FP16 pivots + 8/6/4/2 bits from the lifetime-aware
-        # assignment), scalar gate and KDA row gate, each with its own calibration
-        for gated_ in (False, True):
-            name = "alloc_pivots_kda_gate" if gated_ else "alloc_pivots"
+        # assignment): scalar gate, KDA row gate, and the scalar gate with the
+        # column refit, each with its own calibration
+        for name, gated_, refit_ in (("alloc_pivots", False, False),
+                                     ("alloc_pivots_kda_gate", True, False),
+                                     ("alloc_pivots_refit", False, True)):
             if not want(name):
                 continue
             t1 = time.time()
-            alloc_cal[gated_] = calibrate_alloc(
+            alloc_cal[(gated_, refit_)] = calibrate_alloc(
                 torch, stq, S0, lambda t: alloc_cal_inputs(t, gated_), B=B, hv=hv, hk=hk, d=d,
                 steps=w.calib_steps, nominal=alloc_nominal(w), n_pivot=alloc_pivots(hv, d),
-                gated=gated_)
-            cnt = alloc_cal[gated_][0]
-            res = measure("mixed", stq.FMT_ALLOC, w.n8, args.pools, args.steps, args.warmup,
-                          gated=gated_)
+                gated=gated_, refit=refit_)
+            cnt = alloc_cal[(gated_, refit_)][0]
+            res = measure("mixed", stq.FMT_ALLOC_REFIT if refit_ else stq.FMT_ALLOC, w.n8,
+                          args.pools, args.steps, args.warmup, gated=gated_)
             res["rows_by_width"] = {str(b): int(cnt[:, k].sum())
                                     for k, b in enumerate((16, 8, 6, 4, 2))}
             res["bits_per_value"] = 8 * alloc_unit_bytes(cnt, d) / (d * d)

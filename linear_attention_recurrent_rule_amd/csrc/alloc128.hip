@@ -255,8 +255,12 @@ struct Smem {
     float ra[16][8], rb[16][8]; // column refit: w2 r' s and w2 r'^2 per row
 };
 
+// Three workgroups per CU cap the registers at 168. The instances without the
+// column refit sit well below that; the refit ones would otherwise take 172
+// and drop to two waves per SIMD, which costs about a third more time than the
+// few values the cap spills.
 template <typename TIn, bool REFIT, bool GATED>
-__global__ __launch_bounds__(256) void decode_alloc128_kernel(DecodeArgs a, UnitGeom ug) {
+__global__ __launch_bounds__(256, 3) void decode_alloc128_kernel(DecodeArgs a, UnitGeom ug) {
     __shared__ Smem sh;
     const int t = threadIdx.x;
     const int c = t & 15;
