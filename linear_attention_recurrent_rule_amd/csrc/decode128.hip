@@ -23,8 +23,8 @@
 //    brought into physical row order by lane permutes instead of a gather
 //    through perm;
 //  * per-row factors are formed once per row by the staging lanes and read
-//    from LDS: r k and r q (with 1/16 folded in for 4-bit rows, whose codes are
-//    widened as 16 z), and the update in the form
+//    from LDS: r k and r q (with 16 folded in for 4-bit rows, whose signed
+//    nibbles are converted directly to z / 16), and the update in the form
 //        x_ij = X_ij / c_j = s_i (P_i z_ij + E_ij)
 //    with s_i = b k_i, P_i = a r_i / (b k_i), E_ij = e_j for a row whose b k_i
 //    is not negligible next to a r_i, and s_i = 1, P_i = a r_i, E_ij = 0 for a
@@ -160,7 +160,8 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
     const int t = L.t, c = L.c, g = L.g;
 
     // ---- widen the codes into fp32 registers zb[h][e][s] = code of slot
-    // 4h + s in column 8c + e (4-bit codes as 16 z); column sums
+    // 4h + s in column 8c + e (4-bit codes as z / 16, or as 16 z in a slot
+    // that mixes the two widths); column sums
     // u~ = S~^T (r k), w~ = S~^T (r q) on the matrix cores, two 16x16x32 bf16
     // products per column offset e reading those registers as (0, z) pairs
     // (codes are small integers, exact in bf16; the coefficient splits are
@@ -177,8 +178,6 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
             // no branch, the two words whose bytes are its eight codes
             const int k = slot_class(L, m);
             const uint32_t w4 = (c & 1) ? w1[m] : w0[m]; // a 4-bit row's 4 bytes
-            const uint32_t hi = w4 & 0xF0F0F0F0u;          // odd columns, x16
-            const uint32_t lo = (w4 << 4) & 0xF0F0F0F0u;   // even columns, x16
             if (k == 1) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -186,13 +185,19 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
                     zb[hh][4 + e][s] = sbyte(w1[m], e);
                 }
             } else if (k == 0) {
+                uint32_t w4h = w4 >> 4;
+                asm volatile("" : "+v"(w4h)); // one shift, then byte selects
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    zb[hh][2 * e][s] = sbyte(lo, e);
-                    zb[hh][2 * e + 1][s] = sbyte(hi, e);
+                    zb[hh][2 * e][s] = snib(w4, e);
+                    zb[hh][2 * e + 1][s] = snib(w4h, e);
                 }
             } else {
-                // bytes in column order: lo0 hi0 lo1 hi1 | lo2 hi2 lo3 hi3
+                // a 4-bit lane's codes as 16 z, so that one sign-extending
+                // byte conversion serves both widths; bytes in column order:
+                // lo0 hi0 lo1 hi1 | lo2 hi2 lo3 hi3
+                const uint32_t hi = w4 & 0xF0F0F0F0u;        // odd columns
+                const uint32_t lo = (w4 << 4) & 0xF0F0F0F0u; // even columns
                 const uint32_t own8 = lane_mask(g + 16 * m < L.n8);
                 const uint32_t x0 = sel(own8, w0[m], __builtin_amdgcn_perm(hi, lo, 0x05010400u));
                 const uint32_t x1 = sel(own8, w1[m], __builtin_amdgcn_perm(hi, lo, 0x07030602u));
@@ -211,12 +216,15 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
                 zb[hh][4 + e][s] = sbyte(w1[m], e);
             }
         } else {
-            const uint32_t hi = w0[m] & 0xF0F0F0F0u;         // odd columns, x16
-            const uint32_t lo = (w0[m] << 4) & 0xF0F0F0F0u;  // even columns, x16
+            // even columns in the low nibbles, odd columns in the high ones
+            // (an opaque copy of the shifted word: otherwise the compiler
+            // merges the shift into a bit-field extract per column)
+            uint32_t wh = w0[m] >> 4;
+            asm volatile("" : "+v"(wh));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                zb[hh][2 * e][s] = sbyte(lo, e);
-                zb[hh][2 * e + 1][s] = sbyte(hi, e);
+                zb[hh][2 * e][s] = snib(w0[m], e);
+                zb[hh][2 * e + 1][s] = snib(wh, e);
             }
         }
     }
@@ -536,8 +544,13 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, UnitGeom u
         const float kp = In<TIn>::cvt(pick(x0, x1));
         const float qp = In<TIn>::cvt(pick(x2, x3));
         const float rp = rpv;
-        // 4-bit codes are widened as 16 z; a row gate scales the whole row
-        float scale = rp * self(lane_mask(p < n8), 1.0f, 0.0625f);
+        // 4-bit codes are widened as z / 16, except in the group of four rows
+        // that straddles a split which is not a multiple of 4 (16 z there);
+        // a row gate scales the whole row
+        float f4 = 16.0f;
+        if constexpr (N8 == kRuntimeN8)
+            if ((n8 & 3) != 0 && (p >> 2) == (n8 >> 2)) f4 = 0.0625f;
+        float scale = rp * self(lane_mask(p < n8), 1.0f, f4);
         if (GATED) scale *= __uint_as_float(pick(g0, g1));
         {
             // row p = 4 w + gl + 16 m of wave w, lane group gl, slot m

@@ -64,6 +64,11 @@ template <> struct In<uint16_t> {
 __device__ __forceinline__ float sbyte(uint32_t w, int k) {
     return static_cast<float>(static_cast<int8_t>(w >> (8 * k)));
 }
+// the signed 4-bit field in bits 8k..8k+3 of w, widened exactly as z / 16:
+// one conversion, the byte select folded into it
+__device__ __forceinline__ float snib(uint32_t w, int k) {
+    return __builtin_amdgcn_cvt_off_f32_i4((w >> (8 * k)) & 0xFFu);
+}
 
 // ---- per-lane selects: m is all ones or all zeros in each lane
 __device__ __forceinline__ uint32_t lane_mask(bool b) {
