@@ -119,9 +119,19 @@ def _check(status: int, where: str):
         raise StqError(status, where)
 
 
-def _stream(stream=None):
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+# the current stream's handle straight from torch's C layer where it offers
+# that (a Python Stream object costs microseconds per call)
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream=None, device=None):
+    """Handle of `stream`, else of the current stream (on `device` when given,
+    the device of the state being worked on)."""
+    if stream is not None:
+        return stream.cuda_stream
+    if _RAW_STREAM is not None and device is not None and device.index is not None:
+        return _RAW_STREAM(device.index)
+    return torch.cuda.current_stream().cuda_stream
 
 
 _FLOAT_IN = (torch.float32, torch.bfloat16)
@@ -140,8 +150,11 @@ def _check_meta(t, name: str, shape=None, dtypes=None):
         names = " or ".join(str(d).replace("torch.", "") for d in dtypes)
         raise ValueError(f"{name} must be {names}, got {str(t.dtype).replace('torch.', '')}")
     if shape is not None:
-        ok = t.dim() == len(shape) and all(e is None or int(n) == e
-                                          for n, e in zip(t.shape, shape))
+        ts = t.shape
+        if None in shape:
+            ok = len(ts) == len(shape) and all(e is None or n == e for n, e in zip(ts, shape))
+        else:
+            ok = ts == shape
         if not ok:
             want = "[" + "][".join("*" if e is None else str(e) for e in shape) + "]"
             raise ValueError(f"{name} must have shape {want}, got {list(t.shape)}")
@@ -155,13 +168,22 @@ def _dev_ptr(t: torch.Tensor | None, name: str, shape=None, dtypes=None, device=
     if t is None:
         return None
     _check_meta(t, name, shape, dtypes)
+    return _placed_ptr(t, name, device)
+
+
+def _placed_ptr(t: torch.Tensor | None, name: str, device=None):
+    """The device checks of _dev_ptr (on a HIP device, on `device` when given,
+    contiguous) and the pointer, as an integer for a c_void_p argument."""
+    if t is None:
+        return None
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
-    if device is not None and t.device != device:
+    if device is not None and (t.get_device() != device.index if device.index is not None
+                               else t.device != device):
         raise ValueError(f"{name} is on {t.device}, the state on {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()
 
 
 def _dev_ptrs(*specs, device=None):
@@ -170,7 +192,7 @@ def _dev_ptrs(*specs, device=None):
     names the argument that is wrong rather than the first one on the host."""
     for t, name, shape, dtypes in specs:
         _check_meta(t, name, shape, dtypes)
-    return [_dev_ptr(t, name, shape, dtypes, device) for t, name, shape, dtypes in specs]
+    return [_placed_ptr(t, name, device) for t, name, shape, dtypes in specs]
 
 
 def _in_dtype(q, k, v) -> int:
@@ -244,9 +266,10 @@ class State:
         if nbytes == 0:
             raise StqError(2, "stq_state_bytes (invalid or unsupported geometry)")
         self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self._device = self.buffer.device  # (read once: a device object per call costs time)
         self.c_state = CState()
         _check(_lib().stq_alloc_state(ctypes.byref(self.desc), _dev_ptr(self.buffer, "buffer"),
-                                      nbytes, _stream(stream), ctypes.byref(self.c_state)),
+                                      nbytes, _stream(stream, self._device), ctypes.byref(self.c_state)),
                "stq_alloc_state")
 
     # -- views into the caller-owned buffer (for inspection and tests) --
@@ -350,22 +373,22 @@ class State:
     def calibrate_retention(self, alpha=None, gate=None, flags: int = 0, stream=None):
         """Fold one step's gates (alpha [B][Hv] or gate [B][Hv][d]) into the
         summed log retention (stq_calibrate_retention)."""
-        g, dv = self.geo, self.buffer.device
+        g, dv = self.geo, self._device
         src = gate if gate is not None else alpha
         B = 0 if src is None else _batch(src, "gate" if gate is not None else "alpha")
         pa, pg = _dev_ptrs((alpha, "alpha", (B, g.n_heads_v), _F32),
                            (gate, "gate", (B, g.n_heads_v, g.d), _F32), device=dv)
         _check(_lib().stq_calibrate_retention(ctypes.byref(self.c_state), pa, pg, B, flags,
-                                              _stream(stream)), "stq_calibrate_retention")
+                                              _stream(stream, self._device)), "stq_calibrate_retention")
 
     def allocate(self, horizon: int, candidates: int = 0, stream=None):
         """Pivots and row widths from the calibration statistics (stq_allocate)."""
         _check(_lib().stq_allocate(ctypes.byref(self.c_state), int(horizon), int(candidates),
-                                   _stream(stream)), "stq_allocate")
+                                   _stream(stream, self._device)), "stq_allocate")
 
     def set_alloc_layout(self, counts, c: torch.Tensor, perm: torch.Tensor, stream=None):
         """Install class counts [Hv][5] (host array), c and perm (device)."""
-        g, dv = self.geo, self.buffer.device
+        g, dv = self.geo, self._device
         cnt = np.ascontiguousarray(counts, dtype=np.int32)
         if cnt.shape != (g.n_heads_v, 5):
             raise ValueError(f"counts must have shape [{g.n_heads_v}][5], got {list(cnt.shape)}")
@@ -374,7 +397,7 @@ class State:
         pc, pp = _dev_ptrs((c, "c", (g.n_heads_v, g.d), _F32),
                            (perm, "perm", (g.n_heads_v, g.d), _I32), device=dv)
         _check(_lib().stq_set_alloc_layout(ctypes.byref(self.c_state), cnt.ctypes.data, pc, pp,
-                                           _stream(stream)), "stq_set_alloc_layout")
+                                           _stream(stream, self._device)), "stq_set_alloc_layout")
 
     @property
     def calibrated(self) -> bool:
@@ -386,9 +409,9 @@ class State:
         that `flags` name (stq_calibrate)."""
         g = self.geo
         n = 0 if records is None else _batch(records, "records")
-        p = _dev_ptr(records, "records", (n, g.n_heads_v, g.d, g.d), _F32, self.buffer.device)
-        _check(_lib().stq_calibrate(ctypes.byref(self.c_state), p, n, flags, _stream(stream)),
-               "stq_calibrate")
+        p = _dev_ptr(records, "records", (n, g.n_heads_v, g.d, g.d), _F32, self._device)
+        _check(_lib().stq_calibrate(ctypes.byref(self.c_state), p, n, flags,
+                                    _stream(stream, self._device)), "stq_calibrate")
 
     def calibrate_static(self, records: torch.Tensor | None, flags: int, stream=None):
         """stq_calibrate_static: as calibrate, with the partial results in the
@@ -396,16 +419,16 @@ class State:
         must not overlap)."""
         g = self.geo
         n = 0 if records is None else _batch(records, "records")
-        p = _dev_ptr(records, "records", (n, g.n_heads_v, g.d, g.d), _F32, self.buffer.device)
+        p = _dev_ptr(records, "records", (n, g.n_heads_v, g.d, g.d), _F32, self._device)
         _check(_lib().stq_calibrate_static(ctypes.byref(self.c_state), p, n, flags,
-                                           _stream(stream)), "stq_calibrate_static")
+                                           _stream(stream, self._device)), "stq_calibrate_static")
 
     def calibrate_impact(self, q, k, alpha, beta, flags: int, stream=None, gate=None):
         """Accumulate row impact over one step's samples (q, k [B][Hk][d], alpha,
         beta [B][Hv]); CAL_RESET / CAL_FINALIZE as in stq_calibrate_impact.
         With gate [B][Hv][d] (logical rows) the row gate replaces alpha
         (stq_calibrate_impact_gated)."""
-        g, dv = self.geo, self.buffer.device
+        g, dv = self.geo, self._device
         if q is None:
             B, dt = 0, F32
         else:
@@ -421,20 +444,20 @@ class State:
             (beta, "beta", (B, g.n_heads_v), _F32), device=dv)
         if gated:
             _check(_lib().stq_calibrate_impact_gated(ctypes.byref(self.c_state), pq, pk, dt, pr,
-                                                     pb, B, flags, _stream(stream)),
+                                                     pb, B, flags, _stream(stream, self._device)),
                    "stq_calibrate_impact_gated")
             return
         _check(_lib().stq_calibrate_impact(ctypes.byref(self.c_state), pq, pk, dt, pr, pb, B,
-                                           flags, _stream(stream)), "stq_calibrate_impact")
+                                           flags, _stream(stream, self._device)), "stq_calibrate_impact")
 
     def set_calibration(self, c: torch.Tensor, perm: torch.Tensor, stream=None):
         """Install column factors c [Hv][d] fp32 and row order perm [Hv][d]
         int32 (stq_set_calibration)."""
-        g, dv = self.geo, self.buffer.device
+        g, dv = self.geo, self._device
         pc, pp = _dev_ptrs((c, "c", (g.n_heads_v, g.d), _F32),
                            (perm, "perm", (g.n_heads_v, g.d), _I32), device=dv)
-        _check(_lib().stq_set_calibration(ctypes.byref(self.c_state), pc, pp, _stream(stream)),
-               "stq_set_calibration")
+        _check(_lib().stq_set_calibration(ctypes.byref(self.c_state), pc, pp,
+                                          _stream(stream, self._device)), "stq_set_calibration")
 
     def pack(self, S: torch.Tensor, slots: torch.Tensor | None = None, stream=None):
         """Pack fp32 states S [B][Hv][d][d] (logical rows) into slots
@@ -442,9 +465,9 @@ class State:
         g = self.geo
         B = _batch(S, "S")
         pS, ps = _dev_ptrs((S, "S", (B, g.n_heads_v, g.d, g.d), _F32), (slots, "slots", (B,), _I32),
-                           device=self.buffer.device)
-        _check(_lib().stq_pack_state(ctypes.byref(self.c_state), pS, ps, B, _stream(stream)),
-               "stq_pack_state")
+                           device=self._device)
+        _check(_lib().stq_pack_state(ctypes.byref(self.c_state), pS, ps, B,
+                                     _stream(stream, self._device)), "stq_pack_state")
 
     def _readout(self, q, k, v, o, o_dtype):
         """The readout buffer (allocated when o is None, in o_dtype: fp32 by
@@ -454,7 +477,7 @@ class State:
         B = _batch(q, "q")
         if o is None:
             o = torch.empty((B, self.geo.n_heads_v, self.geo.d),
-                            dtype=o_dtype or torch.float32, device=self.buffer.device)
+                            dtype=o_dtype or torch.float32, device=self._device)
         if not isinstance(o, torch.Tensor) or o.dtype not in _FLOAT_IN:
             raise ValueError("o must be a float32 or bfloat16 tensor")
         if o.dtype == torch.bfloat16:
@@ -476,14 +499,14 @@ class State:
             shape = (B, g.n_heads_v, g.d) if name == "gate" else (B, g.n_heads_v)
             specs.append((t, name, shape, _F32))
         specs.append((o, "o", (B, g.n_heads_v, g.d), _FLOAT_IN))
-        return B, _dev_ptrs(*specs, device=self.buffer.device)
+        return B, _dev_ptrs(*specs, device=self._device)
 
     def decode_step(self, q, k, v, alpha, beta, o=None, slots=None, stream=None, o_dtype=None):
         o, dt = self._readout(q, k, v, o, o_dtype)
         B, (ps, pq, pk, pv, pa, pb, po) = self._step_ptrs(q, k, v, o, slots, alpha=alpha,
                                                          beta=beta)
         _check(_lib().stq_decode_step(ctypes.byref(self.c_state), ps, B, pq, pk, pv, dt, pa, pb,
-                                      po, _stream(stream)), "stq_decode_step")
+                                      po, _stream(stream, self._device)), "stq_decode_step")
         return o
 
     def decode_step_into(self, dst: "State", q, k, v, alpha, beta, o=None, slots=None,
@@ -493,7 +516,8 @@ class State:
         B, (ps, pq, pk, pv, pa, pb, po) = self._step_ptrs(q, k, v, o, slots, alpha=alpha,
                                                          beta=beta)
         _check(_lib().stq_decode_step_into(ctypes.byref(self.c_state), ctypes.byref(dst.c_state),
-                                           ps, B, pq, pk, pv, dt, pa, pb, po, _stream(stream)),
+                                           ps, B, pq, pk, pv, dt, pa, pb, po,
+                                           _stream(stream, self._device)),
                "stq_decode_step_into")
         return o
 
@@ -507,7 +531,7 @@ class State:
         target = self if dst is None else dst
         _check(_lib().stq_decode_step_gated(ctypes.byref(self.c_state),
                                             ctypes.byref(target.c_state), ps, B, pq, pk, pv, dt,
-                                            pg, pb, po, _stream(stream)),
+                                            pg, pb, po, _stream(stream, self._device)),
                "stq_decode_step_gated")
         return o
 
@@ -517,11 +541,11 @@ class State:
             B = _batch(slots, "slots") if slots is not None else g.n_slots
         if out is None:
             out = torch.empty((B, g.n_heads_v, g.d, g.d), dtype=torch.float32,
-                              device=self.buffer.device)
+                              device=self._device)
         po, ps = _dev_ptrs((out, "out", (B, g.n_heads_v, g.d, g.d), _F32),
-                           (slots, "slots", (B,), _I32), device=self.buffer.device)
-        _check(_lib().stq_dequant_state(ctypes.byref(self.c_state), ps, B, po, _stream(stream)),
-               "stq_dequant_state")
+                           (slots, "slots", (B,), _I32), device=self._device)
+        _check(_lib().stq_dequant_state(ctypes.byref(self.c_state), ps, B, po,
+                                        _stream(stream, self._device)), "stq_dequant_state")
         return out
 
 
@@ -535,4 +559,4 @@ def stream_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
     n = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() != n:
         raise ValueError(f"dst holds {dst.numel() * dst.element_size()} bytes, src {n}")
-    _check(_lib().stq_stream_copy(ps, pd, n, _stream(stream)), "stq_stream_copy")
+    _check(_lib().stq_stream_copy(ps, pd, n, _stream(stream, src.device)), "stq_stream_copy")

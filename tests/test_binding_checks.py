@@ -18,6 +18,7 @@ def _state(fmt=stq.FMT_MIXED48, n8=32, nominal=0, piv=0):
     st = stq.State.__new__(stq.State)
     st.geo = stq.Geometry(8, HV, HK, D, n8, fmt, nominal, piv)
     st.buffer = torch.empty(0, dtype=torch.uint8, device="meta")
+    st._device = st.buffer.device  # as State.__init__ sets it
     return st
 
 
