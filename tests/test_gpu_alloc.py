@@ -106,7 +106,8 @@ SUM_ROUNDINGS = 40
 
 
 def pivot_allowance(pool, r, counts, perm, c, k, v, beta, X, d, *, alpha=None, gate=None):
-    """Per pivot value [B][Hv][d][d] (physical rows): a bound on the distance
+    """Per pivot value [B][Hv][d][d] (physical rows; c the column factors per
+    head [Hv][d] or per state [B][Hv][d]): a bound on the distance
     between the kernel's fp32 value of X_ij and the exact one, from its
     rounding chain.  With T1 = g_i h_ij (the gated old value, g the gate:
     alpha or the row gate d_i) and T2 = X_ij - T1 (the delta write):
@@ -138,14 +139,16 @@ def pivot_allowance(pool, r, counts, perm, c, k, v, beta, X, d, *, alpha=None, g
         a = alpha.astype(np.float64)
     piv = (cls == 0)[None, :, :, None]                               # [1][Hv][d][1]
     h = hbits.view(np.float16).astype(np.float64)
-    cc = c.astype(np.float64)[None, :, None, :]                      # [1][Hv][1][d]
+    # c per head [Hv][d], or per state [B][Hv][d] (the refit format)
+    cb = c.astype(np.float64) if c.ndim == 3 else c.astype(np.float64)[None]
+    cc = cb[:, :, None, :]                                           # [.][Hv][1][d]
     rr = r.astype(np.float64)[..., None]
     coef = np.where(piv, gp[..., None] * kp[..., None] / cc, gp[..., None] * rr * kp[..., None])
     val = np.where(piv, h, codes.astype(np.float64))
     terms = coef * val                                              # [B][Hv][d][d]
     u_sum = terms.sum(axis=2)                                       # [B][Hv][d] per column
     u_abs = np.abs(terms).sum(axis=2)
-    vc = v.astype(np.float64) / c.astype(np.float64)[None]
+    vc = v.astype(np.float64) / cb
     e = vc - a[..., None] * u_sum
     de = U * (1.5 * np.abs(vc) + np.abs(e) + SUM_ROUNDINGS * a[..., None] * u_abs)
     Xp = np.take_along_axis(X, perm[None, :, :, None], axis=2)        # physical rows

@@ -27,6 +27,7 @@ if not torch.cuda.is_available():  # pragma: no cover
 
 from linear_attention_recurrent_rule_amd import stq  # noqa: E402
 from tests import gpu_util as gu  # noqa: E402
+from tests import test_gpu_refit as tr  # noqa: E402
 from tests.test_gpu_alloc import _compare, pivot_allowance  # noqa: E402
 
 QMAX = np.array([0, 127, 31, 7, 1])
@@ -86,6 +87,54 @@ def test_alloc_fullsize_step_sampled_parity_and_properties(oracle_mod, gated):
                                 gate=gate[bs] if gated else None)
     stats = _compare(gp[bs], gr[bs], ref["pool"], ref["r"], counts, d, "ragged full size",
                      o=go[bs], ref_o=ref["o"], pivot_err=pivot_err)
+    print(stats)
+
+
+def test_alloc_refit_fullsize_step_sampled_parity(oracle_mod):
+    """The refit format (per-state column factors refit at every step over
+    the integer rows) at the same full size and layout, in the launch the
+    bench times: sampled sequences against the oracle, column factors
+    included."""
+    w = wl.WORKLOADS["highconc_6bit"]
+    B, hv, hk, d = w.B, w.hv, w.hk, w.d
+    print(f"[case] ragged refit full size B={B} hv={hv} hk={hk} d={d}", flush=True)
+    counts = wl.calibration_shaped_counts(hv, d, seed=w.seed + 610, two_bit_heads=4)
+    g = wl.rng_for(w.seed, 611)
+    perm = np.stack([g.permutation(d) for _ in range(hv)]).astype(np.int32)
+    c = g.lognormal(0.0, 0.7, size=(hv, d)).astype(np.float32)
+    cs = g.lognormal(0.0, 0.7, size=(B, hv, d)).astype(np.float32)
+    w2 = (g.uniform(0.05, 1.0, size=(hv, d)) ** 0.5).astype(np.float32)
+    st = stq.State(stq.Geometry(B, hv, hk, d, 0, stq.FMT_ALLOC_REFIT, nominal_bits=8,
+                                n_pivot=int(counts[:, 0].sum())))
+    st.set_alloc_layout(counts, gu.dev(c), gu.dev(perm))
+    pool, r = wl.random_ragged_state(B, counts, d, st.slot_bytes, seed=w.seed + 612)
+    st.pool.copy_(gu.dev(pool))
+    st.r.copy_(gu.dev(r))
+    st.cs.copy_(gu.dev(cs))
+    st.w2.copy_(gu.dev(w2))
+    x = wl.workload_inputs(w, 0)
+    q, k, v, a, b = gu.inputs_to_device(x)
+    torch.cuda.synchronize()
+    print("[case] launching the full-size refit step", flush=True)
+    o = st.decode_step(q, k, v, a, b)
+    torch.cuda.synchronize()
+    gp, gr, go, gcs = st.pool.cpu().numpy(), st.r.cpu().numpy(), o.cpu().numpy(), st.cs.cpu().numpy()
+    assert np.all(np.isfinite(go)) and np.all(np.isfinite(gcs)) and np.all(gcs > 0)
+
+    bs = np.unique(np.concatenate([[0, B - 1], g.choice(B, 6, replace=False)]))
+    print(f"[case] oracle on sequences {bs.tolist()}", flush=True)
+    ref = oracle_mod.alloc_step(pool[bs], r[bs], counts, perm, x.q[bs], x.k[bs], x.v[bs],
+                                x.alpha[bs], x.beta[bs], cs=cs[bs], w2=w2, nthreads=16,
+                                want_X=True)
+    pivot_err = pivot_allowance(pool[bs], r[bs], counts, perm, cs[bs], x.k[bs], x.v[bs],
+                                x.beta[bs], ref["X"], d, alpha=x.alpha[bs])
+    stats = _compare(gp[bs], gr[bs], ref["pool"], ref["r"], counts, d, "ragged refit full size",
+                     o=go[bs], ref_o=ref["o"], pivot_err=pivot_err)
+    zg, _, _ = wl.unpack_ragged(gp[bs], counts, d)
+    zr, _, _ = wl.unpack_ragged(ref["pool"], counts, d)
+    stats["max_cs_rel"] = tr._compare_cs(gcs[bs], ref["cs"], "ragged refit full size", X=ref["X"],
+                                         z=zg, zref=zr, r=gr[bs], perm=perm, w2=w2,
+                                         cs_old=cs[bs])
     print(stats)
 
 
