@@ -150,6 +150,27 @@ def test_bf16_readout_ragged(d, gated):
     _run_pair(make, x, gate)
 
 
+def test_bf16_readout_fullsize():
+    """The launch the benchmark times for this variant: B = 1024 sequences, 32
+    value heads over 16 key heads, d = 128, the 6-bit mix, bf16 inputs."""
+    w = wl.WORKLOADS["highconc_6bit"]
+    print(f"[case] bf16 readout full size B={w.B} hv={w.hv} hk={w.hk} d={w.d} n8={w.n8}",
+          flush=True)
+    ps = wl.random_packed_state(w.B, w.hv, w.d, w.n8, seed=w.seed + 740)
+    x = wl.workload_inputs(w, 0)
+    q, k, v, a, b = gu.inputs_to_device(x)
+    s32 = gu.make_state(w.B, w.hv, w.hk, w.d, w.n8)
+    gu.load_packed(s32, ps)
+    s16 = gu.make_state(w.B, w.hv, w.hk, w.d, w.n8)
+    gu.load_packed(s16, ps)
+    o32 = s32.decode_step(q, k, v, a, b)
+    o16 = s16.decode_step(q, k, v, a, b, o_dtype=torch.bfloat16)
+    _same_state(s32, s16)
+    assert o16.dtype == torch.bfloat16 and o16.shape == o32.shape
+    assert not torch.isnan(o32).any()
+    assert torch.equal(o16.view(torch.int16), o32.to(torch.bfloat16).view(torch.int16))
+
+
 def test_bf16_readout_rejects_other_dtypes():
     st = gu.make_state(2, HV, HK, 32, 8)
     ps = wl.random_packed_state(2, HV, 32, 8, seed=730)
