@@ -113,12 +113,13 @@ __device__ __forceinline__ void per_slot(const Bounds &L, unsigned tab, int g, i
     else with_class(class_of(L, g + 16 * m), f);
 }
 
-// Lane constants of the chunk layouts: masks of c & 1 and c & 2, and the
-// shift 16 (c & 1) that brings the lane's 16-bit field of a 32-bit word down.
+// Lane constants of the chunk layouts: the mask of c & 1 (which 32-bit half
+// of an 8-byte word holds the lane's 4 bytes of nibbles), and the byte
+// selector that picks the lane's 2 bytes of 2-bit fields (bytes b, b + 1 of
+// an 8-byte word, b = 2 (c % 4)) as [b, b, b + 1, b + 1].
 struct ChunkLane {
     uint32_t odd;  // lane mask of c & 1
-    uint32_t half; // lane mask of c & 2
-    uint32_t sh;   // 16 (c & 1)
+    uint32_t fsel; // v_perm selector of the lane's 16-bit field, doubled
 };
 
 // Every slot issues the same two 8-byte loads, A and B, whatever its class
@@ -150,9 +151,10 @@ __device__ __forceinline__ void chunk_offsets(unsigned row, int c, unsigned &off
     }
 }
 
-// Byte e' of the result holds nibble e' of the 16-bit value x (e' = 0..3).
-__device__ __forceinline__ uint32_t nibbles_to_bytes(uint32_t x) {
-    const uint32_t t = __builtin_amdgcn_perm(x, x, 0x01010000u); // bytes [x0, x0, x1, x1]
+// Byte e' of the result holds nibble e' of the lane's 16-bit field in the
+// 8-byte word (hi, lo), which one byte permute brings out as [f0, f0, f1, f1].
+__device__ __forceinline__ uint32_t field_nibbles(uint32_t hi, uint32_t lo, const ChunkLane &cl) {
+    const uint32_t t = __builtin_amdgcn_perm(hi, lo, cl.fsel);
     return (t & 0x000F000Fu) | ((t >> 4) & 0x0F000F00u);
 }
 
@@ -177,13 +179,11 @@ __device__ __forceinline__ void code_words(const uint32_t (&ld)[4], const ChunkL
     } else if constexpr (K == 2) {
         // code bits 0..3 from the nibble word, bits 4..5 from the 2-bit fields
         const uint32_t w = sel(cl.odd, ld[1], ld[0]);
-        const uint32_t f = sel(cl.half, ld[3], ld[2]) >> cl.sh;
-        const uint32_t n = nibbles_to_bytes(f);
+        const uint32_t n = field_nibbles(ld[3], ld[2], cl);
         ev = ((w << 2) & 0x3C3C3C3Cu) | ((n << 6) & 0xC0C0C0C0u);
         od = ((w >> 2) & 0x3C3C3C3Cu) | ((n << 4) & 0xC0C0C0C0u);
     } else {
-        const uint32_t f = sel(cl.half, ld[1], ld[0]) >> cl.sh;
-        const uint32_t n = nibbles_to_bytes(f);
+        const uint32_t n = field_nibbles(ld[1], ld[0], cl);
         ev = (n << 6) & 0xC0C0C0C0u;
         od = (n << 4) & 0xC0C0C0C0u;
     }
@@ -431,8 +431,10 @@ __global__ __launch_bounds__(256, 3) void decode_alloc128_kernel(DecodeArgs a, U
     // column 8c + e
     ChunkLane cl;
     cl.odd = lane_mask(c & 1);
-    cl.half = lane_mask(c & 2);
-    cl.sh = static_cast<uint32_t>(16 * (c & 1));
+    {
+        const uint32_t b = 2u * static_cast<uint32_t>(c & 3);
+        cl.fsel = b * 0x00000101u + (b + 1u) * 0x01010000u;
+    }
     uint32_t lo4 = 0x0F0F0F0Fu;
     asm volatile("" : "+v"(lo4));
     float z[8][8];
