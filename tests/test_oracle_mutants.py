@@ -15,6 +15,7 @@ from tests import test_oracle_pins as pins
 from tests import test_oracle_alloc_pins as apins
 from tests import test_oracle_gate_pins as gpins
 from tests import test_oracle_refit_pins as rpins
+from tests import test_oracle_eq2_pins as epins
 
 SRC = Path(oracle_pkg.__file__).resolve().parent / "stq_oracle.c"
 ALLOC_SRC = Path(oracle_pkg.__file__).resolve().parent / "stq_alloc_oracle.c"
@@ -106,6 +107,9 @@ def _pin_cases():
         (gpins.test_gated_fp_step_one_hot, {}),
         (gpins.test_gated_impact_closed_form, {}),
         (gpins.test_gated_refit_uniform_gate_is_scalar, {}),
+        (epins.test_mixed_step_equals_eq2, {"d": 16, "n8": 8, "gated": False}),
+        (epins.test_mixed_step_equals_eq2, {"d": 32, "n8": 13, "gated": True}),
+        (epins.test_refit_step_equals_eq2, {"d": 32, "n8": 16}),
     ]
 
 
@@ -172,6 +176,8 @@ def _alloc_pin_cases():
         (apins.test_assignment_optimal_on_convex_instances, {"seed": 3}),
         (apins.test_assignment_budget_pivots_and_layout, {}),
         (apins.test_pivot_ranking_uses_the_nominal_width, {}),
+        (epins.test_ragged_step_equals_eq2, {"d": 16, "gated": False}),
+        (epins.test_ragged_step_equals_eq2, {"d": 64, "gated": True}),
     ]
 
 
@@ -190,3 +196,33 @@ def test_alloc_pins_catch_planted_mistake(tmp_path, name, old, new):
         except (AssertionError, ValueError, FloatingPointError, OverflowError):
             caught.append(fn.__name__)
     assert caught, f"no pin caught the planted mistake: {name}"
+
+
+# the update and readout mistakes above, each of which the pins against the
+# dense form of Eq. (2) must catch on their own (both gates, every format)
+UPDATE_MUTANTS = ["u transposed (S k instead of S^T k)", "sign of the delta correction",
+                  "gate dropped on S^T k", "gate dropped on S", "beta dropped",
+                  "readout with k instead of q", "wrong GQA map", "row gate dropped on S^T k",
+                  "row gate dropped on S", "row gate applied by column",
+                  "row gate read in reversed row order"]
+
+
+@pytest.mark.parametrize("name", UPDATE_MUTANTS)
+def test_eq2_pins_alone_catch_update_mistakes(tmp_path, name):
+    old, new = {m[0]: (m[1], m[2]) for m in MUTANTS}[name]
+    src = SRC.read_text()
+    assert src.count(old) >= 1, f"mutation site missing: {name}"
+    msrc = tmp_path / "mutant.c"
+    msrc.write_text(src.replace(old, new))
+    mut = oracle_pkg.Oracle(oracle_pkg.compile_oracle(msrc, tmp_path / "libmutant.so"))
+    caught = []
+    for fn, kw in ((epins.test_mixed_step_equals_eq2, {"d": 16, "n8": 8, "gated": False}),
+                   (epins.test_mixed_step_equals_eq2, {"d": 32, "n8": 13, "gated": True}),
+                   (epins.test_refit_step_equals_eq2, {"d": 32, "n8": 16}),
+                   (epins.test_ragged_step_equals_eq2, {"d": 64, "gated": True}),
+                   (epins.test_ragged_step_equals_eq2, {"d": 16, "gated": False})):
+        try:
+            fn(mut, **kw)
+        except (AssertionError, ValueError, FloatingPointError, OverflowError):
+            caught.append(fn.__name__)
+    assert caught, f"the Eq. (2) pins missed: {name}"
