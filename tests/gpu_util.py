@@ -62,8 +62,31 @@ def _empty8(B, hv, d):
     return np.zeros((B, hv, 0, d), np.int8)
 
 
-def compare_step(gpu: dict, ref: dict, *, n8: int, d: int, label: str = "") -> dict:
-    """Per-step parity against the oracle; returns statistics, raises on failure."""
+# With the oracle's exact code values at hand, a code may differ from the
+# oracle's only where that value lies this close to a rounding boundary: the
+# kernel evaluates it in fp32 (|t| <= 127, a few roundings and a 1-ulp
+# reciprocal), well within 32 ulps of |t|.
+TIE_WINDOW = 2.0 ** -12
+
+
+def exact_code_values(X, r, c, perm):
+    """t = X / (r' c) per stored code, physical rows [B][Hv][d][d]: X the
+    oracle's updated state (logical rows), r the new row factors (physical
+    rows), c the column factors per head [Hv][d] or per state [B][Hv][d]."""
+    B, hv = r.shape[:2]
+    Xp = np.take_along_axis(X, perm[None, :, :, None], axis=2)
+    cc = c.astype(np.float64)
+    cc = cc[None, :, None, :] if cc.ndim == 2 else cc[:, :, None, :]
+    return Xp / (r.astype(np.float64)[..., None] * cc)
+
+
+def compare_step(gpu: dict, ref: dict, *, n8: int, d: int, label: str = "",
+                 t_exact=None) -> dict:
+    """Per-step parity against the oracle; returns statistics, raises on failure.
+    With t_exact (exact_code_values of the oracle's step), every code that
+    differs must sit within TIE_WINDOW of a rounding boundary, in place of
+    the bar on the share of identical codes (for inputs whose values cluster
+    at ties)."""
     B, hv = ref["r"].shape[:2]
     g8 = gpu["pool8"] if gpu["pool8"] is not None else _empty8(B, hv, d)
     g4 = gpu["pool4"] if gpu["pool4"] is not None else np.zeros((B, hv, 0, d // 2), np.uint8)
@@ -83,7 +106,13 @@ def compare_step(gpu: dict, ref: dict, *, n8: int, d: int, label: str = "") -> d
     stats = dict(code_match=match, max_code_diff=max_code, max_r_rel=max_r, max_o_rel_l2=max_o,
                  n_codes=int(diff.size))
     assert np.all(np.isfinite(gpu["o"])), f"{label}: non-finite readout"
-    assert match >= CODE_MATCH_MIN, f"{label}: codes identical {match:.6f} < {CODE_MATCH_MIN} {stats}"
+    if t_exact is None:
+        assert match >= CODE_MATCH_MIN, f"{label}: codes identical {match:.6f} < {CODE_MATCH_MIN} {stats}"
+    else:
+        t = t_exact[diff != 0]
+        off = np.abs(t - np.floor(t) - 0.5) if t.size else np.zeros(1)
+        stats["max_tie_offset"] = float(off.max())
+        assert off.max() <= TIE_WINDOW, f"{label}: a code differs away from a tie {stats}"
     assert max_code <= 1, f"{label}: code differs by {max_code} {stats}"
     assert max_r <= R_RTOL, f"{label}: row factor rel diff {max_r:.3g} {stats}"
     assert max_o <= O_REL_L2, f"{label}: readout rel L2 {max_o:.3g} {stats}"

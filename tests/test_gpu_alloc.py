@@ -59,17 +59,26 @@ def _load(st, pool, r, cs=None):
 
 
 def _compare(gpu_pool, gpu_r, ref_pool, ref_r, counts, d, label, *, o=None, ref_o=None,
-             pivot_err=None):
+             pivot_err=None, t_exact=None):
     """pivot_err (optional, [B][Hv][d][d] in physical row order): an absolute
     allowance added to the one-ulp bar of each pivot value, for values formed
     by cancellation, where the fp32 evaluation error of the terms exceeds
-    half an ulp of the binary16 result."""
+    half an ulp of the binary16 result.  t_exact (optional, the oracle's exact
+    code values in physical rows): a differing integer code must then sit
+    within gu.TIE_WINDOW of a rounding boundary, in place of the bar on the
+    share of identical codes."""
     zg, hg, cls = wl.unpack_ragged(gpu_pool, counts, d)
     zr, hr, _ = wl.unpack_ragged(ref_pool, counts, d)
     ints = np.broadcast_to(cls[None, :, :, None] != 0, zg.shape)
     diff = np.abs(zg - zr)[ints]
     match = float(np.mean(diff == 0)) if diff.size else 1.0
-    assert match >= gu.CODE_MATCH_MIN, f"{label}: codes identical {match:.6f}"
+    if t_exact is None:
+        assert match >= gu.CODE_MATCH_MIN, f"{label}: codes identical {match:.6f}"
+    else:
+        t = np.broadcast_to(t_exact, zg.shape)[ints][diff != 0]
+        off = np.abs(t - np.floor(t) - 0.5)
+        assert off.size == 0 or off.max() <= gu.TIE_WINDOW, \
+            f"{label}: a code differs away from a tie ({off.max():.3g}, match {match:.6f})"
     assert diff.size == 0 or diff.max() <= 1, f"{label}: code differs by {diff.max()}"
     piv = cls[None] == 0
     rows_int = np.broadcast_to(~piv, gpu_r.shape)
@@ -218,6 +227,39 @@ def test_alloc_trajectory_per_step(oracle_mod):
         _compare(st.pool.cpu().numpy(), st.r.cpu().numpy(), ref["pool"], ref["r"], counts, d,
                  f"t={t}", o=o.cpu().numpy(), ref_o=ref["o"])
         pool, r = ref["pool"], ref["r"]
+
+
+@pytest.mark.parametrize("d,gated", [(128, False), (128, True), (64, False)])
+def test_alloc_step_parity_sparse_keys(oracle_mod, d, gated):
+    """Keys with about a quarter of their entries exactly zero: rows whose
+    b k_i vanishes (pivot and integer rows alike) take the other form of the
+    update inside units whose other rows take the usual one."""
+    from tests.test_gpu_parity import _sparse_keys
+
+    B, hv, hk = 5, 8, 4
+    print(f"[case] ragged sparse keys d={d} gated={gated}", flush=True)
+    counts, perm, c, S = _setup(4030, B, hv, d, pivots=3)
+    st = _state(B, hv, hk, d, counts, c, perm)
+    pool, r = oracle_mod.alloc_pack(S.astype(np.float64), counts, perm, c, st.slot_bytes)
+    _load(st, pool, r)
+    x = _sparse_keys(wl.draw_inputs(B, hk, hv, d, dtype="bf16", seed=4030, step=0), 4031 + d)
+    assert np.any(x.k == 0.0)
+    q, k, v, a, b = gu.inputs_to_device(x)
+    if gated:
+        gate = wl.draw_gate(B, hv, d, seed=4030, step=0)
+        o = st.decode_step_gated(q, k, v, gu.dev(gate), b)
+        ref = oracle_mod.alloc_step(pool, r, counts, perm, x.q, x.k, x.v, None, x.beta, c=c,
+                                    gate=gate, want_X=True)
+    else:
+        o = st.decode_step(q, k, v, a, b)
+        ref = oracle_mod.alloc_step(pool, r, counts, perm, x.q, x.k, x.v, x.alpha, x.beta, c=c,
+                                    want_X=True)
+    torch.cuda.synchronize()
+    # rows with k_i = 0 are only rescaled: their code values cluster at halves
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = gu.exact_code_values(ref["X"], ref["r"], c, perm)  # (inf on pivot rows: unused)
+    print(_compare(st.pool.cpu().numpy(), st.r.cpu().numpy(), ref["pool"], ref["r"], counts, d,
+                   f"sparse keys d={d}", o=o.cpu().numpy(), ref_o=ref["o"], t_exact=t))
 
 
 @pytest.mark.parametrize("d,gated", [(128, False), (64, True)])

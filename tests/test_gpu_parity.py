@@ -106,6 +106,40 @@ def test_zero_state_first_step(oracle_mod):
     print(gu.compare_step(dict(pool8=p8, pool4=p4, r=r, o=o), ref, n8=n8, d=d))
 
 
+def _sparse_keys(x: wl.StepInputs, seed: int, frac: float = 0.25) -> wl.StepInputs:
+    """The same inputs with about `frac` of the key entries exactly zero."""
+    import dataclasses
+
+    zero = wl.rng_for(seed, 77).random(x.k.shape) < frac
+    k = np.where(zero, np.float32(0.0), x.k).astype(np.float32)
+    kb = None if x.k_bits is None else np.where(zero, 0, x.k_bits).astype(x.k_bits.dtype)
+    return dataclasses.replace(x, k=k, k_bits=kb)
+
+
+@pytest.mark.parametrize("d,n8,dtype", [(128, 64, "bf16"), (128, 40, "f32"), (64, 32, "bf16"),
+                                        (32, 13, "f32")])
+def test_step_parity_sparse_keys(oracle_mod, d, n8, dtype):
+    """Keys with exact zeros: a row whose b k_i vanishes takes the other form
+    of the update (no delta write, the decayed row alone), inside units
+    whose other rows take the usual one."""
+    B, hv, hk = 6, 8, 4
+    print(f"[case] sparse keys d={d} n8={n8} {dtype}", flush=True)
+    ps = wl.random_packed_state(B, hv, d, n8, seed=1300 + d + n8)
+    x = _sparse_keys(wl.draw_inputs(B, hk, hv, d, dtype=dtype, seed=1301, step=0), 1302 + d)
+    assert np.any(x.k == 0.0) and np.any(x.k != 0.0)
+    st = gu.make_state(B, hv, hk, d, n8)
+    gu.load_packed(st, ps)
+    o = gu.gpu_step(st, x)
+    p8, p4, r = gu.read_packed(st)
+    ref = oracle_mod.step(ps.pool8, ps.pool4, ps.r, ps.c, ps.perm, x.q, x.k, x.v, x.alpha,
+                          x.beta, n8=n8, nthreads=8, want_X=True)
+    # a row with k_i = 0 is only rescaled, so where its codes do not span
+    # the range its new code values cluster at halves: the tie-aware check
+    t = gu.exact_code_values(ref["X"], ref["r"], ps.c, ps.perm)
+    print(gu.compare_step(dict(pool8=p8, pool4=p4, r=r, o=o), ref, n8=n8, d=d,
+                          label=f"sparse keys d={d} n8={n8}", t_exact=t))
+
+
 @pytest.mark.parametrize("d,n8,hv,hk", [(64, 32, 4, 2), (128, 64, 8, 4), (128, 16, 32, 16)])
 def test_slot_mapping_and_untouched_slots(oracle_mod, d, n8, hv, hk):
     """A batch addressing a permuted subset of slots updates exactly those

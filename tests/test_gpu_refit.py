@@ -135,6 +135,36 @@ def test_refit_step_parity(oracle_mod, d, n8, dtype):
     print(stats)
 
 
+@pytest.mark.parametrize("d,n8", [(128, 64), (64, 32)])
+def test_refit_step_parity_sparse_keys(oracle_mod, d, n8):
+    """Keys with exact zeros (rows whose b k_i vanishes keep their decayed
+    value alone) in the refit format, column factors included."""
+    from tests.test_gpu_parity import _sparse_keys
+
+    B, hv, hk = 5, 8, 4
+    print(f"[case] refit sparse keys d={d} n8={n8}", flush=True)
+    g = wl.rng_for(804, n8)
+    c, perm, w2 = _calibration(g, hv, d)
+    S = wl.random_states(B, hv, d, seed=804 + n8, outlier_sigma=1.0)
+    P8, P4, R, CS = oracle_mod.pack_refit(S, c, perm, w2, n8=n8)
+    st = _refit_state(B, hv, hk, d, n8, c, perm, w2)
+    _load(st, P8, P4, R, CS)
+    x = _sparse_keys(wl.draw_inputs(B, hk, hv, d, dtype="bf16", seed=804, step=0), 805 + d)
+    assert np.any(x.k == 0.0)
+    o = gu.gpu_step(st, x)
+    p8, p4, r = gu.read_packed(st)
+    cs = st.cs.cpu().numpy()
+    ref = oracle_mod.step_refit(P8, P4, R, CS, perm, w2, x.q, x.k, x.v, x.alpha, x.beta, n8=n8,
+                                want_X=True)
+    t = gu.exact_code_values(ref["X"], ref["r"], CS, perm)
+    stats = gu.compare_step(dict(pool8=p8, pool4=p4, r=r, o=o), ref, n8=n8, d=d,
+                            label=f"refit sparse keys n8={n8}", t_exact=t)
+    stats["max_cs_rel"] = _compare_cs(
+        cs, ref["cs"], f"refit sparse keys n8={n8}", X=ref["X"], z=wl.unpack_codes(p8, p4),
+        zref=wl.unpack_codes(ref["pool8"], ref["pool4"]), r=r, perm=perm, w2=w2, cs_old=CS)
+    print(stats)
+
+
 def test_refit_dequant_parity(oracle_mod):
     B, hv, hk, d, n8 = 3, 4, 2, 64, 32
     g = wl.rng_for(803, 0)
