@@ -69,7 +69,7 @@ struct Smem {
     float2 row[D];          // {P, byte offset of E in ez} per physical row
     float srow[D + 8];      // s of row p at p + p / 16
     float w2row[D + 8];     // column refit: w2 of row p at p + p / 16
-    float v[D], c[D];
+    float vc[D], c[D];      // v / c and c per column
     float ez[2 * D];        // e, then a zero vector; each as [e/4][c][e%4]
     float4 red[4][8][2][16]; // per wave, column offset e, lane group, chunk c
     float kq[2];
@@ -263,7 +263,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
     // kept for o.  Lane t takes column 8 cc + ce, cc = t % 16, with ce =
     // (t / 16) % 8 rotated by 2 (cc / 4): the 16 lanes of a row group still
     // read 16 different chunks of the sums, and the 32 lanes of a half wave
-    // read v and c from 32 different banks
+    // read v / c and c from 32 different banks
     const int cc = t & 15;
     const int ce = ((t >> 4) + ((t >> 1) & 6)) & 7;
     const int jcol = 8 * cc + ce;
@@ -278,9 +278,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
             const float4 f = sh.red[ww][ce][0][cc];
             u += (f.x + f.y) + f.z;
         }
-        // v / c to within a hair of correct rounding: a row whose update nearly
-        // cancels its decayed content amplifies any rounding of e
-        sh.ez[ezi] = __builtin_fmaf(-L.alpha, u, div_refined(sh.v[jcol], sh.c[jcol]));
+        sh.ez[ezi] = __builtin_fmaf(-L.alpha, u, sh.vc[jcol]);
     } else {
         const float4 f0 = sh.red[0][ce][1][cc];
         wsum = (f0.x + f0.y) + f0.z;
@@ -580,7 +578,10 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, UnitGeom u
         // of the code loads instead of sinking them into the branch above)
         asm volatile("" ::"v"(praw), "v"(rpv));
         const int j = tl;
-        sh.v[j] = In<TIn>::cvt(x0);
+        // v / c to within a hair of correct rounding (a row whose update
+        // nearly cancels its decayed content amplifies any rounding of e),
+        // formed here, where these waves wait for the staging of the others
+        sh.vc[j] = div_refined(In<TIn>::cvt(x0), __uint_as_float(x1));
         sh.c[j] = __uint_as_float(x1);
         sh.ez[D + j] = 0.0f;
     }
