@@ -287,8 +287,12 @@ __global__ __launch_bounds__(256, 3) void decode_alloc128_kernel(DecodeArgs a, U
     // writes it during the step, and so it comes through the scalar cache,
     // where the workgroups of a head find it, instead of a vector load whose
     // latency would delay every row address
-    typedef __attribute__((address_space(4))) const int32_t cint32_t;
-    cint32_t *lay = (cint32_t *)(reinterpret_cast<uintptr_t>(a.layout) + static_cast<size_t>(h) * kLayoutStride * 4);
+    // (the whole row in one scalar load: the class counts and the segment
+    // offset, both needed before the first row address, in one round trip)
+    static_assert(kLayoutStride == 8 && kLayoutSegOff < 8, "one layout row is eight words");
+    typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(4))) const i32x8 ci32x8;
+    const i32x8 lay = *(ci32x8 *)(reinterpret_cast<uintptr_t>(a.layout) + static_cast<size_t>(h) * kLayoutStride * 4);
     Bounds L;
     {
         const int n0 = lay[0], n1 = lay[1], n2 = lay[2], n3 = lay[3];
