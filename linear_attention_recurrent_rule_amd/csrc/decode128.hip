@@ -73,7 +73,6 @@ struct Smem {
     float ez[2 * D];        // e, then a zero vector; each as [e/4][c][e%4]
     float4 red[4][8][2][16]; // per wave, column offset e, lane group, chunk c
     float kq[2];
-    float mul[16][8];       // per row group: code multipliers of its 8 rows
     float ra[16][8], rb[16][8]; // column refit: w2 r' s and w2 r'^2 per row
 };
 
@@ -317,6 +316,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
     }
     const uint32_t mk[3] = {lane_mask(c & 8), lane_mask(c & 4), lane_mask(c & 2)};
     const float rmax = row_max_scatter(amax, mk);
+    float mulv[8];
     {
         const int mm = c >> 1;
         const int p = g + 16 * mm;
@@ -332,28 +332,32 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs &a, Smem &sh, const
         mul = fminf(fmaxf(mul, -kMulMax), kMulMax);
         if ((c & 1) == 0) {
             L.rw[p] = rn;
-            sh.mul[g][mm] = mul;
             if (REFIT) {
                 const float w2 = sh.w2row[si];
                 sh.ra[g][mm] = (w2 * rn) * sc;
                 sh.rb[g][mm] = (w2 * rn) * rn;
             }
         }
+        // every lane of the row group takes the 8 multipliers of its rows
+        // from the lanes that formed them (row m in lanes 2m and 2m + 1)
+        mulv[0] = row_bcast<0>(mul);
+        mulv[1] = row_bcast<2>(mul);
+        mulv[2] = row_bcast<4>(mul);
+        mulv[3] = row_bcast<6>(mul);
+        mulv[4] = row_bcast<8>(mul);
+        mulv[5] = row_bcast<10>(mul);
+        mulv[6] = row_bcast<12>(mul);
+        mulv[7] = row_bcast<14>(mul);
     }
-    // the multipliers of a row group are written and read by the 16 lanes of
-    // that group, inside one wave: a wave-level fence suffices
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (REFIT) {
+        // the refit factors of a row group are written and read by the 16
+        // lanes of that group, inside one wave: a wave-level fence suffices
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
 
     // ---- Table C2 step 6: codes against the stored factors, pack, write back
-    float mulv[8];
-    {
-        const float4 m0 = *reinterpret_cast<const float4 *>(&sh.mul[g][0]);
-        const float4 m1 = *reinterpret_cast<const float4 *>(&sh.mul[g][4]);
-        mulv[0] = m0.x; mulv[1] = m0.y; mulv[2] = m0.z; mulv[3] = m0.w;
-        mulv[4] = m1.x; mulv[5] = m1.y; mulv[6] = m1.z; mulv[7] = m1.w;
-    }
     // column refit partial sums over this lane's 8 rows (REFIT): with
     // x = s y, X = c x and v = r' z', sum_i w2 v X = c sum_i (w2 r' s) z' y
     // and sum_i w2 v^2 = sum_i (w2 r'^2) z'^2

@@ -133,6 +133,12 @@ constexpr int kQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int kQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
 constexpr int kRowMirror = 0x140;     // lane l <- lane 15-l within the row
 
+// The value held by lane N of this lane's 16-lane row (DPP row_newbcast).
+template <int N> __device__ __forceinline__ float row_bcast(float v) {
+    static_assert(N >= 0 && N < 16, "a row has 16 lanes");
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + N, 0xF, 0xF, false));
+}
+
 // Sum over the 64 lanes of a wave (valid in every lane).
 __device__ __forceinline__ float wave_sum(float v) {
     v += dppf<kQuadXor1>(v);
