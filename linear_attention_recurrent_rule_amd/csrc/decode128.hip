@@ -33,8 +33,8 @@
 //    the lane picks e or a zero vector per row by its LDS address;
 //  * the row absmax over the 16 lanes of a row is a DPP reduce-scatter that
 //    leaves row c / 2 in lane c, so each lane derives one row factor and its
-//    reciprocal, and the 8 multipliers are exchanged through LDS inside the
-//    wave (a wave-level fence, no workgroup barrier);
+//    reciprocal, and each lane takes the 8 multipliers of its rows from the
+//    lanes that formed them by DPP row broadcasts (no LDS, no barrier);
 //  * codes: one FMA adds 1.5 * 2^23 (round-half-even to an integer in the low
 //    mantissa bits), then bytes are gathered with v_perm and nibbles with one
 //    shift and one bit-field insert per 8 codes;
