@@ -269,12 +269,25 @@ __global__ __launch_bounds__(256, 3) void decode_alloc128_kernel(DecodeArgs a, U
     const int gl = (t >> 4) & 3;
     const int wv = __builtin_amdgcn_readfirstlane(w);
 
-    const unsigned unit = unit_of_block(ug.remap);
+    const unsigned unit = unit_of_block(ug);
     const int Hv = a.Hv;
     const int b = static_cast<int>(udiv(unit, static_cast<unsigned>(Hv), ug.hv_m));
     const int h = static_cast<int>(unit - static_cast<unsigned>(b) * static_cast<unsigned>(Hv));
     const int hk = static_cast<int>(udiv(static_cast<unsigned>(h), static_cast<unsigned>(ug.G), ug.g_m));
-    const int slot = a.slots ? a.slots[b] : b;
+    // the head's layout, read through the constant address space: nothing
+    // writes it during the step, and so it comes through the scalar cache,
+    // where the workgroups of a head find it, instead of a vector load whose
+    // latency would delay every row address
+    // (the whole row in one scalar load: the class counts and the segment
+    // offset, both needed before the first row address, in one round trip,
+    // issued with the slot's load, on which it does not depend)
+    static_assert(kLayoutStride == 8 && kLayoutSegOff < 8, "one layout row is eight words");
+    typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(4))) const i32x8 ci32x8;
+    const i32x8 lay = *(ci32x8 *)(reinterpret_cast<uintptr_t>(a.layout) + static_cast<size_t>(h) * kLayoutStride * 4);
+    const int slot = slot_of(a, b);
+    prefetch_args(a);
+    asm volatile("" ::"s"(a.slot_bytes), "s"(a.pool8)); // (as above)
     if (slot < 0 || slot >= a.n_slots) { // whole workgroup leaves together
         if (t < D) store_o(a, static_cast<size_t>(unit) * D + t, __int_as_float(0x7fc00000));
         return;
@@ -283,16 +296,6 @@ __global__ __launch_bounds__(256, 3) void decode_alloc128_kernel(DecodeArgs a, U
     const float beta = a.beta[unit];
     const size_t ub = static_cast<size_t>(slot) * Hv + h;
 
-    // the head's layout, read through the constant address space: nothing
-    // writes it during the step, and so it comes through the scalar cache,
-    // where the workgroups of a head find it, instead of a vector load whose
-    // latency would delay every row address
-    // (the whole row in one scalar load: the class counts and the segment
-    // offset, both needed before the first row address, in one round trip)
-    static_assert(kLayoutStride == 8 && kLayoutSegOff < 8, "one layout row is eight words");
-    typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
-    typedef __attribute__((address_space(4))) const i32x8 ci32x8;
-    const i32x8 lay = *(ci32x8 *)(reinterpret_cast<uintptr_t>(a.layout) + static_cast<size_t>(h) * kLayoutStride * 4);
     Bounds L;
     {
         const int n0 = lay[0], n1 = lay[1], n2 = lay[2], n3 = lay[3];

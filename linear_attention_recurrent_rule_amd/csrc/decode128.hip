@@ -465,13 +465,14 @@ __global__ __launch_bounds__(256) void decode128_kernel(DecodeArgs a, UnitGeom u
     L.c = L.t & 15;
     L.g = L.t >> 4;
     const int t = L.t;
-    const unsigned unit = unit_of_block(ug.remap);
+    const unsigned unit = unit_of_block(ug);
     L.unit = unit;
     const int Hv = a.Hv;
     const int b = static_cast<int>(udiv(unit, static_cast<unsigned>(Hv), ug.hv_m));
     const int h = static_cast<int>(unit - static_cast<unsigned>(b) * static_cast<unsigned>(Hv));
     const int hk = static_cast<int>(udiv(static_cast<unsigned>(h), static_cast<unsigned>(ug.G), ug.g_m));
-    const int slot = a.slots ? a.slots[b] : b;
+    const int slot = slot_of(a, b);
+    prefetch_args(a);
     if (slot < 0 || slot >= a.n_slots) { // whole workgroup leaves together
         if (t < D) store_o(a, static_cast<size_t>(unit) * D + t, __int_as_float(0x7fc00000));
         return;

@@ -210,34 +210,24 @@ __device__ __forceinline__ f32x4 column_sums(const u32x4 (&a)[2], const f32x4 (&
 // n / d for a wave-uniform n < 2^31, with m = ceil(2^32 / d) (d >= 2) or
 // m = 0 (d = 1): hi(n m) is the quotient or one more.
 __device__ __forceinline__ unsigned udiv(unsigned n, unsigned d, unsigned m) {
-    if (m == 0) return n;
-    unsigned q = __umulhi(n, m);
-    if (q * d > n) --q;
-    return q;
+    // (selects, not branches: the unit's first scalar loads then stay in one
+    // block and issue together)
+    const unsigned q = m == 0 ? n : __umulhi(n, m);
+    return q * d > n ? q - 1 : q;
 }
 
 inline unsigned div_magic(unsigned d) {
     return d <= 1 ? 0u : static_cast<unsigned>(((1ull << 32) + d - 1) / d);
 }
 
-// Workgroups are dealt round-robin to the 8 XCDs; with remap each XCD gets a
-// contiguous range of units, so value heads sharing a key head (and their
-// q, k) meet in the same L2.
-__device__ __forceinline__ unsigned unit_of_block(int xcd_remap) {
-    unsigned unit = blockIdx.x;
-    if (xcd_remap) {
-        const unsigned per = gridDim.x >> 3;
-        unit = (blockIdx.x & 7u) * per + (blockIdx.x >> 3);
-    }
-    return unit;
-}
-
-// Unit geometry computed once on the host: the divisors of the unit index.
+// Unit geometry computed once on the host: the divisors of the unit index
+// and the XCD remap.
 struct UnitGeom {
     unsigned hv_m; // div_magic(Hv)
     int G;         // value heads per key head
     unsigned g_m;  // div_magic(G)
     int remap;     // xcd remap on
+    unsigned per;  // units per XCD under the remap (units / 8)
 };
 
 inline UnitGeom unit_geom(const DecodeArgs &a) {
@@ -247,7 +237,37 @@ inline UnitGeom unit_geom(const DecodeArgs &a) {
     u.G = a.Hv / a.Hk;
     u.g_m = div_magic(static_cast<unsigned>(u.G));
     u.remap = (units % 8u) == 0u ? 1 : 0;
+    u.per = units >> 3;
     return u;
+}
+
+// Workgroups are dealt round-robin to the 8 XCDs; with remap each XCD gets a
+// contiguous range of units, so value heads sharing a key head (and their
+// q, k) meet in the same L2.  (The grid size comes from the host, so no
+// scalar load of the launch's dimensions precedes the first address.)
+__device__ __forceinline__ unsigned unit_of_block(const UnitGeom &ug) {
+    const unsigned x = blockIdx.x;
+    return ug.remap ? (x & 7u) * ug.per + (x >> 3) : x;
+}
+
+// The state slot of sequence b: slots[b], or b when slots is null.  The load
+// is made in either case (from the first word of q, which every decode
+// reads, when slots is null), so that it issues with the unit's other scalar
+// loads instead of behind a branch.
+__device__ __forceinline__ int slot_of(const DecodeArgs &a, int b) {
+    const int32_t *sp = a.slots ? a.slots + b : static_cast<const int32_t *>(a.q);
+    const int v = *sp;
+    return a.slots ? v : b;
+}
+
+// The decode arguments that the first addresses of a unit need, read into
+// scalar registers together with the slot index: otherwise some are loaded
+// only after the test of the slot, one more scalar round trip before the
+// first row address.  (Placed after the slot's load: a volatile statement
+// ahead of it would make that load a vector-memory one.)
+__device__ __forceinline__ void prefetch_args(const DecodeArgs &a) {
+    asm volatile("" ::"s"(a.pool8), "s"(a.pool4), "s"(a.r), "s"(a.perm), "s"(a.c), "s"(a.q), "s"(a.k),
+                 "s"(a.v), "s"(a.beta), "s"(a.n_slots));
 }
 
 // ---- packing of requantized codes.  bt[e] holds fl32(y_e mul + 1.5 * 2^23),
