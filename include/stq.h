@@ -135,7 +135,9 @@ typedef struct {
                            logical rows (1 until calibrated) */
     double *impact;     /* [Hv][dk]  REFIT calibration: accumulated row impact */
     int32_t *layout;    /* [Hv][8]  ALLOC: class counts [0..4], segment offset
-                           [5] and segment bytes [6] of each head */
+                           [5] and segment bytes [6] of each head; followed by
+                           [Hv][64] words the library derives from them (the
+                           d = 128 decode's per-slot row-chunk descriptors) */
     double *dist;       /* [Hv][dk][5]  ALLOC calibration: candidate distortions */
     double *logret;     /* [Hv][dk]  ALLOC calibration: summed log retention */
     double *nret;       /* [Hv]  ALLOC calibration: retention samples */
@@ -429,7 +431,9 @@ const char *stq_status_str(int32_t status);
 /* Library ABI version (bumped on any change to the declarations above):
  * 2 since the REFIT format and its state fields; 3 since the per-key-row
  * gate entry points; 4 since the ALLOC formats (descriptor and state fields,
- * retention and assignment entry points); 5 since STQ_OUT_BF16 (o is void *). */
+ * retention and assignment entry points); 5 since STQ_OUT_BF16 (o is void *);
+ * 6 since stq_calibrate_static; 7 since an ALLOC state's layout buffer also
+ * holds the per-slot descriptors (its stq_state_bytes grows by 256 B a head). */
 int32_t stq_abi_version(void);
 
 #ifdef __cplusplus

@@ -285,6 +285,16 @@ __global__ __launch_bounds__(256, 3) void decode_alloc128_kernel(DecodeArgs a, U
     typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
     typedef __attribute__((address_space(4))) const i32x8 ci32x8;
     const i32x8 lay = *(ci32x8 *)(reinterpret_cast<uintptr_t>(a.layout) + static_cast<size_t>(h) * kLayoutStride * 4);
+    // and this wave's eight slot descriptors (row base, row bytes, class and
+    // the lane's chunk offsets of each slot), written with the layout
+    static_assert(kSlotDescWords == 4 * 16, "16 descriptor words per wave");
+    typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+    typedef __attribute__((address_space(4))) const i32x16 ci32x16;
+    i32x16 sd = {};
+    if constexpr (!REFIT)
+        sd = *(ci32x16 *)(reinterpret_cast<uintptr_t>(a.layout) +
+                          (static_cast<size_t>(Hv) * kLayoutStride + static_cast<size_t>(h) * kSlotDescWords +
+                           16u * static_cast<unsigned>(wv)) * 4);
     const int slot = slot_of(a, b);
     prefetch_args(a);
     asm volatile("" ::"s"(a.slot_bytes), "s"(a.pool8)); // (as above)
@@ -354,24 +364,66 @@ __global__ __launch_bounds__(256, 3) void decode_alloc128_kernel(DecodeArgs a, U
         x1 = cp0[tl];
     }
 
-    // ---- Table C2 step 1: issue the loads of this lane's row chunks (their
-    // addresses are the first use of the head's layout)
-    const unsigned tab = slot_table(L, wv, t);
+    // ---- Table C2 step 1: issue the loads of this lane's row chunks.  A slot
+    // whose rows share a class (almost all) takes its addresses from its
+    // descriptor with no branch on the class; a slot straddling a class
+    // boundary takes the per-lane path
+    // (the refit instances keep the per-slot class dispatch: their register
+    // budget is spent, and the descriptors' scalar registers cost them spills)
+    const unsigned c2 = 2u * static_cast<unsigned>(c);
     uint32_t ld[8][4]; // per slot: A.x, A.y, B.x, B.y
+    unsigned tab = 0u;
+    if constexpr (REFIT) {
+        tab = slot_table(L, wv, t);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            unsigned offA = 0u, offB = 0u;
+            per_slot(L, tab, g, m, [&](auto KC) __attribute__((always_inline)) {
+                constexpr int K = decltype(KC)::value;
+                chunk_offsets<K>(static_cast<unsigned>(slot_base<K>(L, m) + g * Cls<K>::row), c, offA,
+                                 offB);
+            });
+            const u32x2 A = *reinterpret_cast<const u32x2 *>(seg_in + offA);
+            const u32x2 Bw = *reinterpret_cast<const u32x2 *>(seg_in + offB);
+            ld[m][0] = A[0];
+            ld[m][1] = A[1];
+            ld[m][2] = Bw[0];
+            ld[m][3] = Bw[1];
+        }
+    } else {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
+        const int P = sd[2 * m + 1];
         unsigned offA = 0u, offB = 0u;
-        per_slot(L, tab, g, m, [&](auto KC) __attribute__((always_inline)) {
-            constexpr int K = decltype(KC)::value;
-            chunk_offsets<K>(static_cast<unsigned>(slot_base<K>(L, m) + g * Cls<K>::row), c, offA,
-                             offB);
-        });
+        if (__builtin_expect(P >= 0, 1)) {
+            const unsigned rb = static_cast<unsigned>(P) & 0x1FFu;
+            const unsigned shA = (static_cast<unsigned>(P) >> 16) & 15u;
+            const unsigned shB = (static_cast<unsigned>(P) >> 20) & 15u;
+            const unsigned ob = (static_cast<unsigned>(P) >> 24) & 0x7Fu;
+            const unsigned row = static_cast<unsigned>(sd[2 * m]) + static_cast<unsigned>(g) * rb;
+            offA = row + ((c2 >> shA) << 3);
+            offB = row + ob + ((c2 >> shB) << 3);
+        } else {
+            with_class(class_of(L, g + 16 * m), [&](auto KC) __attribute__((always_inline)) {
+                constexpr int K = decltype(KC)::value;
+                chunk_offsets<K>(static_cast<unsigned>(slot_base<K>(L, m) + g * Cls<K>::row), c, offA,
+                                 offB);
+            });
+        }
         const u32x2 A = *reinterpret_cast<const u32x2 *>(seg_in + offA);
         const u32x2 Bw = *reinterpret_cast<const u32x2 *>(seg_in + offB);
         ld[m][0] = A[0];
         ld[m][1] = A[1];
         ld[m][2] = Bw[0];
         ld[m][3] = Bw[1];
+    }
+    // the class of each slot's four rows (4 bits per slot, 7 where they
+    // straddle a class boundary), for the class branches below
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int P = sd[2 * m + 1];
+        tab |= (P < 0 ? 7u : (static_cast<unsigned>(P) >> 9) & 7u) << (4 * m);
+    }
     }
 
     // ---- per-row and per-column factors, once per unit

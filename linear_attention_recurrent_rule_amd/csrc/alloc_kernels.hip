@@ -706,6 +706,9 @@ __global__ void alloc_init_layout_kernel(int32_t *layout, int Hv, int D, int k, 
     l[k] = D;
     l[kLayoutSegOff] = h * seg;
     l[kLayoutSegBytes] = seg;
+    int32_t *desc = layout + static_cast<size_t>(Hv) * kLayoutStride + static_cast<size_t>(h) * kSlotDescWords;
+    for (int t = 0; t < kSlotDescWords; ++t) desc[t] = 0;
+    if (D == 128) slot_descs_128(l, desc);
 }
 
 } // namespace

@@ -63,8 +63,9 @@ int64_t alloc_slot_bytes(const stq_desc *d) {
     return (bytes + 15) / 16 * 16;
 }
 
-// Layout table rows from class counts [Hv][5]; false if a head's counts are
-// invalid or the segments do not fit slot_bytes (sets *space).
+// Layout table rows from class counts [Hv][5], then the per-slot load
+// descriptors of each head; false if a head's counts are invalid or the
+// segments do not fit slot_bytes (sets *space).
 bool build_layout(const stq_desc *d, int64_t slot_bytes, const int32_t *counts, int32_t *table,
                   bool *space) {
     const int H = d->n_heads_v, D = d->d_k;
@@ -85,6 +86,10 @@ bool build_layout(const stq_desc *d, int64_t slot_bytes, const int32_t *counts, 
         for (int k = 0; k < stq::kNumClasses; ++k) row[k] = counts[h * stq::kNumClasses + k];
         row[stq::kLayoutSegOff] = static_cast<int32_t>(off);
         row[stq::kLayoutSegBytes] = static_cast<int32_t>(seg);
+        int32_t *desc = table + static_cast<size_t>(H) * stq::kLayoutStride +
+                        static_cast<size_t>(h) * stq::kSlotDescWords;
+        for (int t = 0; t < stq::kSlotDescWords; ++t) desc[t] = 0;
+        if (D == 128) stq::slot_descs_128(row, desc);
         off += seg;
     }
     if (off > slot_bytes) {
@@ -117,7 +122,7 @@ stq_status describe(const stq_desc *d, Layout *L) {
         L->slot_bytes = alloc_slot_bytes(d);
         L->pool8 = S * static_cast<size_t>(L->slot_bytes);
         L->r = S * H * D * sizeof(float);
-        L->layout = H * stq::kLayoutStride * sizeof(int32_t);
+        L->layout = H * stq::kLayoutWordsPerHead * sizeof(int32_t);
         L->dist = H * D * stq::kNumClasses * sizeof(double);
         L->logret = H * D * sizeof(double);
         L->nret = H * sizeof(double);
@@ -181,7 +186,7 @@ stq_status dev(hipError_t e) { return e == hipSuccess ? STQ_OK : STQ_E_DEVICE; }
 
 extern "C" {
 
-int32_t stq_abi_version(void) { return 6; }
+int32_t stq_abi_version(void) { return 7; }
 
 const char *stq_status_str(int32_t s) {
     switch (s) {
@@ -689,7 +694,7 @@ stq_status stq_allocate(stq_state *st, int32_t horizon, uint32_t candidates,
     if ((e = stq_assign_rows(H, D, dist.data(), logret.data(), nret[0], horizon, mask, nominal,
                              st->desc.n_pivot, counts.data(), perm.data())) != STQ_OK)
         return e;
-    std::vector<int32_t> table(static_cast<size_t>(H) * stq::kLayoutStride);
+    std::vector<int32_t> table(static_cast<size_t>(H) * stq::kLayoutWordsPerHead);
     bool space = false;
     if (!build_layout(&st->desc, st->slot_bytes, counts.data(), table.data(), &space))
         return space ? STQ_E_SPACE : STQ_E_ARG;
@@ -710,7 +715,7 @@ stq_status stq_set_alloc_layout(stq_state *st, const int32_t *counts, const floa
     if (!alloc_format(st->desc.fmt)) return STQ_E_ARG;
     if (!counts || !c || !perm || !aligned(c, 16) || !aligned(perm, 16)) return STQ_E_ARG;
     const int D = st->desc.d_k, H = st->desc.n_heads_v;
-    std::vector<int32_t> table(static_cast<size_t>(H) * stq::kLayoutStride);
+    std::vector<int32_t> table(static_cast<size_t>(H) * stq::kLayoutWordsPerHead);
     bool space = false;
     if (!build_layout(&st->desc, st->slot_bytes, counts, table.data(), &space))
         return space ? STQ_E_SPACE : STQ_E_ARG;

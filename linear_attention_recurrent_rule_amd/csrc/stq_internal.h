@@ -2,6 +2,7 @@
 // libstq.so.  Not installed; the public interface is include/stq.h.
 #pragma once
 
+#include <hip/hip_runtime.h>
 #include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -78,6 +79,59 @@ constexpr int kNumClasses = 5;
 constexpr int kLayoutStride = 8;
 constexpr int kLayoutSegOff = 5;
 constexpr int kLayoutSegBytes = 6;
+
+// After the [Hv][kLayoutStride] table, the layout buffer holds per head the
+// row-chunk load descriptors of the 128 x 128 ragged decode: for each wave w
+// (rows 16 m + 4 w .. 16 m + 4 w + 3 in its slot m) and slot m, two words.
+//   word 0: the slot's row base, b_k + (16 m - s_k) RB_k, for class k
+//           starting at physical row s_k and segment byte b_k (row p of the
+//           class at b_k + (p - s_k) RB_k, so lane group g adds g RB_k);
+//   word 1: RB_k | k << 9 | shA << 16 | shB << 20 | offB << 24, where lane
+//           column group c reads its two 8-byte words at
+//           8 ((2c) >> shA) and offB + 8 ((2c) >> shB) past its row;
+//           bit 31 set instead when the slot's four rows straddle a class
+//           boundary (that slot takes the per-lane path).
+// Written with the layout; zero for heads of other sizes.
+constexpr int kSlotDescWords = 64;
+constexpr int kLayoutWordsPerHead = kLayoutStride + kSlotDescWords;
+
+// Row bytes of class k at head size D (FP16, 8, 6, 4, 2 bits).
+__host__ __device__ inline int class_row_bytes_d(int k, int D) {
+    return k == 0 ? 2 * D : (k == 1 ? D : (k == 2 ? 3 * D / 4 : (k == 3 ? D / 2 : D / 4)));
+}
+
+// The descriptors above for one head with class counts n[0..4] at D = 128.
+__host__ __device__ inline void slot_descs_128(const int32_t *n, int32_t *out) {
+    constexpr int D = 128;
+    int s[kNumClasses], b[kNumClasses];
+    s[0] = 0;
+    b[0] = 0;
+    for (int k = 1; k < kNumClasses; ++k) {
+        s[k] = s[k - 1] + n[k - 1];
+        b[k] = b[k - 1] + n[k - 1] * class_row_bytes_d(k - 1, D);
+    }
+    auto cls = [&](int p) { return (p >= s[1]) + (p >= s[2]) + (p >= s[3]) + (p >= s[4]); };
+    // per class: shA, shB, offB (pivot: bytes 16c and 16c + 8; 8-bit: 8c;
+    // 6-bit: the 8-byte words holding its nibbles and its 2-bit fields;
+    // 4-bit and 2-bit: the 8-byte word holding its codes)
+    constexpr int shA[kNumClasses] = {0, 1, 2, 2, 3};
+    constexpr int shB[kNumClasses] = {0, 1, 3, 2, 3};
+    constexpr int offB[kNumClasses] = {8, 0, D / 2, 0, 0};
+    for (int w = 0; w < 4; ++w)
+        for (int m = 0; m < 8; ++m) {
+            const int p0 = 16 * m + 4 * w;
+            const int k = cls(p0);
+            int32_t *o = out + 2 * (8 * w + m);
+            if (cls(p0 + 3) != k) {
+                o[0] = 0;
+                o[1] = static_cast<int32_t>(0x80000000u);
+                continue;
+            }
+            const int rb = class_row_bytes_d(k, D);
+            o[0] = b[k] + (16 * m - s[k]) * rb;
+            o[1] = rb | (k << 9) | (shA[k] << 16) | (shB[k] << 20) | (offB[k] << 24);
+        }
+}
 
 // Offline calibration of the ALLOC formats.
 struct AllocCalArgs {

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert "stq_decode_step" in names and len(names) >= 8
     for n in names:
         assert hasattr(lib, n), f"libstq.so does not export {n}"
-    assert lib.stq_abi_version() == 6
+    assert lib.stq_abi_version() == 7
 
 
 def _desc(n_slots=4, hv=4, hk=2, d=64, n8=32, fmt=stq.FMT_MIXED48, dv=None, nominal=0, piv=0):
@@ -275,7 +275,7 @@ def test_alloc_layout_arithmetic_and_rejections():
             slot = _alloc_slot_bytes(H, D, nominal, piv)
             expect = (_r(S * slot) + _r(S * H * D * 4) + _r(H * D * 4) * 2
                       + _r(H * D * 4) + _r(H * D * 8) + _r(H * 64 * D * 4) + _r(H * 64 * D * 8)
-                      + _r(H * 8 * 4) + _r(H * D * 5 * 8) + _r(H * D * 8) + _r(H * 8))
+                      + _r(H * (8 + 64) * 4) + _r(H * D * 5 * 8) + _r(H * D * 8) + _r(H * 8))
             if fmt == stq.FMT_ALLOC_REFIT:
                 expect += _r(S * H * D * 4) + _r(H * D * 4) + _r(H * D * 8)
             got = _bytes(n_slots=S, hv=H, hk=16, d=D, n8=0, fmt=fmt, nominal=nominal, piv=piv)
