@@ -342,11 +342,18 @@ __global__ __launch_bounds__(256, 3) void decode_alloc128_kernel(DecodeArgs a, U
     const float rpv = rr[tl];
     // raw bits only: widening here would make the branch wait for the loads
     uint32_t x0, x1, x2 = 0u, x3 = 0u, g0 = 0u, g1 = 0u, u0 = 0u, u1 = 0u;
+    constexpr bool kPairs = std::is_same<TIn, uint16_t>::value; // bf16 k, q: two per 4-byte load
     if (lowhalf) {
-        x0 = In<TIn>::raw(kp0, l64);
-        x1 = In<TIn>::raw(kp0, 64 + l64);
-        x2 = In<TIn>::raw(qp0, l64);
-        x3 = In<TIn>::raw(qp0, 64 + l64);
+        if constexpr (kPairs) {
+            // lane l holds entries 2l and 2l + 1 of k and of q
+            x0 = reinterpret_cast<const uint32_t *>(kp0)[l64];
+            x2 = reinterpret_cast<const uint32_t *>(qp0)[l64];
+        } else {
+            x0 = In<TIn>::raw(kp0, l64);
+            x1 = In<TIn>::raw(kp0, 64 + l64);
+            x2 = In<TIn>::raw(qp0, l64);
+            x3 = In<TIn>::raw(qp0, 64 + l64);
+        }
         if (GATED) {
             const uint32_t *gp = reinterpret_cast<const uint32_t *>(a.gate) + static_cast<size_t>(unit) * D;
             g0 = gp[l64];
@@ -438,8 +445,21 @@ __global__ __launch_bounds__(256, 3) void decode_alloc128_kernel(DecodeArgs a, U
             const uint32_t a1 = __builtin_amdgcn_ds_bpermute(src, static_cast<int>(hi));
             return sel(up, a1, a0);
         };
-        const float kp = In<TIn>::cvt(pick(x0, x1));
-        const float qp = In<TIn>::cvt(pick(x2, x3));
+        float kp, qp;
+        if constexpr (kPairs) {
+            // entry i in half i & 1 of lane i >> 1: one permute per vector
+            const int src2 = (i >> 1) << 2;
+            const uint32_t odd = lane_mask(i & 1);
+            auto pick2 = [&](uint32_t w) {
+                const uint32_t v2 = __builtin_amdgcn_ds_bpermute(src2, static_cast<int>(w));
+                return __uint_as_float(sel(odd, v2 & 0xFFFF0000u, v2 << 16));
+            };
+            kp = pick2(x0);
+            qp = pick2(x2);
+        } else {
+            kp = In<TIn>::cvt(pick(x0, x1));
+            qp = In<TIn>::cvt(pick(x2, x3));
+        }
         // integer rows: r / W (codes are widened as W z); pivot rows: 1
         const uint32_t piv = lane_mask(k == 0);
         const float winv = __uint_as_float((127u - 2u * static_cast<unsigned>(k - 1)) << 23); // 2^(2 - 2k)
